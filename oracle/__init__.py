@@ -1,0 +1,155 @@
+"""Exact-attention oracle (fp64, CPU).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the bench's
+CPU-baseline leg may import this package; the product path never does.  It
+shares no code with the HIP library.
+
+The arithmetic lives in ``attn_oracle.c`` (plain C, fp64, textbook two-pass
+softmax); this module only marshals numpy arrays through ctypes.  What is
+computed follows the FlashAttention-2 walkthrough page, "kernel main loop"
+section (online-softmax pseudocode; v1 and v2 compute the same mathematics):
+for each query row i,
+
+    s_ij  = scale * q_i . k_j          over allowed j (j < N_k, and j <= i if causal)
+    O_i   = sum_j exp(s_ij - m_i) v_j / sum_j exp(s_ij - m_i),   m_i = max_j s_ij
+    LSE_i = m_i + ln sum_j exp(s_ij - m_i)
+
+Arrays are contiguous [B, H, N, d]; LSE is [B, H, N_q].
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i = ctypes.c_int
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_attention_f64.argtypes = [_dp, _dp, _dp, _dp, _dp, _i, _i, _i, _i, _i, _i, ctypes.c_double]
+    lib.oracle_attention_rows_bf16.argtypes = [_u16p, _u16p, _u16p, _i64p, ctypes.c_int64, _dp, _dp,
+                                               _i, _i, _i, _i, _i, _i, ctypes.c_double]
+    lib.oracle_partial_f64.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _i, _i, _i, _i, _i, _i, ctypes.c_double,
+                                       _i, _i]
+    lib.oracle_merge_f64.argtypes = [_dp, _dp, _dp, _dp, _dp, _i, ctypes.c_int64, _i]
+    lib.oracle_probs_f64.argtypes = [_dp, _dp, _dp, _i, _i, _i, _i, _i, _i, ctypes.c_double]
+    lib.oracle_bf16_to_f64.argtypes = [_u16p, _dp, ctypes.c_int64]
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a, typ):
+    return a.ctypes.data_as(typ)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle: {what} rejected its arguments")
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact fp64 values of bf16 numbers given as uint16 bit patterns."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, dtype=np.float64)
+    _load().oracle_bf16_to_f64(_ptr(bits, _u16p), _ptr(out, _dp), bits.size)
+    return out
+
+
+def attention(q, k, v, causal: bool, scale: float):
+    """O [B,H,N_q,d] and LSE [B,H,N_q] in fp64 from fp64 inputs."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, n_q, d = q.shape
+    n_k = k.shape[2]
+    assert k.shape == (B, H, n_k, d) and v.shape == (B, H, n_k, d)
+    o = np.empty((B, H, n_q, d), dtype=np.float64)
+    lse = np.empty((B, H, n_q), dtype=np.float64)
+    rc = _load().oracle_attention_f64(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(o, _dp), _ptr(lse, _dp),
+                                      B, H, n_q, n_k, d, int(bool(causal)), float(scale))
+    _check(rc, "attention")
+    return o, lse
+
+
+def attention_rows_bf16(q_bits, k_bits, v_bits, rows, causal: bool, scale: float):
+    """O and LSE for selected flat rows ((b*H + h)*N_q + i) of bf16 inputs given as uint16 bit arrays."""
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    k_bits = np.ascontiguousarray(k_bits, dtype=np.uint16)
+    v_bits = np.ascontiguousarray(v_bits, dtype=np.uint16)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    B, H, n_q, d = q_bits.shape
+    n_k = k_bits.shape[2]
+    assert k_bits.shape == (B, H, n_k, d) and v_bits.shape == (B, H, n_k, d)
+    o = np.empty((rows.size, d), dtype=np.float64)
+    lse = np.empty((rows.size,), dtype=np.float64)
+    rc = _load().oracle_attention_rows_bf16(_ptr(q_bits, _u16p), _ptr(k_bits, _u16p), _ptr(v_bits, _u16p),
+                                            _ptr(rows, _i64p), rows.size, _ptr(o, _dp), _ptr(lse, _dp),
+                                            B, H, n_q, n_k, d, int(bool(causal)), float(scale))
+    _check(rc, "attention_rows_bf16")
+    return o, lse
+
+
+def partial(q, k, v, causal: bool, scale: float, key_begin: int, key_end: int):
+    """Unnormalised (acc [B,H,N_q,d], m [B,H,N_q], l [B,H,N_q]) over keys [key_begin, key_end)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, n_q, d = q.shape
+    n_k = k.shape[2]
+    acc = np.empty((B, H, n_q, d), dtype=np.float64)
+    m = np.empty((B, H, n_q), dtype=np.float64)
+    l_ = np.empty((B, H, n_q), dtype=np.float64)
+    rc = _load().oracle_partial_f64(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(acc, _dp), _ptr(m, _dp),
+                                    _ptr(l_, _dp), B, H, n_q, n_k, d, int(bool(causal)), float(scale),
+                                    int(key_begin), int(key_end))
+    _check(rc, "partial")
+    return acc, m, l_
+
+
+def merge(acc, m, l_):
+    """Merge partials stacked on axis 0: acc [S, ..., d], m and l [S, ...] -> (O [..., d], LSE [...])."""
+    acc, m, l_ = _f64(acc), _f64(m), _f64(l_)
+    n_parts = acc.shape[0]
+    d = acc.shape[-1]
+    row_shape = acc.shape[1:-1]
+    n_rows = int(np.prod(row_shape)) if row_shape else 1
+    assert m.shape == (n_parts,) + row_shape and l_.shape == m.shape
+    o = np.empty(row_shape + (d,), dtype=np.float64)
+    lse = np.empty(row_shape, dtype=np.float64)
+    rc = _load().oracle_merge_f64(_ptr(acc, _dp), _ptr(m, _dp), _ptr(l_, _dp), _ptr(o, _dp), _ptr(lse, _dp),
+                                  n_parts, n_rows, d)
+    _check(rc, "merge")
+    return o, lse
+
+
+def probs(q, k, causal: bool, scale: float):
+    """The attention probability matrix P [B,H,N_q,N_k] (zeros where masked)."""
+    q, k = _f64(q), _f64(k)
+    B, H, n_q, d = q.shape
+    n_k = k.shape[2]
+    p = np.empty((B, H, n_q, n_k), dtype=np.float64)
+    rc = _load().oracle_probs_f64(_ptr(q, _dp), _ptr(k, _dp), _ptr(p, _dp), B, H, n_q, n_k, d,
+                                  int(bool(causal)), float(scale))
+    _check(rc, "probs")
+    return p

@@ -1,0 +1,268 @@
+/*
+ * Exact-attention oracle: plain, slow, obviously correct fp64 CPU code.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link
+ * or call this file; only the test suite, the smoke check and the bench's CPU
+ * baseline leg use it.  It shares no code, header, table or helper with the
+ * HIP library.
+ *
+ * What it computes (FlashAttention-2 walkthrough page, "kernel main loop"
+ * section: the online-softmax pseudocode and the remark that v1 and v2 follow
+ * the same online-softmax mathematics; the result is exact attention):
+ *
+ *   s_ij      = scale * sum_k q_ik * k_jk                 (fp64)
+ *   allowed   = { j : j < N_k and (not causal or j <= i) } (top-left causal)
+ *   m_i       = max_{j allowed} s_ij
+ *   l_i       = sum_{j allowed} exp(s_ij - m_i)
+ *   O_i       = (sum_{j allowed} exp(s_ij - m_i) * v_j) / l_i
+ *   LSE_i     = m_i + ln l_i
+ *
+ * This is the textbook two-pass softmax (max, then exponentials), not the
+ * online recurrence the GPU path uses; the two reach the same result up to
+ * rounding.  Tensors are contiguous [B][H][N][d]; LSE is [B][H][N_q].
+ *
+ * A key-range variant returns the unnormalised partial (acc, m, l) over
+ * [key_begin, key_end) and a merge routine combines such partials; these
+ * follow the "FA2 cross-paper synthesis" page, section 5 item 5 (split the
+ * key/value sequence for single-query decode) with the same rescaling algebra
+ * as the online recurrence (walkthrough page, main-loop pseudocode).  An
+ * empty key range yields m = -inf, l = 0, acc = 0 and contributes nothing.
+ *
+ * Parity pins: every function here is pinned by CPU tests (brute force at 50
+ * digits, closed forms, invariants, torch's fp64 CPU attention, a float64
+ * transcription of the pages' recurrence); none is "parity unpinned".
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC (no fast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* bf16 bit pattern -> double, exactly (a bf16 is the top half of a float). */
+static double bf16_bits_to_double(uint16_t bits) {
+  uint32_t u = ((uint32_t)bits) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+void oracle_bf16_to_f64(const uint16_t* src, double* dst, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) dst[i] = bf16_bits_to_double(src[i]);
+}
+
+/* Number of keys row i may attend to: the allowed set is always a prefix. */
+static int64_t allowed_prefix(int64_t i, int64_t n_k, int causal) {
+  if (!causal) return n_k;
+  return (i + 1 < n_k) ? i + 1 : n_k;
+}
+
+/*
+ * One query row against keys [j0, j1) (already clipped to the allowed set).
+ * Writes the unnormalised partial: acc[d] = sum exp(s_j - m) v_j, *m, *l.
+ * s is caller scratch of at least j1 - j0 doubles.
+ */
+static void partial_row(const double* q, const double* K, const double* V, int64_t j0, int64_t j1,
+                        int d, double scale, double* s, double* acc, double* m_out, double* l_out) {
+  for (int c = 0; c < d; ++c) acc[c] = 0.0;
+  if (j1 <= j0) {
+    *m_out = -INFINITY;
+    *l_out = 0.0;
+    return;
+  }
+  /* pass 1: scores and their maximum */
+  double m = -INFINITY;
+  for (int64_t j = j0; j < j1; ++j) {
+    const double* kj = K + j * d;
+    double dot = 0.0;
+    for (int c = 0; c < d; ++c) dot += q[c] * kj[c];
+    s[j - j0] = scale * dot;
+    if (s[j - j0] > m) m = s[j - j0];
+  }
+  /* pass 2: exponentials, their sum, and the weighted sum of values */
+  double l = 0.0;
+  for (int64_t j = j0; j < j1; ++j) {
+    double p = exp(s[j - j0] - m);
+    l += p;
+    const double* vj = V + j * d;
+    for (int c = 0; c < d; ++c) acc[c] += p * vj[c];
+  }
+  *m_out = m;
+  *l_out = l;
+}
+
+/* Full attention for one row: normalise the partial over the allowed prefix. */
+static void attend_row(const double* q, const double* K, const double* V, int64_t n_allowed, int d,
+                       double scale, double* s, double* o, double* lse) {
+  double m, l;
+  partial_row(q, K, V, 0, n_allowed, d, scale, s, o, &m, &l);
+  for (int c = 0; c < d; ++c) o[c] /= l;
+  *lse = m + log(l);
+}
+
+static int check_shape(int B, int H, int n_q, int n_k, int d) {
+  return (B >= 1 && H >= 1 && n_q >= 0 && n_k >= 1 && d >= 1) ? 0 : -1;
+}
+
+/*
+ * O, LSE for all rows.  Q, K, V are fp64 values (the exact values of the
+ * bf16 inputs, or any reals for pins).  Returns 0, or -1 on a bad shape.
+ */
+int oracle_attention_f64(const double* Q, const double* K, const double* V, double* O, double* LSE,
+                         int B, int H, int n_q, int n_k, int d, int causal, double scale) {
+  if (check_shape(B, H, n_q, n_k, d)) return -1;
+  const int64_t rows_per_block = 64;
+  const int64_t n_blocks = (n_q + rows_per_block - 1) / rows_per_block;
+  const int64_t n_tasks = (int64_t)B * H * n_blocks;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)n_k);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < n_tasks; ++t) {
+      const int64_t bh = t / n_blocks, blk = t % n_blocks;
+      const double* Kh = K + bh * (int64_t)n_k * d;
+      const double* Vh = V + bh * (int64_t)n_k * d;
+      const int64_t i_end = (blk + 1) * rows_per_block < n_q ? (blk + 1) * rows_per_block : n_q;
+      for (int64_t i = blk * rows_per_block; i < i_end; ++i) {
+        const int64_t row = bh * n_q + i;
+        attend_row(Q + row * d, Kh, Vh, allowed_prefix(i, n_k, causal), d, scale, s, O + row * d, LSE + row);
+      }
+    }
+    free(s);
+  }
+  return 0;
+}
+
+/*
+ * Same result for a chosen set of rows of bf16 inputs.  Q, K, V hold bf16 bit
+ * patterns of the whole [B][H][N][d] tensors; rows[r] = (b*H + h)*N_q + i.
+ * Only the heads the listed rows touch are converted.  O_rows is [n_rows][d],
+ * LSE_rows is [n_rows].  Returns 0, or -1 on a bad shape / row index.
+ */
+int oracle_attention_rows_bf16(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const int64_t* rows,
+                               int64_t n_rows, double* O_rows, double* LSE_rows, int B, int H, int n_q, int n_k,
+                               int d, int causal, double scale) {
+  if (check_shape(B, H, n_q, n_k, d)) return -1;
+  for (int64_t r = 0; r < n_rows; ++r)
+    if (rows[r] < 0 || rows[r] >= (int64_t)B * H * n_q) return -1;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)n_k);
+    double* q = (double*)malloc(sizeof(double) * (size_t)d);
+    double* Kh = (double*)malloc(sizeof(double) * (size_t)n_k * d);
+    double* Vh = (double*)malloc(sizeof(double) * (size_t)n_k * d);
+    int64_t cached_bh = -1;
+    if (!s || !q || !Kh || !Vh) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      if (failed) continue;
+      const int64_t bh = rows[r] / n_q, i = rows[r] % n_q;
+      if (bh != cached_bh) {
+        oracle_bf16_to_f64(K + bh * (int64_t)n_k * d, Kh, (int64_t)n_k * d);
+        oracle_bf16_to_f64(V + bh * (int64_t)n_k * d, Vh, (int64_t)n_k * d);
+        cached_bh = bh;
+      }
+      oracle_bf16_to_f64(Q + rows[r] * d, q, d);
+      attend_row(q, Kh, Vh, allowed_prefix(i, n_k, causal), d, scale, s, O_rows + r * d, LSE_rows + r);
+    }
+    free(s); free(q); free(Kh); free(Vh);
+  }
+  return failed ? -1 : 0;
+}
+
+/*
+ * Unnormalised partial over keys [key_begin, key_end) intersected with the
+ * allowed set, for every row: acc [B][H][N_q][d], m and l [B][H][N_q].
+ */
+int oracle_partial_f64(const double* Q, const double* K, const double* V, double* acc, double* m, double* l,
+                       int B, int H, int n_q, int n_k, int d, int causal, double scale, int key_begin,
+                       int key_end) {
+  if (check_shape(B, H, n_q, n_k, d) || key_begin < 0 || key_end < key_begin) return -1;
+  const int64_t n_rows = (int64_t)B * H * n_q;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)n_k);
+#pragma omp for schedule(static)
+    for (int64_t row = 0; row < n_rows; ++row) {
+      const int64_t bh = row / n_q, i = row % n_q;
+      const int64_t n_allowed = allowed_prefix(i, n_k, causal);
+      const int64_t j0 = key_begin;
+      const int64_t j1 = key_end < n_allowed ? key_end : n_allowed;
+      partial_row(Q + row * d, K + bh * (int64_t)n_k * d, V + bh * (int64_t)n_k * d, j0, j1, d, scale, s,
+                  acc + row * d, m + row, l + row);
+    }
+    free(s);
+  }
+  return 0;
+}
+
+/*
+ * Merge n_parts partials per row (part-major: acc [n_parts][n_rows][d], m and
+ * l [n_parts][n_rows]) into O [n_rows][d] and LSE [n_rows]:
+ *   M = max_c m_c;  w_c = exp(m_c - M) (0 for an empty part);
+ *   l = sum_c w_c l_c;  O = (sum_c w_c acc_c) / l;  LSE = M + ln l.
+ */
+int oracle_merge_f64(const double* acc, const double* m, const double* l, double* O, double* LSE, int n_parts,
+                     int64_t n_rows, int d) {
+  if (n_parts < 1 || n_rows < 0 || d < 1) return -1;
+  for (int64_t row = 0; row < n_rows; ++row) {
+    double M = -INFINITY;
+    for (int c = 0; c < n_parts; ++c)
+      if (m[c * n_rows + row] > M) M = m[c * n_rows + row];
+    double lsum = 0.0;
+    for (int k = 0; k < d; ++k) O[row * d + k] = 0.0;
+    for (int c = 0; c < n_parts; ++c) {
+      const double mc = m[c * n_rows + row];
+      if (mc == -INFINITY) continue; /* empty part: weight 0 */
+      const double w = exp(mc - M);
+      lsum += w * l[c * n_rows + row];
+      for (int k = 0; k < d; ++k) O[row * d + k] += w * acc[(c * n_rows + row) * d + k];
+    }
+    for (int k = 0; k < d; ++k) O[row * d + k] /= lsum;
+    LSE[row] = M + log(lsum);
+  }
+  return 0;
+}
+
+/*
+ * The probability matrix P [B][H][N_q][N_k] (zero where not allowed), for
+ * small shapes in tests: P_ij = exp(s_ij - m_i) / l_i.
+ */
+int oracle_probs_f64(const double* Q, const double* K, double* P, int B, int H, int n_q, int n_k, int d,
+                     int causal, double scale) {
+  if (check_shape(B, H, n_q, n_k, d)) return -1;
+  double* s = (double*)malloc(sizeof(double) * (size_t)n_k);
+  if (!s) return -1;
+  for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+    for (int64_t i = 0; i < n_q; ++i) {
+      const double* q = Q + (bh * n_q + i) * d;
+      double* prow = P + (bh * n_q + i) * n_k;
+      const int64_t n_allowed = allowed_prefix(i, n_k, causal);
+      double m = -INFINITY;
+      for (int64_t j = 0; j < n_allowed; ++j) {
+        const double* kj = K + (bh * n_k + j) * d;
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c) dot += q[c] * kj[c];
+        s[j] = scale * dot;
+        if (s[j] > m) m = s[j];
+      }
+      double l = 0.0;
+      for (int64_t j = 0; j < n_allowed; ++j) l += exp(s[j] - m);
+      for (int64_t j = 0; j < n_k; ++j) prow[j] = (j < n_allowed) ? exp(s[j] - m) / l : 0.0;
+    }
+  }
+  free(s);
+  return 0;
+}
+
+/* Threads the parallel regions above use (reported beside CPU timings). */
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_num_threads(void) { return 1; }
+#endif

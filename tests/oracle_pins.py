@@ -1,0 +1,284 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` function takes an oracle module (the real one, or a mutated
+copy built by the mutation test) and raises AssertionError when the oracle
+disagrees with:
+
+  P1  brute force at 50 significant digits (mpmath), without the max shift;
+  P2  rows of P summing to 1 and P vanishing where masked;
+  P3  constant V returning that constant;
+  P4  causal row 0 returning v_0 with LSE = s_00;
+  P5  Q = 0: O = mean of the allowed values, LSE = ln(#allowed);
+  P6  one-hot scores: a closed form in e^a;
+  P7  LSE = ln sum exp(s) (exact summation) and max s <= LSE <= max s + ln n;
+  P8  torch's fp64 CPU scaled_dot_product_attention (a library special case);
+  P9  invariants: joint key/value permutation, query permutation, linearity
+      in V, and split-then-merge equal to the unsplit result;
+  P10 a float64 transcription of the pages' tiled online recurrence
+      (FlashAttention-2 walkthrough page, main-loop pseudocode) with random
+      tile sizes.
+
+The definition pinned is exact attention with top-left causal masking
+(key j allowed for query i iff j <= i), scale applied to q.k before the
+softmax, and LSE the natural log of sum exp of the scaled, masked scores.
+"""
+import math
+
+import mpmath
+import numpy as np
+import torch
+
+RNG = np.random.default_rng
+
+
+def _allowed(i, n_k, causal):
+    return min(i + 1, n_k) if causal else n_k
+
+
+def pin_p1_bruteforce(orc):
+    mpmath.mp.dps = 50
+    rng = RNG(101)
+    cases = [(1, 2, 5, 7, 3, False), (1, 2, 5, 7, 3, True), (2, 1, 8, 4, 4, True), (1, 1, 6, 6, 2, True),
+             (1, 1, 1, 8, 4, False), (1, 1, 8, 1, 4, True)]
+    for B, H, n_q, n_k, d, causal in cases:
+        q = rng.normal(size=(B, H, n_q, d)) * 1.5
+        k = rng.normal(size=(B, H, n_k, d)) * 1.5
+        v = rng.normal(size=(B, H, n_k, d))
+        scale = 0.7
+        o, lse = orc.attention(q, k, v, causal, scale)
+        for b in range(B):
+            for h in range(H):
+                for i in range(n_q):
+                    n = _allowed(i, n_k, causal)
+                    ex = []
+                    for j in range(n):
+                        s = mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(q[b, h, i, c]) * mpmath.mpf(k[b, h, j, c])
+                                                            for c in range(d))
+                        ex.append(mpmath.e ** s)
+                    z = mpmath.fsum(ex)
+                    for c in range(d):
+                        ref = mpmath.fsum(ex[j] * mpmath.mpf(v[b, h, j, c]) for j in range(n)) / z
+                        assert abs(float(ref) - o[b, h, i, c]) <= 1e-13 * (1 + abs(float(ref))), (b, h, i, c)
+                    ref_lse = mpmath.log(z)
+                    assert abs(float(ref_lse) - lse[b, h, i]) <= 1e-13 * (1 + abs(float(ref_lse))), (b, h, i)
+
+
+def pin_p2_rows_sum_to_one(orc):
+    rng = RNG(202)
+    for causal in (False, True):
+        q = rng.normal(size=(2, 3, 9, 5)) * 2
+        k = rng.normal(size=(2, 3, 11, 5)) * 2
+        p = orc.probs(q, k, causal, 0.9)
+        assert np.all(p >= 0)
+        assert np.max(np.abs(p.sum(-1) - 1.0)) <= 1e-14
+        if causal:
+            for i in range(9):
+                assert np.all(p[:, :, i, i + 1:] == 0.0)
+        # P agrees with the O the oracle returns: O = P V
+        v = rng.normal(size=(2, 3, 11, 5))
+        o, _ = orc.attention(q, k, v, causal, 0.9)
+        assert np.max(np.abs(np.einsum("bhij,bhjc->bhic", p, v) - o)) <= 1e-13
+
+
+def pin_p3_constant_v(orc):
+    rng = RNG(303)
+    for causal in (False, True):
+        q = rng.normal(size=(1, 2, 13, 8)) * 3
+        k = rng.normal(size=(1, 2, 17, 8)) * 3
+        c = rng.normal(size=(8,))
+        v = np.broadcast_to(c, (1, 2, 17, 8)).copy()
+        o, _ = orc.attention(q, k, v, causal, 0.5)
+        assert np.max(np.abs(o - c)) <= 1e-14 * (1 + np.max(np.abs(c)))
+
+
+def pin_p4_causal_row0(orc):
+    rng = RNG(404)
+    q = rng.normal(size=(2, 2, 6, 4))
+    k = rng.normal(size=(2, 2, 9, 4))
+    v = rng.normal(size=(2, 2, 9, 4))
+    scale = 1.3
+    o, lse = orc.attention(q, k, v, True, scale)
+    assert np.max(np.abs(o[:, :, 0, :] - v[:, :, 0, :])) <= 1e-15
+    s00 = scale * np.sum(q[:, :, 0, :] * k[:, :, 0, :], axis=-1)
+    assert np.max(np.abs(lse[:, :, 0] - s00)) <= 1e-14
+
+
+def pin_p5_uniform_scores(orc):
+    rng = RNG(505)
+    n_q, n_k, d = 10, 7, 6
+    q = np.zeros((1, 2, n_q, d))
+    k = rng.normal(size=(1, 2, n_k, d))
+    v = rng.normal(size=(1, 2, n_k, d))
+    for causal in (False, True):
+        o, lse = orc.attention(q, k, v, causal, 0.8)
+        for i in range(n_q):
+            n = _allowed(i, n_k, causal)
+            assert np.max(np.abs(o[:, :, i, :] - v[:, :, :n, :].mean(axis=2))) <= 1e-14
+            assert np.max(np.abs(lse[:, :, i] - math.log(n))) <= 1e-14
+
+
+def pin_p6_one_hot(orc):
+    # q_i = k_i = c e_i (N <= d) so s_ij = a * delta_ij with a = scale * c^2.
+    n, d, c, scale = 6, 8, 4.0, 0.125   # a = 2
+    a = scale * c * c
+    q = np.zeros((1, 1, n, d))
+    for i in range(n):
+        q[0, 0, i, i] = c
+    k = q.copy()
+    v = RNG(606).normal(size=(1, 1, n, d))
+    for causal in (False, True):
+        o, lse = orc.attention(q, k, v, causal, scale)
+        for i in range(n):
+            na = i + 1 if causal else n
+            z = math.exp(a) + (na - 1)
+            ref = (math.exp(a) * v[0, 0, i] + (v[0, 0, :na].sum(axis=0) - v[0, 0, i])) / z
+            assert np.max(np.abs(o[0, 0, i] - ref)) <= 1e-14
+            assert abs(lse[0, 0, i] - math.log(z)) <= 1e-14
+
+
+def pin_p7_lse_identity(orc):
+    rng = RNG(707)
+    n_q, n_k, d = 7, 12, 5
+    q = rng.normal(size=(1, 1, n_q, d)) * 4
+    k = rng.normal(size=(1, 1, n_k, d)) * 4
+    v = rng.normal(size=(1, 1, n_k, d))
+    scale = 0.6
+    for causal in (False, True):
+        _, lse = orc.attention(q, k, v, causal, scale)
+        for i in range(n_q):
+            n = _allowed(i, n_k, causal)
+            s = [scale * math.fsum(q[0, 0, i, c] * k[0, 0, j, c] for c in range(d)) for j in range(n)]
+            smax = max(s)
+            ref = smax + math.log(math.fsum(math.exp(x - smax) for x in s))
+            assert abs(lse[0, 0, i] - ref) <= 1e-13 * (1 + abs(ref))
+            assert smax - 1e-13 <= lse[0, 0, i] <= smax + math.log(n) + 1e-13
+
+
+def pin_p8_torch_sdpa(orc):
+    rng = RNG(808)
+    for (n_q, n_k, d, causal) in [(33, 33, 16, False), (33, 33, 16, True), (20, 45, 8, True), (45, 20, 8, True),
+                                  (64, 70, 32, False)]:
+        q = rng.normal(size=(2, 3, n_q, d))
+        k = rng.normal(size=(2, 3, n_k, d))
+        v = rng.normal(size=(2, 3, n_k, d))
+        scale = 1.0 / math.sqrt(d)
+        o, lse = orc.attention(q, k, v, causal, scale)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        if causal:
+            # top-left alignment written out: key j visible to query i iff j <= i
+            mask = torch.ones(n_q, n_k, dtype=torch.bool).tril()
+            ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale)
+        else:
+            ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale)
+        assert np.max(np.abs(ref.numpy() - o)) <= 1e-12
+        scores = torch.matmul(tq, tk.transpose(-1, -2)) * scale
+        if causal:
+            scores = scores.masked_fill(~mask, float("-inf"))
+        assert np.max(np.abs(torch.logsumexp(scores, dim=-1).numpy() - lse)) <= 1e-12
+
+
+def pin_p9_invariants(orc):
+    rng = RNG(909)
+    n_q, n_k, d = 14, 19, 6
+    q = rng.normal(size=(1, 2, n_q, d))
+    k = rng.normal(size=(1, 2, n_k, d))
+    v = rng.normal(size=(1, 2, n_k, d))
+    v2 = rng.normal(size=(1, 2, n_k, d))
+    scale = 0.45
+    o, lse = orc.attention(q, k, v, False, scale)
+    # joint key/value permutation (non-causal) changes nothing
+    perm = rng.permutation(n_k)
+    o_p, lse_p = orc.attention(q, k[:, :, perm], v[:, :, perm], False, scale)
+    assert np.max(np.abs(o_p - o)) <= 1e-13 and np.max(np.abs(lse_p - lse)) <= 1e-13
+    # query permutation permutes output rows
+    qp = rng.permutation(n_q)
+    o_q, lse_q = orc.attention(q[:, :, qp], k, v, False, scale)
+    assert np.max(np.abs(o_q - o[:, :, qp])) <= 1e-13 and np.max(np.abs(lse_q - lse[:, :, qp])) <= 1e-13
+    # linear in V
+    for causal in (False, True):
+        oa, _ = orc.attention(q, k, v, causal, scale)
+        ob, _ = orc.attention(q, k, v2, causal, scale)
+        oc, _ = orc.attention(q, k, 2.0 * v - 3.0 * v2, causal, scale)
+        assert np.max(np.abs(oc - (2.0 * oa - 3.0 * ob))) <= 1e-12
+    # split the keys into chunks, merge the partials: equals the unsplit result
+    for causal in (False, True):
+        o_full, lse_full = orc.attention(q, k, v, causal, scale)
+        for n_splits in (1, 2, 3, 7, n_k):
+            L = -(-n_k // n_splits)
+            parts = [orc.partial(q, k, v, causal, scale, c * L, min((c + 1) * L, n_k)) for c in range(n_splits)]
+            acc = np.stack([p[0] for p in parts])
+            m = np.stack([p[1] for p in parts])
+            l_ = np.stack([p[2] for p in parts])
+            o_m, lse_m = orc.merge(acc, m, l_)
+            assert np.max(np.abs(o_m - o_full)) <= 1e-13, (causal, n_splits)
+            assert np.max(np.abs(lse_m - lse_full)) <= 1e-13, (causal, n_splits)
+        # an empty chunk is (acc 0, m -inf, l 0)
+        acc, m, l_ = orc.partial(q, k, v, True, scale, n_k, n_k)
+        assert np.all(acc == 0) and np.all(np.isneginf(m)) and np.all(l_ == 0)
+    # row-selected bf16 entry point equals the full one on bf16-exact values
+    qb = torch.from_numpy(q).to(torch.bfloat16)
+    kb = torch.from_numpy(k).to(torch.bfloat16)
+    vb = torch.from_numpy(v).to(torch.bfloat16)
+    bits = [t.contiguous().view(torch.int16).numpy().view(np.uint16) for t in (qb, kb, vb)]
+    vals = [t.to(torch.float64).numpy() for t in (qb, kb, vb)]
+    assert np.array_equal(orc.bf16_bits_to_f64(bits[0]), vals[0])
+    for causal in (False, True):
+        o_full, lse_full = orc.attention(*vals, causal, scale)
+        rows = np.array([0, 5, n_q - 1, n_q, 2 * n_q - 1], dtype=np.int64)
+        o_r, lse_r = orc.attention_rows_bf16(*bits, rows, causal, scale)
+        assert np.array_equal(o_r, o_full.reshape(-1, d)[rows])
+        assert np.array_equal(lse_r, lse_full.reshape(-1)[rows])
+
+
+def recurrence_model(q, k, v, causal, scale, block_r, block_c):
+    """The pages' tiled online recurrence (FlashAttention-2 walkthrough page,
+    main-loop pseudocode), in float64, one (b, h) at a time:
+    per query block, m = -inf, l = 0, acc = 0; per key block S = scale*Q K^T,
+    mask, m_new = max(m, rowmax S), P = exp(S - m_new),
+    acc = acc*exp(m - m_new) + P V, l = l*exp(m - m_new) + rowsum P; finally
+    O = acc / l and LSE = m + ln l."""
+    B, H, n_q, d = q.shape
+    n_k = k.shape[2]
+    o = np.zeros((B, H, n_q, d))
+    lse = np.zeros((B, H, n_q))
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, n_q, block_r):
+                r1 = min(r0 + block_r, n_q)
+                m = np.full(r1 - r0, -np.inf)
+                l_ = np.zeros(r1 - r0)
+                acc = np.zeros((r1 - r0, d))
+                for c0 in range(0, n_k, block_c):
+                    c1 = min(c0 + block_c, n_k)
+                    s = scale * (q[b, h, r0:r1] @ k[b, h, c0:c1].T)
+                    if causal:
+                        rows = np.arange(r0, r1)[:, None]
+                        cols = np.arange(c0, c1)[None, :]
+                        s = np.where(cols <= rows, s, -np.inf)
+                    m_new = np.maximum(m, s.max(axis=1))
+                    p = np.exp(s - m_new[:, None])
+                    alpha = np.exp(m - m_new)
+                    acc = acc * alpha[:, None] + p @ v[b, h, c0:c1]
+                    l_ = l_ * alpha + p.sum(axis=1)
+                    m = m_new
+                o[b, h, r0:r1] = acc / l_[:, None]
+                lse[b, h, r0:r1] = m + np.log(l_)
+    return o, lse
+
+
+def pin_p10_recurrence(orc):
+    rng = RNG(1010)
+    for causal in (False, True):
+        q = rng.normal(size=(1, 2, 37, 8))
+        k = rng.normal(size=(1, 2, 37, 8))
+        v = rng.normal(size=(1, 2, 37, 8))
+        o, lse = orc.attention(q, k, v, causal, 0.35)
+        for block_r, block_c in [(1, 1), (4, 7), (16, 5), (37, 37), (64, 64)]:
+            o_r, lse_r = recurrence_model(q, k, v, causal, 0.35, block_r, block_c)
+            assert np.max(np.abs(o_r - o)) <= 1e-12
+            assert np.max(np.abs(lse_r - lse)) <= 1e-12
+
+
+ALL_PINS = [pin_p1_bruteforce, pin_p2_rows_sum_to_one, pin_p3_constant_v, pin_p4_causal_row0,
+            pin_p5_uniform_scores, pin_p6_one_hot, pin_p7_lse_identity, pin_p8_torch_sdpa,
+            pin_p9_invariants, pin_p10_recurrence]

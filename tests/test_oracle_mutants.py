@@ -1,0 +1,59 @@
+"""Mutation test of the pins: plausible mistakes planted in a copy of the
+oracle's C source (on the CPU) must each make at least one pin fail."""
+import importlib.util
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+from tests import oracle_pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "attn_oracle.c")
+
+# (name, original text, mutated text)
+MUTANTS = [
+    ("causal_off_by_one", "return (i + 1 < n_k) ? i + 1 : n_k;", "return (i < n_k) ? i : n_k;"),
+    ("causal_ignored", "if (!causal) return n_k;", "return n_k;"),
+    ("scale_dropped", "s[j - j0] = scale * dot;", "s[j - j0] = dot;"),
+    ("scale_squared", "s[j - j0] = scale * dot;", "s[j - j0] = scale * scale * dot;"),
+    ("max_not_subtracted_in_lse", "*lse = m + log(l);", "*lse = log(l);"),
+    ("values_from_keys", "const double* vj = V + j * d;", "const double* vj = K + j * d;"),
+    ("normalisation_dropped", "for (int c = 0; c < d; ++c) o[c] /= l;", ""),
+    ("log2_lse", "*lse = m + log(l);", "*lse = m + log2(l);"),
+    ("merge_weights_dropped", "const double w = exp(mc - M);", "const double w = 1.0;"),
+    ("feature_index_reversed", "for (int c = 0; c < d; ++c) dot += q[c] * kj[c];",
+     "for (int c = 0; c < d; ++c) dot += q[c] * kj[d - 1 - c];"),
+    ("first_key_skipped", "for (int64_t j = j0; j < j1; ++j) {\n    double p = exp", "for (int64_t j = j0 + 1; j < j1; ++j) {\n    double p = exp"),
+]
+
+
+def _build_mutant(tmp_path, name, before, after):
+    text = open(SRC).read()
+    assert before in text, f"mutation site for {name} not found"
+    pkg = tmp_path / f"oracle_mut_{name}"
+    shutil.copytree(os.path.join(ROOT, "oracle"), pkg,
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__", "*.tmp"))
+    (pkg / "attn_oracle.c").write_text(text.replace(before, after, 1))
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", str(pkg / "liboracle.so"),
+                    str(pkg / "attn_oracle.c"), "-lm"], check=True)
+    spec = importlib.util.spec_from_file_location(pkg.name, pkg / "__init__.py",
+                                                  submodule_search_locations=[str(pkg)])
+    mod = importlib.util.module_from_spec(spec)
+    sys.modules[pkg.name] = mod
+    spec.loader.exec_module(mod)
+    return mod
+
+
+@pytest.mark.parametrize("name,before,after", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, before, after):
+    mod = _build_mutant(tmp_path, name, before, after)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mod)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name}"

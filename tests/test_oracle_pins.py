@@ -1,0 +1,11 @@
+"""The fp64 oracle against its pins (brute force, closed forms, invariants,
+torch's fp64 CPU attention, the pages' recurrence).  CPU only."""
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_oracle_pin(pin):
+    pin(oracle)
