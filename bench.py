@@ -1,0 +1,212 @@
+"""Benchmark of the exact-attention forward on one MI355X.
+
+A step is one fa2_fwd call over one batch of the long-sequence workload
+B=1, H=32, N_q=N_k=16384, d=128 (bf16, non-causal, scale 1/sqrt(d)), inputs
+resident in HBM.  Throughput counts 4*B*H*N_q*N_k*d FLOP per step (halved for
+causal).  The same run also times the other named workloads (the causal
+variants, the d=64 and d=128 training shapes, and the split-KV decode) and the
+fp64 oracle on a bounded sample of the headline workload, and prints ONE JSON
+line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu] [--calib-copy]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 256 * 4 * 1024 * 2.4e9 / 1e12   # 2516.6: 256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd TFLOP/s (bf16, causal/non-causal) and % of MI355X MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "exact_attention_85_amd", "csrc", "fa2_fwd.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(key: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
+    absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(key)
+    if not e or e.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, steps: int, warmup: int):
+    """Average milliseconds per call of fn over `steps` calls on torch's current
+    stream, timed with events recorded on that stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def cpu_baseline(w, causal: bool, q, k, v):
+    """The fp64 oracle on a bounded sample of rows of the workload (about 10-30 s
+    of host work), in TFLOP/s with the same FLOP count per row."""
+    import numpy as np
+
+    import oracle
+
+    h_bits = [workloads.bf16_bits(t[:1, :1]) for t in (q, k, v)]  # head (b=0, h=0) on the host
+    flop_row = 4.0 * w.n_k * w.d / (2 if causal else 1)  # the metric's per-row count
+    rng = np.random.default_rng(7)
+
+    def run(n_rows):
+        rows = np.sort(rng.choice(w.n_q, size=n_rows, replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attention_rows_bf16(*h_bits, rows, causal, w.scale)
+        dt = time.perf_counter() - t0
+        return dt, n_rows * flop_row
+
+    dt, _ = run(64)
+    per_row = max(dt / 64, 1e-6)
+    n_rows = int(min(w.n_q, max(64, 15.0 / per_row)))
+    dt, flop = run(n_rows)
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n_rows} query rows of head (b=0,h=0) of {w.name}, "
+                      f"{'causal' if causal else 'non-causal'}, fp64 two-pass softmax, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration for profiles)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the attention forward "
+              f"shards over heads with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import exact_attention_85_amd as fa2
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fa2.load_library()
+
+    w = workloads.C4
+    causal = False
+    q, k, v = workloads.make_qkv(w, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.n_q), dtype=torch.float32, device=dev)
+
+    if args.calib_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step():
+        fa2.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(stop) / args.steps
+    flop = w.flop(causal)
+    tflops = flop / (ms * 1e-3) / 1e12
+    assert torch.isfinite(lse).all().item(), "non-finite LSE"
+    log(f"{w.name} non-causal: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% "
+        f"of {PEAK_BF16_TFLOPS:.1f}), wall {t_wall:.2f} s")
+
+    traffic = measured_traffic(f"fwd_kernel:{w.name}:noncausal")
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name}_noncausal", "B": w.B, "H": w.H, "N_q": w.n_q, "N_k": w.n_k, "d": w.d,
+                   "causal": False, "scale": w.scale, "inputs": "iid N(0,1) fp32 -> bf16 RNE, seeded"},
+        "roofline": {"kernel": "fwd_kernel<128,4,false>", "bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "algorithmic_flop_per_launch": flop, "algorithmic_bytes_per_launch": w.io_bytes()},
+    }
+
+    if not args.no_extra:
+        extra = []
+        steps_x = max(5, args.steps // 2)
+        for wx, cx in ((workloads.C4, True), (workloads.C3, False), (workloads.C3, True), (workloads.C2, False),
+                       (workloads.C2, True), (workloads.C1, False)):
+            qx, kx, vx = workloads.make_qkv(wx, dev)
+            ox = torch.empty_like(qx)
+            lx = torch.empty((wx.B, wx.H, wx.n_q), dtype=torch.float32, device=dev)
+            msx = time_launches(lambda: fa2.forward(qx, kx, vx, causal=cx, scale=wx.scale, out=ox, lse=lx),
+                                steps_x, args.warmup)
+            tf = wx.flop(cx) / (msx * 1e-3) / 1e12
+            extra.append({"workload": wx.name, "causal": cx, "ms": round(msx, 4), "TFLOP/s": round(tf, 2),
+                          "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+            log(f"{wx.name} causal={cx}: {msx:.3f} ms, {tf:.1f} TFLOP/s")
+            del qx, kx, vx, ox, lx
+        # split-KV decode: bound by streaming K and V from HBM
+        wd = workloads.C5
+        qd, kd, vd = workloads.make_qkv(wd, dev)
+        od = torch.empty_like(qd)
+        ld = torch.empty((wd.B, wd.H, wd.n_q), dtype=torch.float32, device=dev)
+        ws = torch.empty(fa2.splitkv_workspace_bytes(wd.B, wd.H, wd.n_q, wd.d, wd.num_splits) // 4,
+                         dtype=torch.float32, device=dev)
+        msd = time_launches(lambda: fa2.forward_splitkv(qd, kd, vd, num_splits=wd.num_splits, scale=wd.scale,
+                                                        workspace=ws, out=od, lse=ld), steps_x, args.warmup)
+        gbs = wd.io_bytes() / (msd * 1e-3) / 1e9
+        extra.append({"workload": wd.name, "causal": False, "ms": round(msd, 4), "GB/s": round(gbs, 1),
+                      "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                      "TFLOP/s": round(wd.flop(False) / (msd * 1e-3) / 1e12, 3),
+                      "algorithmic_bytes": wd.io_bytes(),
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                   "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                   "traffic": measured_traffic(f"splitkv:{wd.name}")}})
+        log(f"{wd.name}: {msd:.3f} ms, {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s)")
+        del qd, kd, vd, od, ld, ws
+        result["workloads"] = extra
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, causal, q, k, v)
+        log(f"oracle: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,17 @@
+"""FlashAttention-2 style exact-attention forward for AMD MI355X (gfx950).
+
+The computation runs entirely in the HIP kernels of ``libfa2.so`` behind the
+C ABI of ``include/fa2.h``; this package only marshals torch tensors (device
+memory and the current stream) into those calls.  There is no CPU fallback:
+if the library is missing or a GPU is absent the calls raise.
+"""
+from ._binding import (  # noqa: F401
+    FA2_MAX_SPLITS,
+    Fa2Error,
+    forward,
+    forward_splitkv,
+    lib_path,
+    load_library,
+    splitkv_workspace_bytes,
+    status_string,
+)

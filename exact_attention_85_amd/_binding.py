@@ -1,0 +1,131 @@
+"""ctypes binding of libfa2.so (names as in include/fa2.h).
+
+Argument marshalling only: dtype/device/contiguity checks, output and
+workspace allocation with torch, and the raw stream handle.  Every step of the
+attention computation runs in the library's kernels.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libfa2.so")
+FA2_MAX_SPLITS = 256
+
+_lib = None
+
+
+class Fa2Error(RuntimeError):
+    """A non-zero fa2_status returned by the library."""
+
+    def __init__(self, status: int, text: str):
+        super().__init__(text)
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Loads libfa2.so (built by __graft_entry__.build() or exact_attention_85_amd/build.py).
+    Raises if it is missing: there is no fallback path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run exact_attention_85_amd/build.py first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa2_fwd.restype = i
+    lib.fa2_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa2_splitkv_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa2_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, ctypes.c_size_t, vp]
+    lib.fa2_fwd_splitkv.restype = i
+    lib.fa2_status_string.argtypes = [i]
+    lib.fa2_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().fa2_status_string(int(status)).decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise Fa2Error(rc, status_string(rc))
+
+
+def _check_inputs(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be a bfloat16 torch tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must live on the GPU")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on the same device")
+    B, H, n_q, d = q.shape
+    n_k = k.shape[2]
+    if tuple(k.shape) != (B, H, n_k, d) or tuple(v.shape) != (B, H, n_k, d):
+        raise ValueError("k and v must be [B, H, N_k, d] with q's B, H, d")
+    return B, H, n_q, n_k, d
+
+
+def _scale(scale, d):
+    return float(1.0 / math.sqrt(d)) if scale is None else float(scale)
+
+
+def _stream_handle(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def forward(q, k, v, causal: bool = False, scale=None, out=None, lse=None):
+    """O = softmax(scale * Q K^T [+ causal mask]) V and LSE, via fa2_fwd.
+
+    q: [B, H, N_q, d], k, v: [B, H, N_k, d] bf16 contiguous on the GPU.
+    Returns (o [B, H, N_q, d] bf16, lse [B, H, N_q] fp32).  The work is
+    enqueued on torch's current stream of q's device."""
+    lib = load_library()
+    B, H, n_q, n_k, d = _check_inputs(q, k, v)
+    if out is None:
+        out = torch.empty((B, H, n_q, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    rc = lib.fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                     B, H, n_q, n_k, d, int(bool(causal)), _scale(scale, d), _stream_handle(q.device))
+    _check(rc)
+    return out, lse
+
+
+def splitkv_workspace_bytes(B, H, n_q, d, num_splits) -> int:
+    return int(load_library().fa2_splitkv_workspace_bytes(B, H, n_q, d, num_splits))
+
+
+def forward_splitkv(q, k, v, num_splits: int = 16, causal: bool = False, scale=None, workspace=None,
+                    out=None, lse=None):
+    """Same result as forward(), with the key sequence split into num_splits chunks
+    (fp32 partials in a workspace, then a merge pass), via fa2_fwd_splitkv.
+
+    Returns (o, lse, workspace); the workspace holds the per-chunk partials
+    acc [S][R][d], m [S][R], l [S][R] (R = B*H*N_q) as fp32."""
+    lib = load_library()
+    B, H, n_q, n_k, d = _check_inputs(q, k, v)
+    need = lib.fa2_splitkv_workspace_bytes(B, H, n_q, d, int(num_splits))
+    if workspace is None:
+        workspace = torch.empty((max(need, 4) + 3) // 4, dtype=torch.float32, device=q.device)
+    if out is None:
+        out = torch.empty((B, H, n_q, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    rc = lib.fa2_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                             B, H, n_q, n_k, d, int(bool(causal)), _scale(scale, d), int(num_splits),
+                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                             _stream_handle(q.device))
+    _check(rc)
+    return out, lse, workspace

@@ -1,0 +1,138 @@
+// Host side of the C ABI declared in include/fa2.h: argument validation (pure
+// CPU, before any HIP call), kernel dispatch and status strings.
+#include "fa2.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa2_internal.h"
+
+namespace {
+
+constexpr long long kMaxGrid = (1LL << 31) - 1;
+constexpr long long kMaxHeadElems = (1LL << 31) - 1;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+Range range_of(const void* p, long long bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+// Shapes, head dim and scale shared by both entry points.
+int check_common(const void* Q, const void* K, const void* V, const void* O, const float* LSE, int B, int H,
+                 int N_q, int N_k, int d, float scale) {
+  if (!Q || !K || !V || !O || !LSE) return FA2_ERR_NULLPTR;
+  if (B < 1 || H < 1 || N_q < 1 || N_k < 1) return FA2_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return FA2_ERR_HEAD_DIM;
+  if ((long long)N_q * d > kMaxHeadElems || (long long)N_k * d > kMaxHeadElems) return FA2_ERR_BAD_SHAPE;
+  if ((long long)B * H > kMaxGrid) return FA2_ERR_BAD_SHAPE;
+  // |scale| * log2(e) must stay finite in fp32
+  if (!isfinite(scale) || fabsf(scale) > 2.0e38f) return FA2_ERR_BAD_SCALE;
+  return FA2_OK;
+}
+
+int check_alias(const void* Q, const void* K, const void* V, const void* O, const float* LSE, int B, int H, int N_q,
+                int N_k, int d, const void* ws, size_t ws_bytes) {
+  const long long bh = (long long)B * H;
+  const Range q = range_of(Q, bh * N_q * d * 2), k = range_of(K, bh * N_k * d * 2),
+              v = range_of(V, bh * N_k * d * 2);
+  const Range o = range_of(O, bh * N_q * d * 2), l = range_of(LSE, bh * N_q * 4);
+  if (overlap(o, q) || overlap(o, k) || overlap(o, v) || overlap(o, l)) return FA2_ERR_ALIAS;
+  if (overlap(l, q) || overlap(l, k) || overlap(l, v)) return FA2_ERR_ALIAS;
+  if (ws) {
+    const Range w = range_of(ws, (long long)ws_bytes);
+    if (overlap(w, q) || overlap(w, k) || overlap(w, v) || overlap(w, o) || overlap(w, l)) return FA2_ERR_ALIAS;
+  }
+  return FA2_OK;
+}
+
+fa2::FwdParams make_params(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q,
+                           int N_k, int d, int causal, float scale) {
+  fa2::FwdParams p{};
+  p.q = static_cast<const uint16_t*>(Q);
+  p.k = static_cast<const uint16_t*>(K);
+  p.v = static_cast<const uint16_t*>(V);
+  p.o = static_cast<uint16_t*>(O);
+  p.lse = LSE;
+  p.B = B;
+  p.H = H;
+  p.n_q = N_q;
+  p.n_k = N_k;
+  p.d = d;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.num_splits = 1;
+  p.split_len = N_k;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q, int N_k, int d,
+            int causal, float scale, void* stream) {
+  int rc = check_common(Q, K, V, O, LSE, B, H, N_q, N_k, d, scale);
+  if (rc != FA2_OK) return rc;
+  const int br = 128;  // query rows per workgroup of the forward kernel
+  if ((long long)((N_q + br - 1) / br) * B * H > kMaxGrid) return FA2_ERR_BAD_SHAPE;
+  rc = check_alias(Q, K, V, O, LSE, B, H, N_q, N_k, d, nullptr, 0);
+  if (rc != FA2_OK) return rc;
+  const fa2::FwdParams p = make_params(Q, K, V, O, LSE, B, H, N_q, N_k, d, causal, scale);
+  if (fa2::launch_fwd(p, static_cast<hipStream_t>(stream)) != hipSuccess) return FA2_ERR_HIP;
+  return FA2_OK;
+}
+
+size_t fa2_splitkv_workspace_bytes(int B, int H, int N_q, int d, int num_splits) {
+  if (B < 1 || H < 1 || N_q < 1 || d < 1 || num_splits < 1 || num_splits > FA2_MAX_SPLITS) return 0;
+  return (size_t)num_splits * (size_t)B * (size_t)H * (size_t)N_q * (size_t)(d + 2) * 4u;
+}
+
+int fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q, int N_k,
+                    int d, int causal, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  int rc = check_common(Q, K, V, O, LSE, B, H, N_q, N_k, d, scale);
+  if (rc != FA2_OK) return rc;
+  if (num_splits < 1 || num_splits > FA2_MAX_SPLITS || num_splits > N_k) return FA2_ERR_SPLITS;
+  const int br = 128;
+  if ((long long)((N_q + br - 1) / br) * B * H * num_splits > kMaxGrid) return FA2_ERR_BAD_SHAPE;
+  const size_t need = fa2_splitkv_workspace_bytes(B, H, N_q, d, num_splits);
+  if (!workspace || workspace_bytes < need) return FA2_ERR_WORKSPACE;
+  rc = check_alias(Q, K, V, O, LSE, B, H, N_q, N_k, d, workspace, need);
+  if (rc != FA2_OK) return rc;
+
+  fa2::FwdParams p = make_params(Q, K, V, O, LSE, B, H, N_q, N_k, d, causal, scale);
+  p.num_splits = num_splits;
+  p.split_len = (N_k + num_splits - 1) / num_splits;
+  const long long R = (long long)B * H * N_q;
+  float* ws = static_cast<float*>(workspace);
+  p.ws_acc = ws;
+  p.ws_m = ws + (long long)num_splits * R * d;
+  p.ws_l = p.ws_m + (long long)num_splits * R;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fa2::launch_splitkv_partial(p, s) != hipSuccess) return FA2_ERR_HIP;
+  if (fa2::launch_splitkv_merge(p, s) != hipSuccess) return FA2_ERR_HIP;
+  return FA2_OK;
+}
+
+const char* fa2_status_string(int status) {
+  switch (status) {
+    case FA2_OK: return "FA2_OK: success";
+    case FA2_ERR_NULLPTR: return "FA2_ERR_NULLPTR: a required pointer is NULL";
+    case FA2_ERR_BAD_SHAPE: return "FA2_ERR_BAD_SHAPE: B, H, N_q, N_k must be >= 1 and within the size limits";
+    case FA2_ERR_HEAD_DIM: return "FA2_ERR_HEAD_DIM: head dim d must be 64 or 128";
+    case FA2_ERR_BAD_SCALE: return "FA2_ERR_BAD_SCALE: scale must be finite with |scale| <= 2e38";
+    case FA2_ERR_WORKSPACE: return "FA2_ERR_WORKSPACE: split-KV workspace missing or too small";
+    case FA2_ERR_ALIAS: return "FA2_ERR_ALIAS: an output overlaps an input, another output or the workspace";
+    case FA2_ERR_SPLITS: return "FA2_ERR_SPLITS: num_splits must be in [1, min(N_k, FA2_MAX_SPLITS)]";
+    case FA2_ERR_HIP: return "FA2_ERR_HIP: the HIP runtime rejected a kernel launch";
+    default: return "unknown fa2 status";
+  }
+}
+
+}  // extern "C"

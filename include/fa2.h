@@ -1,0 +1,127 @@
+/*
+ * fa2.h — FlashAttention-2 style exact-attention forward for AMD MI355X (gfx950).
+ *
+ * C ABI.  Every tensor argument is a DEVICE pointer owned by the caller
+ * (for example the data pointer of a torch tensor); the library never
+ * allocates, frees or synchronises, keeps no state between calls and only
+ * enqueues work on `stream` (a hipStream_t passed as void*; NULL = the
+ * default stream).  Calls return as soon as the work is enqueued.
+ *
+ * Layouts (contiguous, row-major):
+ *   Q   [B][H][N_q][d]   bf16 (raw 16-bit storage)
+ *   K,V [B][H][N_k][d]   bf16
+ *   O   [B][H][N_q][d]   bf16, rounded to nearest even from fp32
+ *   LSE [B][H][N_q]      fp32, natural logarithm
+ *
+ * What is computed (the FlashAttention-2 source walkthrough page, "kernel main
+ * loop" section: the online-softmax pseudocode, whose result is exact
+ * attention; the epilogue writes O and the log-sum-exp):
+ *   s_ij   = scale * sum_c Q[i][c] * K[j][c]
+ *   key j is visible to query i iff j < N_k and, when causal != 0, j <= i
+ *            (top-left alignment, so every query row sees key 0)
+ *   O[i]   = sum_j softmax_j(s_ij) * V[j]      over visible keys
+ *   LSE[i] = log(sum_j exp(s_ij))              over visible keys
+ * Products are formed from the bf16 inputs, accumulated in fp32; the
+ * probabilities are rounded to bf16 before the P.V product and the softmax
+ * denominator is summed from the fp32 probabilities.
+ *
+ * Errors: every argument is validated on the host BEFORE any HIP call, and a
+ * negative fa2_status is returned with nothing enqueued.  FA2_ERR_HIP means
+ * a launch was rejected by the runtime (hipGetLastError).  Faults during
+ * execution surface at the caller's next synchronisation.  No C++ exception
+ * crosses this interface.  Overlapping calls on different streams that share
+ * output buffers race; the library does not detect that.
+ */
+#ifndef FA2_H_
+#define FA2_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa2_status {
+  FA2_OK = 0,
+  FA2_ERR_NULLPTR = -1,   /* a required pointer is NULL */
+  FA2_ERR_BAD_SHAPE = -2, /* B, H, N_q, N_k < 1, or a size beyond the limits below */
+  FA2_ERR_HEAD_DIM = -3,  /* d is not 64 or 128 */
+  FA2_ERR_BAD_SCALE = -4, /* scale is not finite */
+  FA2_ERR_WORKSPACE = -5, /* split-KV workspace NULL or smaller than fa2_splitkv_workspace_bytes() */
+  FA2_ERR_ALIAS = -6,     /* an output overlaps an input, another output or the workspace */
+  FA2_ERR_SPLITS = -7,    /* num_splits outside [1, min(N_k, FA2_MAX_SPLITS)] */
+  FA2_ERR_HIP = -8        /* the HIP runtime rejected a kernel launch */
+} fa2_status;
+
+/* Size limits (validated): N_k * d and N_q * d below 2^31 per head, and the
+ * launch grid below 2^31 workgroups. */
+#define FA2_MAX_SPLITS 256
+
+/*
+ * fa2_fwd — exact attention forward (the FlashAttention-2 forward pass).
+ *
+ * Launch shape (the walkthrough page, "launch grid" section: one workgroup
+ * per query block, batch and head, with the query sequence split into
+ * blocks): ceil(N_q / B_r) * B * H workgroups, B_r query rows each; every
+ * workgroup streams the K/V blocks its rows can see (the synthesis page,
+ * section 2 item 2: queries on the outer loop, keys/values on the inner loop,
+ * no inter-workgroup communication).  With causal != 0, key blocks above the
+ * diagonal are skipped and only diagonal blocks are masked.
+ *
+ * Q, K, V, O, LSE: device pointers as laid out above.  O and LSE must not
+ * overlap Q, K, V or each other.
+ * B, H, N_q, N_k: >= 1.   d: 64 or 128.   causal: 0 or non-zero.
+ * scale: finite multiplier of q.k (callers usually pass fp32(1/sqrt(d))).
+ * stream: hipStream_t or NULL.
+ * Returns FA2_OK or a negative fa2_status.
+ */
+int fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+            int B, int H, int N_q, int N_k, int d, int causal, float scale, void* stream);
+
+/*
+ * fa2_splitkv_workspace_bytes — bytes of caller-owned device workspace that
+ * fa2_fwd_splitkv needs: num_splits * B * H * N_q * (d + 2) * 4.
+ * Returns 0 when an argument is out of range.
+ */
+size_t fa2_splitkv_workspace_bytes(int B, int H, int N_q, int d, int num_splits);
+
+/*
+ * fa2_fwd_splitkv — the same result as fa2_fwd, computed by splitting the key
+ * sequence into num_splits chunks (the synthesis page, section 5 item 5: for
+ * single-query decode the query-block parallelism vanishes, so parallelise
+ * over the key/value sequence and merge the partial results).
+ *
+ * Chunk c covers keys [c*L, min((c+1)*L, N_k)), L = ceil(N_k / num_splits);
+ * a chunk may be empty.  Pass 1 writes, per chunk and query row, the fp32
+ * partial (acc, m, l) into the workspace:
+ *   m   = max of the chunk's visible scaled scores s_ij (natural-log units),
+ *         -inf when the chunk holds no visible key;
+ *   l   = sum over the chunk of exp(s_ij - m)            (0 when empty);
+ *   acc = sum over the chunk of exp(s_ij - m) * V[j]     (0 when empty).
+ * Pass 2 merges them in chunk order: M = max_c m_c, w_c = exp(m_c - M)
+ * (0 for an empty chunk), O = (sum_c w_c acc_c) / (sum_c w_c l_c),
+ * LSE = M + log(sum_c w_c l_c) — the same rescaling as the online softmax
+ * (walkthrough page, main-loop pseudocode).
+ *
+ * Workspace layout (fp32, R = B*H*N_q rows, row = (b*H + h)*N_q + i):
+ *   acc [num_splits][R][d], then m [num_splits][R], then l [num_splits][R].
+ * Its contents after the call are the partials above; it must not overlap
+ * any input or output.  Both passes run in order on `stream`.
+ *
+ * Other arguments and errors as fa2_fwd, plus:
+ * num_splits: 1 <= num_splits <= min(N_k, FA2_MAX_SPLITS).
+ * workspace, workspace_bytes: device buffer of at least
+ *   fa2_splitkv_workspace_bytes(B, H, N_q, d, num_splits) bytes.
+ */
+int fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                    int B, int H, int N_q, int N_k, int d, int causal, float scale,
+                    int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* fa2_status_string — static, human-readable text for a status code. */
+const char* fa2_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H_ */
