@@ -10,7 +10,7 @@
 namespace {
 
 constexpr long long kMaxGrid = (1LL << 31) - 1;
-constexpr long long kMaxHeadElems = (1LL << 31) - 1;
+constexpr long long kMaxHeadElems = (1LL << 30) - 1;  // one head's Q or K/V below 2^31 bytes
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)

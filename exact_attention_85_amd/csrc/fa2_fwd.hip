@@ -80,6 +80,15 @@ __device__ __forceinline__ f32x8 slice8(const f32x16& s, int t) {
 }
 
 // ---------------------------------------------------------------------------
+// Buffer resource over [base, base + bytes): loads whose per-lane offset lies
+// beyond `bytes` return zero, which is how ragged query/key tails are
+// zero-filled without branches.  The host limits one head to < 2^31 bytes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
 // Forward / split-KV partial kernel.
 //   D   head dim (64 or 128)
 //   NW  waves per workgroup; the query block is B_r = 32*NW rows
@@ -88,21 +97,34 @@ __device__ __forceinline__ f32x8 slice8(const f32x16& s, int t) {
 // Kernel arguments beyond FwdParams: sl2 = max(|scale| * log2 e, FLT_MIN) and
 // qsign = 0x80008000 when scale < 0 (Q is negated in registers so that the
 // folded multiplier stays positive), else 0.
+//
+// K/V tiles go straight from HBM/L2 into LDS (buffer_load ... lds): lane i of
+// a load writes LDS slot (M0 + 16 i), so each lane fetches the (row, chunk)
+// whose swizzled slot it owns.  Tile j+1 is in flight while tile j computes;
+// one barrier per tile both publishes tile j and retires tile j-1's buffer.
+//
+// The O accumulator is rescaled only on tiles where some row of the wave
+// finds a new maximum (alpha = 1 for every row otherwise); the running maximum
+// itself stays exact, so the largest probability of each row is exactly 1
+// before its conversion to bf16.
+
 template <int D, int NW, bool SPLIT>
-__global__ void __launch_bounds__(64 * NW) fwd_kernel(FwdParams p, float sl2, unsigned qsign) {
+__global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float sl2, unsigned qsign) {
   constexpr int T = 64 * NW;
   constexpr int BR = 32 * NW;
   constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int SLOTS = kBC * CPR;    // slots per tile per tensor
-  constexpr int NLD = SLOTS / T;      // 16-byte global loads per thread per tensor per tile
+  constexpr int NLD = SLOTS / T;      // buffer->LDS loads per thread per tensor per tile
   constexpr int KT = D / 16;          // k-steps of Q K^T
   constexpr int NB = D / 32;          // 32-wide blocks of the head dim in O^T
+  constexpr int TILE_BYTES = SLOTS * 16;
   static_assert(SLOTS % T == 0, "tile must split evenly over the threads");
 
-  __shared__ u32x4 lds[2][2][SLOTS];  // [stage][K=0 / V=1][slot]
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][TILE_BYTES];  // [stage][K=0 / V=1]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5;           // which 8-wide k half of an MFMA operand this lane holds
   const int col = lane & 31;          // query row (within the wave) of this lane
   const int j16 = lane & 15, cg = (lane >> 4) & 1;
@@ -137,71 +159,58 @@ __global__ void __launch_bounds__(64 * NW) fwd_kernel(FwdParams p, float sl2, un
   const int n_tiles = khi > kbeg ? (khi - kbeg + kBC - 1) / kBC : 0;
 
   const uint16_t* Qh = p.q + (long long)bh * p.n_q * D;
-  const uint16_t* Kh = p.k + (long long)bh * p.n_k * D;
-  const uint16_t* Vh = p.v + (long long)bh * p.n_k * D;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + (long long)bh * p.n_k * D, (long long)khi * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + (long long)bh * p.n_k * D, (long long)khi * D * 2);
 
   // ---- Q fragment: B operand of S^T = K Q^T; lane holds Q[row][16t + 8hf .. +7] ----
   bf16x8 qf[KT];
   {
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qh, (long long)p.n_q * D * 2);
     const u32x4 sign = {qsign, qsign, qsign, qsign};
-    if (row < p.n_q) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(Qh + (long long)row * D);
 #pragma unroll
-      for (int t = 0; t < KT; ++t) qf[t] = as_bf16x8(src[2 * t + hf] ^ sign);
-    } else {
-#pragma unroll
-      for (int t = 0; t < KT; ++t) qf[t] = as_bf16x8(u32x4{0, 0, 0, 0});
+    for (int t = 0; t < KT; ++t) {
+      const u32x4 raw = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, (unsigned)((row * D + 16 * t + 8 * hf) * 2), 0, 0));
+      qf[t] = as_bf16x8(raw ^ sign);
     }
   }
 
-  // ---- K/V tile staging: global -> registers -> LDS ----
-  u32x4 kreg[NLD], vreg[NLD];
-  auto gload = [&](int k0) {
+  // ---- buffer->LDS tile loads ----
+  // Load i of this wave fills physical slots (i*NW + wave)*64 .. +63; the lane
+  // owning slot s fetches the (row, chunk) that the swizzle stores there.  The
+  // whole byte offset goes in the per-lane voffset, which the range check uses.
+  auto issue_tile = [&](int k0, int st) {
+    const unsigned toff = (unsigned)k0 * D * 2;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int u = tid + i * T;
-      const int r = u / CPR, c = u % CPR;
-      const int key = k0 + r;
-      if (key < khi) {
-        const long long off = (long long)key * D + c * 8;
-        kreg[i] = *reinterpret_cast<const u32x4*>(Kh + off);
-        vreg[i] = *reinterpret_cast<const u32x4*>(Vh + off);
-      } else {
-        kreg[i] = u32x4{0, 0, 0, 0};
-        vreg[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto sstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int u = tid + i * T;
-      const int s = swz<D>(u / CPR, u % CPR);
-      lds[st][0][s] = kreg[i];
-      lds[st][1][s] = vreg[i];
+      const int s = (i * NW + wave) * 64 + lane;
+      const int r = s / CPR;
+      const int c = (s % CPR) ^ (swz<D>(r, 0) - r * CPR);
+      const unsigned off = (unsigned)((r * D + c * 8) * 2) + toff;
+      const int sbase = (i * NW + wave) * 64 * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(&lds[st][0][sbase]), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(&lds[st][1][sbase]), 16, off, 0, 0, 0);
     }
   };
 
   f32x16 acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
-  float m_run = -INFINITY;  // running max of the scaled scores, log2 units
+  float m_run = -INFINITY;  // reference maximum of the scaled scores, log2 units
   float l_run = 0.f;        // this lane's share of the running denominator
 
-  if (n_tiles > 0) {
-    gload(kbeg);
-    sstore(0);
-  }
-  __syncthreads();
+  if (n_tiles > 0) issue_tile(kbeg, 0);
 
   for (int j = 0; j < n_tiles; ++j) {
     const int k0 = kbeg + j * kBC;
     const int st = j & 1;
-    if (j + 1 < n_tiles) gload(k0 + kBC);  // prefetch the next tile while this one computes
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 1 < n_tiles) issue_tile(k0 + kBC, st ^ 1);
 
     if (k0 < khi_w) {
-      const u32x4* Kt = lds[st][0];
-      const char* Vt = reinterpret_cast<const char*>(lds[st][1]);
+      const char* Kt = lds[st][0];
+      const char* Vt = lds[st][1];
 
       // S^T = K Q^T : two 32-key blocks
       f32x16 s[2];
@@ -210,7 +219,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_kernel(FwdParams p, float sl2, un
         s[kb] = f32x16{};
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
-          const bf16x8 a = as_bf16x8(Kt[swz<D>(kb * 32 + col, 2 * t + hf)]);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kt + swz<D>(kb * 32 + col, 2 * t + hf) * 16);
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kb], 0, 0, 0);
         }
       }
@@ -232,10 +241,15 @@ __global__ void __launch_bounds__(64 * NW) fwd_kernel(FwdParams p, float sl2, un
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * sl2);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+      const float m_new = fmaxf(m_run, mx);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      if (__ballot(m_new > m_run)) {  // some row of this wave has a new maximum
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        l_run *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
+      }
       m_run = m_new;
 
       float rs = 0.f;
@@ -247,11 +261,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_kernel(FwdParams p, float sl2, un
           s[kb][r] = e;
           rs += e;
         }
-      l_run = l_run * alpha + rs;
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
-      }
+      l_run += rs;
 
       // O^T += V^T P^T.  k-step (kb, t) contracts keys kb*32 + 16t + {4hf..4hf+3, 8+4hf..8+4hf+3}
       // (the keys this lane's S^T registers 8t..8t+7 hold); the A operand is read transposed.
@@ -274,9 +284,6 @@ __global__ void __launch_bounds__(64 * NW) fwd_kernel(FwdParams p, float sl2, un
           }
         }
     }
-
-    if (j + 1 < n_tiles) sstore(st ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue ----

@@ -53,8 +53,8 @@ typedef enum fa2_status {
   FA2_ERR_HIP = -8        /* the HIP runtime rejected a kernel launch */
 } fa2_status;
 
-/* Size limits (validated): N_k * d and N_q * d below 2^31 per head, and the
- * launch grid below 2^31 workgroups. */
+/* Size limits (validated): N_k * d and N_q * d below 2^30 per head (one
+ * head's Q, K or V under 2 GiB), and the launch grid below 2^31 workgroups. */
 #define FA2_MAX_SPLITS 256
 
 /*

@@ -64,7 +64,7 @@ def test_null_pointers(which):
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(nq=0), dict(nk=0), dict(B=-1), dict(nk=-5),
-                                dict(nk=(1 << 31) // 64 + 1), dict(nq=(1 << 31) // 64 + 1)])
+                                dict(nk=(1 << 30) // 64 + 1), dict(nq=(1 << 30) // 64 + 1)])
 def test_bad_shapes(kw):
     assert fwd(**kw) == BAD_SHAPE
 
