@@ -89,6 +89,188 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, lo
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Per-wave state of one 32-row query block: the Q fragment (B operand of
+// S^T = K Q^T; lane holds Q[row][16t + 8hf .. +7]), the O^T accumulator
+// (acc[nb][4g + i] = O^T[32nb + 8g + 4hf + i][row]), the running maximum of
+// the scaled scores in log2 units and this lane's share of the denominator.
+template <int D>
+struct WaveRows {
+  bf16x8 qf[D / 16];
+  f32x16 acc[D / 32];
+  float m_run;
+  float l_run;
+};
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (stride 0) over [base, base + bytes): loads whose
+// per-lane offset lies at or beyond `bytes` return zero.
+__device__ __forceinline__ i32x4 raw_rsrc(const void* base, long long bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  return i32x4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// 16 bytes per lane from buffer `rs` at byte offset voff into LDS at
+// dst + 16*lane (buffer_load_dwordx4 ... lds; M0 holds the LDS base and is
+// restored afterwards).  Issued through asm so that the compiler does not
+// order later LDS reads of the other stage behind it; the kernel waits for
+// these loads itself (s_waitcnt vmcnt(0) before the barrier that publishes a
+// tile).
+__device__ __forceinline__ void lds_dma16(i32x4 rs, const char* dst, unsigned voff) {
+  const unsigned m0v = (unsigned)(uintptr_t)(const lds_void*)dst;
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0v), "v"(voff), "s"(rs)
+      : "memory");
+}
+
+// Issue the loads of one K tile and one V tile (kBC rows from key k0) into
+// LDS.  Load i of a wave fills physical slots (i*NW + wave)*64 .. +63; the
+// lane owning slot s fetches the (row, chunk) that the swizzle stores there.
+// The whole byte offset goes in the per-lane voffset, which the buffer range
+// check applies to.
+template <int D, int NW>
+__device__ __forceinline__ void issue_tile(i32x4 krs, i32x4 vrs, const char* kdst, const char* vdst, int k0,
+                                           int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int NLD = kBC * CPR / (64 * NW);
+  const unsigned toff = (unsigned)k0 * D * 2;
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int s = (i * NW + wave) * 64 + lane;
+    const int r = s / CPR;
+    const int c = (s % CPR) ^ (swz<D>(r, 0) - r * CPR);
+    const unsigned off = (unsigned)((r * D + c * 8) * 2) + toff;
+    const int sbase = (i * NW + wave) * 64 * 16;
+    lds_dma16(krs, kdst + sbase, off);
+    lds_dma16(vrs, vdst + sbase, off);
+  }
+}
+
+// LDS byte addresses a lane reads from, computed once per kernel.  With the
+// XOR swizzle the address of (row, chunk) is not affine in the chunk, so each
+// lane keeps one register per distinct pattern and every other index (key
+// block, k-step, stage) becomes an immediate offset:
+//   ka[t]       K operand: key row col, chunk 2t + hf            (+ kb*32 rows)
+//   va[2nb + h] V^T operand: rows 4hf + j16/4 + 8h, d 32nb + 16cg + 4(j16%4)
+//               (+ kb*32 + 16t rows).  The swizzle repeats every 16 rows, so
+//               whole 16-row steps are plain offsets.
+template <int D>
+struct LdsAddr {
+  unsigned ka[D / 16];
+  unsigned va[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ void make_lds_addr(LdsAddr<D>& a, unsigned base, int lane) {
+  const int hf = lane >> 5, col = lane & 31;
+  const int j16 = lane & 15, cg = (lane >> 4) & 1;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) a.ka[t] = base + swz<D>(col, 2 * t + hf) * 16;
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kr = 4 * hf + (j16 >> 2) + 8 * h;
+      const int dd = 32 * nb + 16 * cg + 4 * (j16 & 3);
+      a.va[2 * nb + h] = base + swz<D>(kr, dd >> 3) * 16 + (dd & 7) * 2;
+    }
+  // opaque to the optimiser: keep these in registers instead of recomputing them per tile
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) asm volatile("" : "+v"(a.ka[i]), "+v"(a.va[i]));
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_load(unsigned addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) T*>((uintptr_t)addr);
+}
+
+// One kBC-key tile for one wave: S^T = K Q^T, mask (only when need_mask),
+// online softmax, O^T += V^T P^T.  KOFF / VOFF: byte offsets of this stage's
+// K and V tiles relative to the addresses in `la`.
+template <int D, unsigned KOFF, unsigned VOFF>
+__device__ __forceinline__ void tile_step(WaveRows<D>& w, const LdsAddr<D>& la, bool need_mask, int k0, int kend,
+                                          int row, int causal, float sl2, int lane) {
+  constexpr int KT = D / 16;
+  constexpr int NB = D / 32;
+  constexpr unsigned ROW = D * 2;  // bytes per tile row
+  const int hf = lane >> 5;
+
+  // S^T = K Q^T over two 32-key blocks, the two accumulation chains interleaved
+  f32x16 s0 = {}, s1 = {};
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    const bf16x8 a0 = lds_load<bf16x8>(la.ka[t] + KOFF);
+    const bf16x8 a1 = lds_load<bf16x8>(la.ka[t] + KOFF + 32 * ROW);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, w.qf[t], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, w.qf[t], s1, 0, 0, 0);
+  }
+  // s{kb}[r] is the score of query `row` against key k0 + kb*32 + 8*(r/4) + 4*hf + r%4
+  if (need_mask) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+      if (key >= kend || (causal && key > row)) s0[r] = -INFINITY;
+      if (key + 32 >= kend || (causal && key + 32 > row)) s1[r] = -INFINITY;
+    }
+  }
+
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+  const float m_new = fmaxf(w.m_run, mx);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  if (__ballot(m_new > w.m_run)) {  // some row of this wave has a new maximum
+    const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_use);
+    w.l_run *= alpha;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) w.acc[nb] *= alpha;
+  }
+  w.m_run = m_new;
+
+  float rs = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], sl2, -m_use));
+    s0[r] = e0;
+    rs += e0;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], sl2, -m_use));
+    s1[r] = e1;
+    rs += e1;
+  }
+  w.l_run += rs;
+
+  // O^T += V^T P^T.  k-step (kb, t) contracts keys kb*32 + 16t + {4hf..4hf+3, 8+4hf..8+4hf+3}
+  // (the keys this lane's S^T registers 8t..8t+7 hold); the A operand is read transposed.
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8 pb = cvt_bf16x8(slice8(kb == 0 ? s0 : s1, t));
+      const unsigned roff = VOFF + (kb * 32 + 16 * t) * ROW;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<lds_i16x4*>((uintptr_t)(la.va[2 * nb] + roff)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<lds_i16x4*>((uintptr_t)(la.va[2 * nb + 1] + roff)));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        w.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, w.acc[nb], 0, 0, 0);
+      }
+    }
+}
+
 // Forward / split-KV partial kernel.
 //   D   head dim (64 or 128)
 //   NW  waves per workgroup; the query block is B_r = 32*NW rows
@@ -98,27 +280,23 @@ typedef __attribute__((address_space(3))) void lds_void;
 // qsign = 0x80008000 when scale < 0 (Q is negated in registers so that the
 // folded multiplier stays positive), else 0.
 //
-// K/V tiles go straight from HBM/L2 into LDS (buffer_load ... lds): lane i of
-// a load writes LDS slot (M0 + 16 i), so each lane fetches the (row, chunk)
-// whose swizzled slot it owns.  Tile j+1 is in flight while tile j computes;
-// one barrier per tile both publishes tile j and retires tile j-1's buffer.
+// K/V tiles go straight from HBM/L2 into LDS (buffer_load ... lds).  Two LDS
+// stages, each its own __shared__ object so that the compiler can see that
+// reading one stage does not depend on the loads in flight into the other:
+// tile j+1 streams in while tile j computes, and one barrier per tile both
+// publishes tile j and retires the buffer of tile j-1.
 //
 // The O accumulator is rescaled only on tiles where some row of the wave
 // finds a new maximum (alpha = 1 for every row otherwise); the running maximum
 // itself stays exact, so the largest probability of each row is exactly 1
 // before its conversion to bf16.
-
 template <int D, int NW, bool SPLIT>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float sl2, unsigned qsign) {
-  constexpr int T = 64 * NW;
   constexpr int BR = 32 * NW;
-  constexpr int CPR = D / 8;          // 16-byte chunks per row
-  constexpr int SLOTS = kBC * CPR;    // slots per tile per tensor
-  constexpr int NLD = SLOTS / T;      // buffer->LDS loads per thread per tensor per tile
-  constexpr int KT = D / 16;          // k-steps of Q K^T
-  constexpr int NB = D / 32;          // 32-wide blocks of the head dim in O^T
-  constexpr int TILE_BYTES = SLOTS * 16;
-  static_assert(SLOTS % T == 0, "tile must split evenly over the threads");
+  constexpr int KT = D / 16;
+  constexpr int NB = D / 32;
+  constexpr int TILE_BYTES = kBC * D * 2;
+  static_assert((kBC * D / 8) % (64 * NW) == 0, "tile must split evenly over the threads");
 
   __shared__ __attribute__((aligned(1024))) char lds[2][2][TILE_BYTES];  // [stage][K=0 / V=1]
 
@@ -127,7 +305,6 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5;           // which 8-wide k half of an MFMA operand this lane holds
   const int col = lane & 31;          // query row (within the wave) of this lane
-  const int j16 = lane & 15, cg = (lane >> 4) & 1;
 
   // ---- workgroup -> (batch*head, query block, key chunk) ----
   const int n_qb = (p.n_q + BR - 1) / BR;
@@ -159,11 +336,10 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
   const int n_tiles = khi > kbeg ? (khi - kbeg + kBC - 1) / kBC : 0;
 
   const uint16_t* Qh = p.q + (long long)bh * p.n_q * D;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + (long long)bh * p.n_k * D, (long long)khi * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + (long long)bh * p.n_k * D, (long long)khi * D * 2);
+  const i32x4 krs = raw_rsrc(p.k + (long long)bh * p.n_k * D, (long long)khi * D * 2);
+  const i32x4 vrs = raw_rsrc(p.v + (long long)bh * p.n_k * D, (long long)khi * D * 2);
 
-  // ---- Q fragment: B operand of S^T = K Q^T; lane holds Q[row][16t + 8hf .. +7] ----
-  bf16x8 qf[KT];
+  WaveRows<D> w;
   {
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qh, (long long)p.n_q * D * 2);
     const u32x4 sign = {qsign, qsign, qsign, qsign};
@@ -171,125 +347,47 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
     for (int t = 0; t < KT; ++t) {
       const u32x4 raw = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, (unsigned)((row * D + 16 * t + 8 * hf) * 2), 0, 0));
-      qf[t] = as_bf16x8(raw ^ sign);
+      w.qf[t] = as_bf16x8(raw ^ sign);
     }
   }
-
-  // ---- buffer->LDS tile loads ----
-  // Load i of this wave fills physical slots (i*NW + wave)*64 .. +63; the lane
-  // owning slot s fetches the (row, chunk) that the swizzle stores there.  The
-  // whole byte offset goes in the per-lane voffset, which the range check uses.
-  auto issue_tile = [&](int k0, int st) {
-    const unsigned toff = (unsigned)k0 * D * 2;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int s = (i * NW + wave) * 64 + lane;
-      const int r = s / CPR;
-      const int c = (s % CPR) ^ (swz<D>(r, 0) - r * CPR);
-      const unsigned off = (unsigned)((r * D + c * 8) * 2) + toff;
-      const int sbase = (i * NW + wave) * 64 * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(&lds[st][0][sbase]), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(&lds[st][1][sbase]), 16, off, 0, 0, 0);
-    }
-  };
+  for (int nb = 0; nb < NB; ++nb) w.acc[nb] = f32x16{};
+  w.m_run = -INFINITY;
+  w.l_run = 0.f;
 
-  f32x16 acc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
-  float m_run = -INFINITY;  // reference maximum of the scaled scores, log2 units
-  float l_run = 0.f;        // this lane's share of the running denominator
+  LdsAddr<D> la;
+  make_lds_addr<D>(la, (unsigned)(uintptr_t)(const lds_void*)&lds[0][0][0], lane);
+  constexpr unsigned STAGE = 2 * TILE_BYTES;
 
-  if (n_tiles > 0) issue_tile(kbeg, 0);
+  // a tile needs masking when it crosses this wave's causal diagonal or the key tail
+#define FA2_STEP(STG, k0_)                                                                             \
+  do {                                                                                               \
+    const int kk = (k0_);                                                                            \
+    if (kk < khi_w)                                                                                  \
+      tile_step<D, STG * STAGE, STG * STAGE + TILE_BYTES>(                                           \
+          w, la, (kk + kBC > kend) || (p.causal && kk + kBC - 1 > q0w), kk, kend, row, p.causal, sl2, lane); \
+  } while (0)
 
-  for (int j = 0; j < n_tiles; ++j) {
+  // unrolled by two so that each stage's LDS offsets are compile-time constants
+  if (n_tiles > 0) issue_tile<D, NW>(krs, vrs, lds[0][0], lds[0][1], kbeg, wave, lane);
+  for (int j = 0; j < n_tiles; j += 2) {
     const int k0 = kbeg + j * kBC;
-    const int st = j & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (j + 1 < n_tiles) issue_tile(k0 + kBC, st ^ 1);
-
-    if (k0 < khi_w) {
-      const char* Kt = lds[st][0];
-      const char* Vt = lds[st][1];
-
-      // S^T = K Q^T : two 32-key blocks
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-#pragma unroll
-        for (int t = 0; t < KT; ++t) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kt + swz<D>(kb * 32 + col, 2 * t + hf) * 16);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kb], 0, 0, 0);
-        }
-      }
-      // s[kb][r] is the score of query `row` against key k0 + kb*32 + 8*(r/4) + 4*hf + r%4
-
-      const bool need_mask = (k0 + kBC > kend) || (p.causal && k0 + kBC - 1 > q0w);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key >= kend || (p.causal && key > row)) s[kb][r] = -INFINITY;
-          }
-      }
-
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      if (__ballot(m_new > m_run)) {  // some row of this wave has a new maximum
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        l_run *= alpha;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
-      }
-      m_run = m_new;
-
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sl2, -m_use));
-          s[kb][r] = e;
-          rs += e;
-        }
-      l_run += rs;
-
-      // O^T += V^T P^T.  k-step (kb, t) contracts keys kb*32 + 16t + {4hf..4hf+3, 8+4hf..8+4hf+3}
-      // (the keys this lane's S^T registers 8t..8t+7 hold); the A operand is read transposed.
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 pb = cvt_bf16x8(slice8(s[kb], t));
-          const int kr = kb * 32 + 16 * t + 4 * hf + (j16 >> 2);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const int dd = 32 * nb + 16 * cg + 4 * (j16 & 3);
-            const int boff = (dd & 7) * 2;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(Vt + swz<D>(kr, dd >> 3) * 16 + boff));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(Vt + swz<D>(kr + 8, dd >> 3) * 16 + boff));
-            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[nb], 0, 0, 0);
-          }
-        }
+    if (j + 1 < n_tiles) issue_tile<D, NW>(krs, vrs, lds[1][0], lds[1][1], k0 + kBC, wave, lane);
+    FA2_STEP(0, k0);
+    if (j + 1 < n_tiles) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (j + 2 < n_tiles) issue_tile<D, NW>(krs, vrs, lds[0][0], lds[0][1], k0 + 2 * kBC, wave, lane);
+      FA2_STEP(1, k0 + kBC);
     }
   }
+#undef FA2_STEP
 
   // ---- epilogue ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = w.l_run + __shfl_xor(w.l_run, 32);
   if (row >= p.n_q) return;
-  // acc[nb][4g + i] = O^T[32nb + 8g + 4hf + i][row]
   if (!SPLIT) {
     const float inv = 1.f / l_tot;
     uint16_t* Orow = p.o + ((long long)bh * p.n_q + row) * D;
@@ -297,13 +395,13 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 o4 = {acc[nb][4 * g] * inv, acc[nb][4 * g + 1] * inv, acc[nb][4 * g + 2] * inv,
-                          acc[nb][4 * g + 3] * inv};
+        const f32x4 o4 = {w.acc[nb][4 * g] * inv, w.acc[nb][4 * g + 1] * inv, w.acc[nb][4 * g + 2] * inv,
+                          w.acc[nb][4 * g + 3] * inv};
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         const bf16x4 b4 = __builtin_convertvector(o4, bf16x4);
         *reinterpret_cast<u32x2*>(Orow + 32 * nb + 8 * g + 4 * hf) = __builtin_bit_cast(u32x2, b4);
       }
-    if (hf == 0) p.lse[(long long)bh * p.n_q + row] = (m_run + __log2f(l_tot)) * kLn2;
+    if (hf == 0) p.lse[(long long)bh * p.n_q + row] = (w.m_run + __log2f(l_tot)) * kLn2;
   } else {
     const long long R = (long long)p.B * p.H * p.n_q;
     const long long rg = (long long)bh * p.n_q + row;
@@ -312,11 +410,11 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 o4 = {acc[nb][4 * g], acc[nb][4 * g + 1], acc[nb][4 * g + 2], acc[nb][4 * g + 3]};
+        const f32x4 o4 = {w.acc[nb][4 * g], w.acc[nb][4 * g + 1], w.acc[nb][4 * g + 2], w.acc[nb][4 * g + 3]};
         *reinterpret_cast<f32x4*>(wa + 32 * nb + 8 * g + 4 * hf) = o4;
       }
     if (hf == 0) {
-      p.ws_m[split * R + rg] = m_run == -INFINITY ? -INFINITY : m_run * kLn2;
+      p.ws_m[split * R + rg] = w.m_run == -INFINITY ? -INFINITY : w.m_run * kLn2;
       p.ws_l[split * R + rg] = l_tot;
     }
   }
