@@ -421,26 +421,32 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
 }
 
 // ---------------------------------------------------------------------------
-// Split-KV partial for single-query decode (N_q == 1).  One workgroup per
-// (batch*head, chunk).  With a single query row the products are matrix-vector
-// shaped and the kernel is bound by streaming K and V from HBM, so it uses
-// plain fp32 dot products: D/8 lanes share one key row (16 bytes each) and
-// the chunk is walked in blocks of kDecBlock keys with the same running-max
-// rescaling as the tile kernel.
+// Split-KV partial for single-query decode (N_q == 1).  One workgroup (4
+// waves) per (batch*head, key chunk).  With a single query row both products
+// are matrix-vector shaped and the kernel is bound by streaming K and V from
+// HBM, so it uses VALU dot products: D/8 lanes share one key row (16 bytes
+// each), a wave covers 64*8/D keys per load, and each lane keeps kDecU keys'
+// K and V loads in flight per step.  Every wave runs its own online softmax
+// over the steps it owns (steps are dealt round-robin to the waves), so the
+// stream never waits at a workgroup barrier; the four wave partials are merged
+// once at the end with the same rescaling.
 constexpr int kDecThreads = 256;
-constexpr int kDecBlock = 128;
+constexpr int kDecU = 16;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(FwdParams p, float sl2, unsigned qsign) {
-  constexpr int LPK = D / 8;                 // lanes per key row
-  constexpr int KPI = kDecThreads / LPK;     // key rows per workgroup-wide load
-  constexpr int NIT = kDecBlock / KPI;       // loads per thread per block
-  __shared__ float sc[kDecBlock];
-  __shared__ float red[kDecThreads / 64];
-  __shared__ float accs[KPI][D + 4];
+  constexpr int LPK = D / 8;        // lanes per key row
+  constexpr int KPW = 64 / LPK;     // key rows per wave-wide load
+  constexpr int STEP = KPW * kDecU; // keys per wave step
+  constexpr int NWAVE = kDecThreads / 64;
+  __shared__ float part_acc[NWAVE][D];
+  __shared__ float part_m[NWAVE], part_l[NWAVE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sub = tid % LPK, kslot = tid / LPK;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sub = lane % LPK, kg = lane / LPK;
 
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int split = L % p.num_splits;
@@ -450,106 +456,108 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(FwdParams p
   int kend = kbeg + p.split_len < p.n_k ? kbeg + p.split_len : p.n_k;
   if (p.causal) kend = min(kend, 1);  // the single query row 0 sees key 0 only
 
-  const uint16_t* Kh = p.k + (long long)bh * p.n_k * D;
-  const uint16_t* Vh = p.v + (long long)bh * p.n_k * D;
+  // loads past key kend return zero (range check on the per-lane offset)
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + (long long)bh * p.n_k * D, (long long)kend * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + (long long)bh * p.n_k * D, (long long)kend * D * 2);
 
-  float q[8];
+  bf16x2 q2[4];
   {
     const u32x4 raw = *reinterpret_cast<const u32x4*>(p.q + (long long)bh * D + sub * 8) ^
                       u32x4{qsign, qsign, qsign, qsign};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      q[2 * i] = __builtin_bit_cast(float, raw[i] << 16);
-      q[2 * i + 1] = __builtin_bit_cast(float, raw[i] & 0xffff0000u);
+      const unsigned qw = raw[i];
+      q2[i] = __builtin_bit_cast(bf16x2, qw);
     }
   }
 
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY;  // log2 units, uniform over the wave
+  float l_run = 0.f;        // this key group's share
 
-  for (int kb0 = kbeg; kb0 < kend; kb0 += kDecBlock) {
-    u32x4 kr[NIT], vr[NIT];
+  for (int k0 = kbeg + wave * STEP; k0 < kend; k0 += NWAVE * STEP) {
+    u32x4 kr[kDecU], vr[kDecU];
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int key = kb0 + it * KPI + kslot;
-      if (key < kend) {
-        const long long off = (long long)key * D + sub * 8;
-        kr[it] = *reinterpret_cast<const u32x4*>(Kh + off);
-        vr[it] = *reinterpret_cast<const u32x4*>(Vh + off);
-      } else {
-        kr[it] = u32x4{0, 0, 0, 0};
-        vr[it] = u32x4{0, 0, 0, 0};
-      }
+    for (int u = 0; u < kDecU; ++u) {
+      const unsigned off = (unsigned)(((k0 + u * KPW + kg) * D + sub * 8) * 2);
+      kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+      vr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
     }
-    // scores
+    float sc[kDecU];
+    float mloc = -INFINITY;
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
+    for (int u = 0; u < kDecU; ++u) {
       float dot = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        dot = __builtin_fmaf(q[2 * i], __builtin_bit_cast(float, kr[it][i] << 16), dot);
-        dot = __builtin_fmaf(q[2 * i + 1], __builtin_bit_cast(float, kr[it][i] & 0xffff0000u), dot);
+        const unsigned kw = kr[u][i];  // named copy: bit-casting a vector element in place reads element 0
+        dot = __builtin_amdgcn_fdot2_f32_bf16(q2[i], __builtin_bit_cast(bf16x2, kw), dot, false);
       }
 #pragma unroll
-      for (int w = LPK / 2; w >= 1; w >>= 1) dot += __shfl_xor(dot, w);
-      const int key = kb0 + it * KPI + kslot;
-      if (sub == 0) sc[it * KPI + kslot] = key < kend ? dot * sl2 : -INFINITY;
+      for (int x = LPK / 2; x >= 1; x >>= 1) dot += __shfl_xor(dot, x);
+      sc[u] = (k0 + u * KPW + kg < kend) ? dot * sl2 : -INFINITY;
+      mloc = fmaxf(mloc, sc[u]);
     }
-    __syncthreads();
-    // block max
-    float mx = tid < kDecBlock ? sc[tid] : -INFINITY;
 #pragma unroll
-    for (int w = 32; w >= 1; w >>= 1) mx = fmaxf(mx, __shfl_xor(mx, w));
-    if (lane == 0) red[wave] = mx;
-    __syncthreads();
-    mx = red[0];
-#pragma unroll
-    for (int w = 1; w < kDecThreads / 64; ++w) mx = fmaxf(mx, red[w]);
-    const float m_new = fmaxf(m_run, mx);
+    for (int x = LPK; x < 64; x <<= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, x));
+    const float m_new = fmaxf(m_run, mloc);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_new;
-    __syncthreads();  // everyone has read red[] before it is reused
-    float pe = 0.f;
-    if (tid < kDecBlock) {
-      pe = __builtin_amdgcn_exp2f(sc[tid] - m_use);
-      sc[tid] = pe;
-    }
-#pragma unroll
-    for (int w = 32; w >= 1; w >>= 1) pe += __shfl_xor(pe, w);
-    if (lane == 0) red[wave] = pe;
-    __syncthreads();
-    float bsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecThreads / 64; ++w) bsum += red[w];
-    l_run = l_run * alpha + bsum;
+    float ps = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] *= alpha;
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const float pk = sc[it * KPI + kslot];
+    for (int u = 0; u < kDecU; ++u) {
+      const float pk = __builtin_amdgcn_exp2f(sc[u] - m_use);
+      ps += pk;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = __builtin_fmaf(pk, __builtin_bit_cast(float, vr[it][i] << 16), acc[2 * i]);
-        acc[2 * i + 1] = __builtin_fmaf(pk, __builtin_bit_cast(float, vr[it][i] & 0xffff0000u), acc[2 * i + 1]);
+        acc[2 * i] = __builtin_fmaf(pk, __builtin_bit_cast(float, vr[u][i] << 16), acc[2 * i]);
+        acc[2 * i + 1] = __builtin_fmaf(pk, __builtin_bit_cast(float, vr[u][i] & 0xffff0000u), acc[2 * i + 1]);
       }
     }
-    __syncthreads();  // sc[] and red[] are rewritten by the next block
+    l_run = l_run * alpha + ps;
   }
 
-  // sum the KPI key slots' accumulators
+  // fold the key groups of the wave (lanes with equal `sub`)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) accs[kslot][sub * 8 + i] = acc[i];
+  for (int x = LPK; x < 64; x <<= 1) {
+    l_run += __shfl_xor(l_run, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], x);
+  }
+  if (kg == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part_acc[wave][sub * 8 + i] = acc[i];
+  }
+  if (lane == 0) {
+    part_m[wave] = m_run;
+    part_l[wave] = l_run;
+  }
   __syncthreads();
+
+  // merge the wave partials (log2 units) and write the chunk partial
+  float M = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < NWAVE; ++v) M = fmaxf(M, part_m[v]);
+  float wgt[NWAVE];
+  float lsum = 0.f;
+#pragma unroll
+  for (int v = 0; v < NWAVE; ++v) {
+    wgt[v] = part_m[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(part_m[v] - M);
+    lsum += wgt[v] * part_l[v];
+  }
   const long long R = (long long)p.B * p.H;  // N_q == 1
   for (int dd = tid; dd < D; dd += kDecThreads) {
     float t = 0.f;
-    for (int s = 0; s < KPI; ++s) t += accs[s][dd];
+#pragma unroll
+    for (int v = 0; v < NWAVE; ++v) t += wgt[v] * part_acc[v][dd];
     p.ws_acc[((long long)split * R + bh) * D + dd] = t;
   }
   if (tid == 0) {
-    p.ws_m[split * R + bh] = m_run == -INFINITY ? -INFINITY : m_run * kLn2;
-    p.ws_l[split * R + bh] = l_run;
+    p.ws_m[split * R + bh] = M == -INFINITY ? -INFINITY : M * kLn2;
+    p.ws_l[split * R + bh] = lsum;
   }
 }
 
