@@ -113,7 +113,7 @@ def forward_splitkv(q, k, v, num_splits: int = 16, causal: bool = False, scale=N
     (fp32 partials in a workspace, then a merge pass), via fa2_fwd_splitkv.
 
     Returns (o, lse, workspace); the workspace holds the per-chunk partials
-    acc [S][R][d], m [S][R], l [S][R] (R = B*H*N_q) as fp32."""
+    acc [S][R][d], then m, l and l_lse, each [S][R] (R = B*H*N_q), as fp32."""
     lib = load_library()
     B, H, n_q, n_k, d = _check_inputs(q, k, v)
     need = lib.fa2_splitkv_workspace_bytes(B, H, n_q, d, int(num_splits))

@@ -90,7 +90,7 @@ int fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, in
 
 size_t fa2_splitkv_workspace_bytes(int B, int H, int N_q, int d, int num_splits) {
   if (B < 1 || H < 1 || N_q < 1 || d < 1 || num_splits < 1 || num_splits > FA2_MAX_SPLITS) return 0;
-  return (size_t)num_splits * (size_t)B * (size_t)H * (size_t)N_q * (size_t)(d + 2) * 4u;
+  return (size_t)num_splits * (size_t)B * (size_t)H * (size_t)N_q * (size_t)(d + 3) * 4u;
 }
 
 int fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q, int N_k,
@@ -114,6 +114,7 @@ int fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float*
   p.ws_acc = ws;
   p.ws_m = ws + (long long)num_splits * R * d;
   p.ws_l = p.ws_m + (long long)num_splits * R;
+  p.ws_ll = p.ws_l + (long long)num_splits * R;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (fa2::launch_splitkv_partial(p, s) != hipSuccess) return FA2_ERR_HIP;
   if (fa2::launch_splitkv_merge(p, s) != hipSuccess) return FA2_ERR_HIP;

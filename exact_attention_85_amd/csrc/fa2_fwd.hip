@@ -11,12 +11,12 @@
 // Per 64-key tile, each wave:
 //   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, K from LDS, Q resident in VGPRs
 //   mask             only on tiles that cross the diagonal or the key tail
-//   online softmax   running max m and sum l per row, base-2 exponent with
+//   online softmax   per-row reference maximum and sums, base-2 exponent with
 //                    scale*log2(e) folded into one FMA; P stays in registers
 //   O^T += V^T P^T   v_mfma_f32_32x32x16_bf16, V read transposed from LDS with
 //                    ds_read_b64_tr_b16, P converted to bf16 (RNE)
-// and the epilogue divides by l once (deferred normalisation, synthesis page,
-// section 2 item 1) and writes O (bf16) and LSE = m + ln l (fp32).
+// and the epilogue divides once per row (deferred normalisation, synthesis
+// page, section 2 item 1) and writes O (bf16) and LSE = m + ln l (fp32).
 //
 // Computing S transposed puts one query row in each lane column, so the
 // accumulator of S^T is directly the B operand of the second product and every
@@ -91,14 +91,15 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Per-wave state of one 32-row query block: the Q fragment (B operand of
 // S^T = K Q^T; lane holds Q[row][16t + 8hf .. +7]), the O^T accumulator
-// (acc[nb][4g + i] = O^T[32nb + 8g + 4hf + i][row]), the running maximum of
-// the scaled scores in log2 units and this lane's share of the denominator.
+// (acc[nb][4g + i] = O^T[32nb + 8g + 4hf + i][row]), the reference maximum of
+// the scaled scores in log2 units, and this lane's shares of the two sums.
 template <int D>
 struct WaveRows {
   bf16x8 qf[D / 16];
   f32x16 acc[D / 32];
   float m_run;
-  float l_run;
+  float l_run;   // sum of fp32 probabilities (for LSE)
+  float l16;     // sum of the bf16-rounded probabilities (normalises O)
 };
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -190,74 +191,134 @@ __device__ __forceinline__ T lds_load(unsigned addr) {
   return *reinterpret_cast<const __attribute__((address_space(3))) T*>((uintptr_t)addr);
 }
 
-// One kBC-key tile for one wave: S^T = K Q^T, mask (only when need_mask),
-// online softmax, O^T += V^T P^T.  KOFF / VOFF: byte offsets of this stage's
-// K and V tiles relative to the addresses in `la`.
-template <int D, unsigned KOFF, unsigned VOFF>
-__device__ __forceinline__ void tile_step(WaveRows<D>& w, const LdsAddr<D>& la, bool need_mask, int k0, int kend,
-                                          int row, int causal, float sl2, int lane) {
-  constexpr int KT = D / 16;
-  constexpr int NB = D / 32;
-  constexpr unsigned ROW = D * 2;  // bytes per tile row
-  const int hf = lane >> 5;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-  // S^T = K Q^T over two 32-key blocks, the two accumulation chains interleaved
-  f32x16 s0 = {}, s1 = {};
+// S^T = K Q^T for one kBC-key tile (two 32-key blocks, two interleaved
+// accumulation chains).  KOFF: byte offset of the tile's K buffer relative to
+// the addresses in `la`.  s{kb}[r] is the score of query `row` against key
+// k0 + kb*32 + 8*(r/4) + 4*hf + r%4.
+template <int D, unsigned KOFF>
+__device__ __forceinline__ void qk_tile(const WaveRows<D>& w, const LdsAddr<D>& la, f32x16& s0, f32x16& s1) {
+  constexpr unsigned ROW = D * 2;
+  s0 = f32x16{};
+  s1 = f32x16{};
 #pragma unroll
-  for (int t = 0; t < KT; ++t) {
+  for (int t = 0; t < D / 16; ++t) {
     const bf16x8 a0 = lds_load<bf16x8>(la.ka[t] + KOFF);
     const bf16x8 a1 = lds_load<bf16x8>(la.ka[t] + KOFF + 32 * ROW);
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, w.qf[t], s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, w.qf[t], s1, 0, 0, 0);
   }
-  // s{kb}[r] is the score of query `row` against key k0 + kb*32 + 8*(r/4) + 4*hf + r%4
-  if (need_mask) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = k0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-      if (key >= kend || (causal && key > row)) s0[r] = -INFINITY;
-      if (key + 32 >= kend || (causal && key + 32 > row)) s1[r] = -INFINITY;
-    }
-  }
+}
 
-  float mx = -INFINITY;
+// -inf for keys past kend or, causal, above the query row.  Key k0 + 4hf + c
+// is visible iff c <= lim; c is a compile-time constant per register.
+__device__ __forceinline__ void mask_scores(f32x16& s0, f32x16& s1, int k0, int kend, int row, int causal, int hf) {
+  const int lim = (causal ? min(row, kend - 1) : kend - 1) - k0 - 4 * hf;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s0[r]);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-  const float m_new = fmaxf(w.m_run, mx);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  if (__ballot(m_new > w.m_run)) {  // some row of this wave has a new maximum
-    const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_use);
-    w.l_run *= alpha;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) w.acc[nb] *= alpha;
+  for (int r = 0; r < 16; ++r) {
+    const int c = 8 * (r >> 2) + (r & 3);
+    if (c > lim) s0[r] = -INFINITY;
+    if (c + 32 > lim) s1[r] = -INFINITY;
   }
-  w.m_run = m_new;
+}
 
+// Probabilities exp2(s * sl2 - m_use) in place; returns this lane's fp32 sum.
+__device__ __forceinline__ float exp_tile(f32x16& s0, f32x16& s1, float sl2, float m_use) {
   float rs = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], sl2, -m_use));
-    s0[r] = e0;
-    rs += e0;
+    s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], sl2, -m_use));
+    rs += s0[r];
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], sl2, -m_use));
-    s1[r] = e1;
-    rs += e1;
+    s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], sl2, -m_use));
+    rs += s1[r];
+  }
+  return rs;
+}
+
+// acc + the sum of the 32 bf16 probabilities in pb (v_dot2 against (1, 1)).
+// Dwords are copied into named values first: bit-casting a vector element in
+// place reads element 0.
+__device__ __forceinline__ float sum_bf16(const bf16x8 (&pb)[4], float acc) {
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 v = __builtin_bit_cast(u32x4, pb[i]);
+    const unsigned v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v0), ones, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v1), ones, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v2), ones, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v3), ones, acc, false);
+  }
+  return acc;
+}
+
+// One kBC-key tile for one wave: S^T = K Q^T, mask (only when need_mask),
+// online softmax, O^T += V^T P^T.  KOFF / VOFF: byte offsets of this stage's K
+// and V tiles relative to the addresses in `la`.
+//
+// Softmax against a reference maximum.  The probabilities are first formed
+// against the current reference m_run, with no max pass and no rescale of O.
+// Only when a lane's tile sum exceeds kLazyBound (so no probability can exceed
+// it), or when some row has no reference yet, is the tile redone exactly: new
+// maximum, rescale of O and of both sums, probabilities again.  The result does
+// not depend on the reference: O = acc / l16 with l16 the sum of the bf16
+// probabilities exactly as accumulated (each O row is an exact convex
+// combination of V rows), and LSE = m_run + log2(l_run) with l_run the fp32 sum.
+constexpr float kLazyBound = 2048.f;
+
+template <int D, unsigned KOFF, unsigned VOFF>
+__device__ __forceinline__ void tile_step(WaveRows<D>& w, const LdsAddr<D>& la, bool need_mask, int k0, int kend,
+                                          int row, int causal, float sl2, int lane) {
+  constexpr int NB = D / 32;
+  constexpr unsigned ROW = D * 2;
+  const int hf = lane >> 5;
+  f32x16 s0, s1;
+  qk_tile<D, KOFF>(w, la, s0, s1);
+  if (need_mask) mask_scores(s0, s1, k0, kend, row, causal, hf);
+
+  bool exact = __ballot(w.m_run == -INFINITY) != 0;  // some row has no reference yet
+  float rs = 0.f;
+  if (!exact) {
+    rs = exp_tile(s0, s1, sl2, w.m_run);
+    if (__ballot(rs > kLazyBound)) {
+      exact = true;
+      qk_tile<D, KOFF>(w, la, s0, s1);  // scores again (the K tile is still in LDS)
+      if (need_mask) mask_scores(s0, s1, k0, kend, row, causal, hf);
+    }
+  }
+  if (exact) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    const float m_new = fmaxf(w.m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_use);
+    w.l_run *= alpha;
+    w.l16 *= alpha;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) w.acc[nb] *= alpha;
+    w.m_run = m_new;
+    rs = exp_tile(s0, s1, sl2, m_use);
   }
   w.l_run += rs;
+  bf16x8 pb[4];
+  pb[0] = cvt_bf16x8(slice8(s0, 0));
+  pb[1] = cvt_bf16x8(slice8(s0, 1));
+  pb[2] = cvt_bf16x8(slice8(s1, 0));
+  pb[3] = cvt_bf16x8(slice8(s1, 1));
+  w.l16 = sum_bf16(pb, w.l16);
 
-  // O^T += V^T P^T.  k-step (kb, t) contracts keys kb*32 + 16t + {4hf..4hf+3, 8+4hf..8+4hf+3}
-  // (the keys this lane's S^T registers 8t..8t+7 hold); the A operand is read transposed.
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const bf16x8 pb = cvt_bf16x8(slice8(kb == 0 ? s0 : s1, t));
       const unsigned roff = VOFF + (kb * 32 + 16 * t) * ROW;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -266,7 +327,7 @@ __device__ __forceinline__ void tile_step(WaveRows<D>& w, const LdsAddr<D>& la, 
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             reinterpret_cast<lds_i16x4*>((uintptr_t)(la.va[2 * nb + 1] + roff)));
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        w.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, w.acc[nb], 0, 0, 0);
+        w.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[2 * kb + t], w.acc[nb], 0, 0, 0);
       }
     }
 }
@@ -285,11 +346,6 @@ __device__ __forceinline__ void tile_step(WaveRows<D>& w, const LdsAddr<D>& la, 
 // reading one stage does not depend on the loads in flight into the other:
 // tile j+1 streams in while tile j computes, and one barrier per tile both
 // publishes tile j and retires the buffer of tile j-1.
-//
-// The O accumulator is rescaled only on tiles where some row of the wave
-// finds a new maximum (alpha = 1 for every row otherwise); the running maximum
-// itself stays exact, so the largest probability of each row is exactly 1
-// before its conversion to bf16.
 template <int D, int NW, bool SPLIT>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float sl2, unsigned qsign) {
   constexpr int BR = 32 * NW;
@@ -354,6 +410,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
   for (int nb = 0; nb < NB; ++nb) w.acc[nb] = f32x16{};
   w.m_run = -INFINITY;
   w.l_run = 0.f;
+  w.l16 = 0.f;
 
   LdsAddr<D> la;
   make_lds_addr<D>(la, (unsigned)(uintptr_t)(const lds_void*)&lds[0][0][0], lane);
@@ -387,9 +444,10 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
 
   // ---- epilogue ----
   const float l_tot = w.l_run + __shfl_xor(w.l_run, 32);
+  const float l16_tot = w.l16 + __shfl_xor(w.l16, 32);
   if (row >= p.n_q) return;
   if (!SPLIT) {
-    const float inv = 1.f / l_tot;
+    const float inv = 1.f / l16_tot;
     uint16_t* Orow = p.o + ((long long)bh * p.n_q + row) * D;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -415,7 +473,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
       }
     if (hf == 0) {
       p.ws_m[split * R + rg] = w.m_run == -INFINITY ? -INFINITY : w.m_run * kLn2;
-      p.ws_l[split * R + rg] = l_tot;
+      p.ws_l[split * R + rg] = l16_tot;
+      p.ws_ll[split * R + rg] = l_tot;
     }
   }
 }
@@ -557,7 +616,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(FwdParams p
   }
   if (tid == 0) {
     p.ws_m[split * R + bh] = M == -INFINITY ? -INFINITY : M * kLn2;
-    p.ws_l[split * R + bh] = lsum;
+    p.ws_l[split * R + bh] = lsum;   // P is used in fp32 here: one sum serves both
+    p.ws_ll[split * R + bh] = lsum;
   }
 }
 
@@ -578,12 +638,13 @@ __global__ void __launch_bounds__(256) splitkv_merge_kernel(FwdParams p) {
   float o[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.f;
-  float lsum = 0.f;
+  float lsum = 0.f, llsum = 0.f;
   for (int c = 0; c < S; ++c) {
     const float mc = p.ws_m[c * R + rg];
     if (mc == -INFINITY) continue;  // empty chunk
     const float w = __builtin_amdgcn_exp2f((mc - M) * kLog2e);
     lsum += w * p.ws_l[c * R + rg];
+    llsum += w * p.ws_ll[c * R + rg];
     const float* a = p.ws_acc + (c * R + rg) * D;
 #pragma unroll
     for (int i = 0; i < PER; ++i) o[i] += w * a[lane + 64 * i];
@@ -595,7 +656,7 @@ __global__ void __launch_bounds__(256) splitkv_merge_kernel(FwdParams p) {
     const __bf16 b = (__bf16)(o[i] * inv);
     orow[lane + 64 * i] = __builtin_bit_cast(uint16_t, b);
   }
-  if (lane == 0) p.lse[rg] = M + __logf(lsum);
+  if (lane == 0) p.lse[rg] = M + __logf(llsum);
 }
 
 // scale handling shared by all launches: fold |scale|*log2(e) into one positive

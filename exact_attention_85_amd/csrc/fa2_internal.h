@@ -16,8 +16,9 @@ struct FwdParams {
   uint16_t* o;       // bf16 output (forward mode)
   float* lse;        // fp32 natural-log LSE (forward mode)
   float* ws_acc;     // split mode: [S][R][d] unnormalised accumulators
-  float* ws_m;       // split mode: [S][R] chunk maxima (natural-log units)
-  float* ws_l;       // split mode: [S][R] chunk denominators
+  float* ws_m;       // split mode: [S][R] chunk reference maxima (natural-log units)
+  float* ws_l;       // split mode: [S][R] sums of the probabilities as accumulated in acc
+  float* ws_ll;      // split mode: [S][R] fp32 sums of the probabilities (for LSE)
   int B, H, n_q, n_k, d;
   int causal;
   float scale;

@@ -21,9 +21,10 @@
  *            (top-left alignment, so every query row sees key 0)
  *   O[i]   = sum_j softmax_j(s_ij) * V[j]      over visible keys
  *   LSE[i] = log(sum_j exp(s_ij))              over visible keys
- * Products are formed from the bf16 inputs, accumulated in fp32; the
- * probabilities are rounded to bf16 before the P.V product and the softmax
- * denominator is summed from the fp32 probabilities.
+ * Products are formed from the bf16 inputs and accumulated in fp32.  The
+ * probabilities are rounded to bf16 for the P.V product; O is divided by the
+ * sum of those rounded probabilities (so each output row is an exact convex
+ * combination of V rows), and LSE uses the sum of the fp32 probabilities.
  *
  * Errors: every argument is validated on the host BEFORE any HIP call, and a
  * negative fa2_status is returned with nothing enqueued.  FA2_ERR_HIP means
@@ -80,7 +81,7 @@ int fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
 
 /*
  * fa2_splitkv_workspace_bytes — bytes of caller-owned device workspace that
- * fa2_fwd_splitkv needs: num_splits * B * H * N_q * (d + 2) * 4.
+ * fa2_fwd_splitkv needs: num_splits * B * H * N_q * (d + 3) * 4.
  * Returns 0 when an argument is out of range.
  */
 size_t fa2_splitkv_workspace_bytes(int B, int H, int N_q, int d, int num_splits);
@@ -93,18 +94,22 @@ size_t fa2_splitkv_workspace_bytes(int B, int H, int N_q, int d, int num_splits)
  *
  * Chunk c covers keys [c*L, min((c+1)*L, N_k)), L = ceil(N_k / num_splits);
  * a chunk may be empty.  Pass 1 writes, per chunk and query row, the fp32
- * partial (acc, m, l) into the workspace:
- *   m   = max of the chunk's visible scaled scores s_ij (natural-log units),
- *         -inf when the chunk holds no visible key;
- *   l   = sum over the chunk of exp(s_ij - m)            (0 when empty);
- *   acc = sum over the chunk of exp(s_ij - m) * V[j]     (0 when empty).
+ * partial (acc, m, l, l_lse) into the workspace:
+ *   m     = a reference level in natural-log units: the running maximum of
+ *           the chunk's visible scaled scores s_ij at its last refresh (at most
+ *           the true maximum; -inf exactly when the chunk holds no visible key);
+ *   acc   = sum over the chunk of p_ij * V[j], p_ij = exp(s_ij - m) as used in
+ *           the P.V product (0 when empty);
+ *   l     = sum of the same p_ij                          (0 when empty);
+ *   l_lse = sum of exp(s_ij - m) in fp32                  (0 when empty).
  * Pass 2 merges them in chunk order: M = max_c m_c, w_c = exp(m_c - M)
  * (0 for an empty chunk), O = (sum_c w_c acc_c) / (sum_c w_c l_c),
- * LSE = M + log(sum_c w_c l_c) — the same rescaling as the online softmax
- * (walkthrough page, main-loop pseudocode).
+ * LSE = M + log(sum_c w_c l_lse_c) — the same rescaling as the online
+ * softmax (walkthrough page, main-loop pseudocode).  acc / l and
+ * m + log(l_lse) do not depend on the reference m.
  *
  * Workspace layout (fp32, R = B*H*N_q rows, row = (b*H + h)*N_q + i):
- *   acc [num_splits][R][d], then m [num_splits][R], then l [num_splits][R].
+ *   acc [num_splits][R][d], then m, l and l_lse, each [num_splits][R].
  * Its contents after the call are the partials above; it must not overlap
  * any input or output.  Both passes run in order on `stream`.
  *

@@ -92,7 +92,7 @@ def test_alias():
 
 def test_splits_and_workspace():
     lib = fa2.load_library()
-    assert lib.fa2_splitkv_workspace_bytes(64, 32, 1, 128, 16) == 16 * 64 * 32 * 1 * 130 * 4
+    assert lib.fa2_splitkv_workspace_bytes(64, 32, 1, 128, 16) == 16 * 64 * 32 * 1 * 131 * 4
     assert lib.fa2_splitkv_workspace_bytes(1, 1, 1, 64, 0) == 0
     assert lib.fa2_splitkv_workspace_bytes(1, 1, 1, 64, 257) == 0
     assert split(s=0) == SPLITS

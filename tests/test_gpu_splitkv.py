@@ -18,9 +18,10 @@ DEV = "cuda:0"
 
 def _partials(ws, S, R, d):
     acc = ws[: S * R * d].view(S, R, d)
-    m = ws[S * R * d: S * R * d + S * R].view(S, R)
-    l_ = ws[S * R * d + S * R: S * R * (d + 2)].view(S, R)
-    return acc, m, l_
+    m = ws[S * R * d: S * R * (d + 1)].view(S, R)
+    l_ = ws[S * R * (d + 1): S * R * (d + 2)].view(S, R)
+    l_lse = ws[S * R * (d + 2): S * R * (d + 3)].view(S, R)
+    return acc, m, l_, l_lse
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -38,7 +39,7 @@ def test_splitkv_parity_and_partials(nq, nk, S, causal, d):
                     what="merged", out_grid=True)
     # per-chunk partials: compare the chunk's normalised output and its log-sum-exp
     R = 2 * 3 * nq
-    acc, m, l_ = (t.cpu().double().numpy() for t in _partials(ws, S, R, d))
+    acc, m, l_, l_lse = (t.cpu().double().numpy() for t in _partials(ws, S, R, d))
     qd, kd, vd = (workloads.bf16_to_f64(t) for t in (q, k, v))
     L = -(-nk // S)
     for c in range(S):
@@ -46,13 +47,13 @@ def test_splitkv_parity_and_partials(nq, nk, S, causal, d):
         a_ref, m_ref, l_ref = a_ref.reshape(R, d), m_ref.reshape(R), l_ref.reshape(R)
         empty = np.isneginf(m_ref)
         assert np.array_equal(np.isneginf(m[c]), empty), c
-        assert np.all(l_[c][empty] == 0) and np.all(acc[c][empty] == 0)
+        assert np.all(l_[c][empty] == 0) and np.all(l_lse[c][empty] == 0) and np.all(acc[c][empty] == 0)
         ne = ~empty
         if ne.any():
             o_c = acc[c][ne] / l_[c][ne][:, None]
             o_c_ref = a_ref[ne] / l_ref[ne][:, None]
             assert np.max(np.abs(o_c - o_c_ref)) <= 1e-2, c
-            lse_c = m[c][ne] + np.log(l_[c][ne])
+            lse_c = m[c][ne] + np.log(l_lse[c][ne])
             lse_c_ref = m_ref[ne] + np.log(l_ref[ne])
             assert np.max(np.abs(lse_c - lse_c_ref)) <= 1e-3, c
 
