@@ -203,6 +203,19 @@ def main():
                                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                                    "traffic": measured_traffic(f"splitkv:{wd.name}")}})
         log(f"{wd.name}: {msd:.3f} ms, {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s)")
+        # the same decode with the split count fa2_num_splits picks (1 here: B*H fills the chip,
+        # so fa2_fwd streams each head's keys in one workgroup and writes O directly)
+        s_auto = fa2.num_splits(wd.B, wd.H, wd.n_q, wd.n_k, wd.d)
+        if s_auto == 1:
+            fn = lambda: fa2.forward(qd, kd, vd, scale=wd.scale, out=od, lse=ld)  # noqa: E731
+        else:
+            fn = lambda: fa2.forward_splitkv(qd, kd, vd, num_splits=s_auto, scale=wd.scale,  # noqa: E731
+                                             workspace=ws, out=od, lse=ld)
+        msa = time_launches(fn, steps_x, args.warmup)
+        gba = wd.io_bytes() / (msa * 1e-3) / 1e9
+        extra.append({"workload": wd.name.replace("_s16", "_auto"), "num_splits": s_auto, "causal": False,
+                      "ms": round(msa, 4), "GB/s": round(gba, 1), "frac_of_hbm_peak": round(gba / PEAK_HBM_GBS, 4)})
+        log(f"decode with fa2_num_splits -> {s_auto}: {msa:.3f} ms, {gba:.0f} GB/s")
         del qd, kd, vd, od, ld, ws
         result["workloads"] = extra
 

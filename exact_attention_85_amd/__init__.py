@@ -8,10 +8,12 @@ if the library is missing or a GPU is absent the calls raise.
 from ._binding import (  # noqa: F401
     FA2_MAX_SPLITS,
     Fa2Error,
+    attention,
     forward,
     forward_splitkv,
     lib_path,
     load_library,
+    num_splits,
     splitkv_workspace_bytes,
     status_string,
 )

@@ -45,6 +45,8 @@ def load_library():
     lib.fa2_splitkv_workspace_bytes.restype = ctypes.c_size_t
     lib.fa2_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, ctypes.c_size_t, vp]
     lib.fa2_fwd_splitkv.restype = i
+    lib.fa2_num_splits.argtypes = [i, i, i, i, i, i]
+    lib.fa2_num_splits.restype = i
     lib.fa2_status_string.argtypes = [i]
     lib.fa2_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -129,3 +131,25 @@ def forward_splitkv(q, k, v, num_splits: int = 16, causal: bool = False, scale=N
                              _stream_handle(q.device))
     _check(rc)
     return out, lse, workspace
+
+
+def num_splits(B, H, n_q, n_k, d, num_cus: int = 0) -> int:
+    """fa2_num_splits: the key-chunk count that fills num_cus compute units
+    (0 = ask the current HIP device).  Raises Fa2Error on bad arguments."""
+    rc = int(load_library().fa2_num_splits(int(B), int(H), int(n_q), int(n_k), int(d), int(num_cus)))
+    if rc < 0:
+        _check(rc)
+    return rc
+
+
+def attention(q, k, v, causal: bool = False, scale=None):
+    """forward() or forward_splitkv(), whichever fa2_num_splits picks for q's
+    device: a split count of 1 (or a single query row) takes fa2_fwd, otherwise
+    the split path with a workspace from torch's allocator.  Returns (o, lse)."""
+    B, H, n_q, n_k, d = _check_inputs(q, k, v)
+    with torch.cuda.device(q.device):
+        s = num_splits(B, H, n_q, n_k, d, 0)
+    if s == 1:
+        return forward(q, k, v, causal=causal, scale=scale)
+    o, lse, _ = forward_splitkv(q, k, v, num_splits=s, causal=causal, scale=scale)
+    return o, lse

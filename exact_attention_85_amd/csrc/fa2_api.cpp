@@ -121,6 +121,32 @@ int fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float*
   return FA2_OK;
 }
 
+int fa2_num_splits(int B, int H, int N_q, int N_k, int d, int num_cus) {
+  if (B < 1 || H < 1 || N_q < 1 || N_k < 1) return FA2_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return FA2_ERR_HEAD_DIM;
+  if (num_cus <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || num_cus <= 0)
+      return FA2_ERR_HIP;
+  }
+  // workgroups of the unsplit launch: one per (batch, head) for a single query
+  // row (the streaming decode kernel), else one per 128-row query block
+  const long long units = (long long)B * H * (N_q == 1 ? 1 : (N_q + 127) / 128);
+  if (units >= num_cus) return 1;
+  // split until the partial pass fills every compute unit once ...
+  long long s = (num_cus + units - 1) / units;
+  // ... or twice for the tile kernel (two workgroups share a compute unit),
+  // which only pays while each chunk keeps at least 2048 keys
+  const long long s2 = (2LL * num_cus + units - 1) / units;
+  if (N_q > 1 && N_k / s2 >= 2048) s = s2;
+  // chunks shorter than 512 keys spend more on the merge than they gain
+  const long long cap = N_k / 512 > 1 ? N_k / 512 : 1;
+  if (s > cap) s = cap;
+  if (s > FA2_MAX_SPLITS) s = FA2_MAX_SPLITS;
+  return (int)s;
+}
+
 const char* fa2_status_string(int status) {
   switch (status) {
     case FA2_OK: return "FA2_OK: success";

@@ -494,7 +494,9 @@ constexpr int kDecU = 16;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-template <int D>
+// DIRECT: a single chunk (num_splits == 1) whose result is final, so the
+// workgroup writes O and LSE itself instead of a workspace partial.
+template <int D, bool DIRECT>
 __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(FwdParams p, float sl2, unsigned qsign) {
   constexpr int LPK = D / 8;        // lanes per key row
   constexpr int KPW = 64 / LPK;     // key rows per wave-wide load
@@ -607,6 +609,18 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(FwdParams p
     wgt[v] = part_m[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(part_m[v] - M);
     lsum += wgt[v] * part_l[v];
   }
+  if (DIRECT) {
+    // every query row sees key 0, so lsum > 0
+    const float inv = 1.f / lsum;
+    for (int dd = tid; dd < D; dd += kDecThreads) {
+      float t = 0.f;
+#pragma unroll
+      for (int v = 0; v < NWAVE; ++v) t += wgt[v] * part_acc[v][dd];
+      p.o[(long long)bh * D + dd] = __builtin_bit_cast(uint16_t, (__bf16)(t * inv));
+    }
+    if (tid == 0) p.lse[bh] = (M + __log2f(lsum)) * kLn2;
+    return;
+  }
   const long long R = (long long)p.B * p.H;  // N_q == 1
   for (int dd = tid; dd < D; dd += kDecThreads) {
     float t = 0.f;
@@ -679,25 +693,30 @@ hipError_t launch_tile(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <bool DIRECT>
+hipError_t launch_decode(const FwdParams& p, hipStream_t stream) {
+  float sl2;
+  unsigned qsign;
+  fold_scale(p.scale, &sl2, &qsign);
+  const unsigned grid = (unsigned)((long long)p.B * p.H * p.num_splits);
+  if (p.d == 128)
+    hipLaunchKernelGGL((decode_partial_kernel<128, DIRECT>), dim3(grid), dim3(kDecThreads), 0, stream, p, sl2, qsign);
+  else
+    hipLaunchKernelGGL((decode_partial_kernel<64, DIRECT>), dim3(grid), dim3(kDecThreads), 0, stream, p, sl2, qsign);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
+  // one query row per head: the streaming decode kernel over the whole key range
+  if (p.n_q == 1) return launch_decode<true>(p, stream);
   if (p.d == 128) return launch_tile<128, 4, false>(p, stream);
   return launch_tile<64, 4, false>(p, stream);
 }
 
 hipError_t launch_splitkv_partial(const FwdParams& p, hipStream_t stream) {
-  if (p.n_q == 1) {
-    float sl2;
-    unsigned qsign;
-    fold_scale(p.scale, &sl2, &qsign);
-    const unsigned grid = (unsigned)((long long)p.B * p.H * p.num_splits);
-    if (p.d == 128)
-      hipLaunchKernelGGL(decode_partial_kernel<128>, dim3(grid), dim3(kDecThreads), 0, stream, p, sl2, qsign);
-    else
-      hipLaunchKernelGGL(decode_partial_kernel<64>, dim3(grid), dim3(kDecThreads), 0, stream, p, sl2, qsign);
-    return hipGetLastError();
-  }
+  if (p.n_q == 1) return launch_decode<false>(p, stream);
   if (p.d == 128) return launch_tile<128, 4, true>(p, stream);
   return launch_tile<64, 4, true>(p, stream);
 }

@@ -67,7 +67,9 @@ typedef enum fa2_status {
  * workgroup streams the K/V blocks its rows can see (the synthesis page,
  * section 2 item 2: queries on the outer loop, keys/values on the inner loop,
  * no inter-workgroup communication).  With causal != 0, key blocks above the
- * diagonal are skipped and only diagonal blocks are masked.
+ * diagonal are skipped and only diagonal blocks are masked.  N_q == 1 (one
+ * decode step) runs one workgroup per (batch, head) that streams all N_k keys
+ * with fp32 probabilities, so O there is divided by the same fp32 sum as LSE.
  *
  * Q, K, V, O, LSE: device pointers as laid out above.  O and LSE must not
  * overlap Q, K, V or each other.
@@ -121,6 +123,30 @@ size_t fa2_splitkv_workspace_bytes(int B, int H, int N_q, int d, int num_splits)
 int fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE,
                     int B, int H, int N_q, int N_k, int d, int causal, float scale,
                     int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa2_num_splits — a key-chunk count for fa2_fwd_splitkv that fills the chip
+ * (the walkthrough page, "launch grid" section: the first version derives the
+ * split count from batch x heads and the multiprocessor count so that
+ * occupancy stays high, while too many splits add HBM traffic and merge work;
+ * the synthesis page, section 5 item 5).  Split the key sequence only when the
+ * batch x head x query-block grid leaves compute units idle.
+ *
+ * units = B*H for N_q == 1, else B*H*ceil(N_q/128) (the workgroups of the
+ * unsplit launch).  Returns 1 when units >= num_cus; otherwise the smallest
+ * count that gives every compute unit one workgroup, or two for N_q > 1 when
+ * each chunk still holds >= 2048 keys, capped at max(1, N_k/512) and
+ * FA2_MAX_SPLITS.  A return of 1 with N_q > 1 means fa2_fwd is the better call
+ * (no merge pass); fa2_fwd with N_q == 1 already streams the keys at full
+ * bandwidth when B*H fills the chip.
+ *
+ * num_cus: compute units of the target device; <= 0 queries the current HIP
+ * device (the only case that makes a HIP call).
+ * Returns the split count (>= 1) or a negative fa2_status: FA2_ERR_BAD_SHAPE,
+ * FA2_ERR_HEAD_DIM, or FA2_ERR_HIP when the device query fails.  Nothing is
+ * enqueued.
+ */
+int fa2_num_splits(int B, int H, int N_q, int N_k, int d, int num_cus);
 
 /* fa2_status_string — static, human-readable text for a status code. */
 const char* fa2_status_string(int status);

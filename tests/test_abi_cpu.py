@@ -21,8 +21,8 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(fa2_[a-z0-9_]+)\s*\(", text)))
 
 
-def test_header_declares_the_four_entry_points():
-    assert declared_functions() == ["fa2_fwd", "fa2_fwd_splitkv", "fa2_splitkv_workspace_bytes",
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["fa2_fwd", "fa2_fwd_splitkv", "fa2_num_splits", "fa2_splitkv_workspace_bytes",
                                     "fa2_status_string"]
 
 
@@ -100,3 +100,57 @@ def test_splits_and_workspace():
     assert split(s=300, nk=256) == SPLITS     # more splits than keys
     assert split(ws=None) == WORKSPACE
     assert split(ws_bytes=100) == WORKSPACE
+
+
+# --- split-count heuristic (pure host arithmetic when num_cus > 0) ---
+CUS = 256
+
+
+# Shapes whose best split count was measured on MI355X (key-chunk sweep over
+# S in {1, 2, 4, ..., 128}): the heuristic must land on the measured best or on a
+# count within 5% of it.
+@pytest.mark.parametrize("shape,allowed", [
+    ((64, 32, 1, 8192, 128), {1}),          # decode, B*H = 2048 fills the chip
+    ((1, 32, 1, 65536, 128), {8}),          # decode, B*H = 32
+    ((1, 8, 1, 131072, 128), {16, 32}),     # decode, B*H = 8
+    ((32, 8, 1, 4096, 128), {1, 2}),        # decode, B*H = 256
+    ((1, 8, 2048, 2048, 128), {2, 4}),      # prefill, 128 query blocks
+    ((1, 4, 4096, 4096, 128), {2, 4}),
+    ((1, 2, 1024, 32768, 128), {16}),       # 16 query blocks, long keys
+    ((2, 8, 512, 16384, 64), {8}),
+    ((1, 16, 256, 8192, 128), {8}),
+    ((1, 32, 128, 4096, 128), {8}),
+    ((4, 16, 4096, 4096, 128), {1}),        # 2048 query blocks: no split
+])
+def test_num_splits_measured_shapes(shape, allowed):
+    assert fa2.num_splits(*shape, num_cus=CUS) in allowed
+
+
+def test_num_splits_properties():
+    for B, H in ((1, 1), (1, 3), (2, 8), (4, 32), (64, 32)):
+        for n_q in (1, 100, 128, 4096):
+            for n_k in (1, 7, 512, 5000, 1 << 20):
+                for d in (64, 128):
+                    s = fa2.num_splits(B, H, n_q, n_k, d, num_cus=CUS)
+                    units = B * H * (1 if n_q == 1 else -(-n_q // 128))
+                    assert 1 <= s <= min(fa2.FA2_MAX_SPLITS, max(1, n_k // 512))
+                    if units >= CUS:
+                        assert s == 1
+                    else:
+                        # enough workgroups to cover the chip unless the chunk floor binds
+                        assert units * s >= CUS or s == min(fa2.FA2_MAX_SPLITS, max(1, n_k // 512))
+    # more units never asks for more splits
+    prev = 10 ** 9
+    for H in range(1, 300):
+        s = fa2.num_splits(1, H, 1, 1 << 16, 128, num_cus=CUS)
+        assert s <= prev
+        prev = s
+
+
+def test_num_splits_errors():
+    with pytest.raises(fa2.Fa2Error) as e:
+        fa2.num_splits(0, 1, 1, 1, 64, num_cus=CUS)
+    assert e.value.status == BAD_SHAPE
+    with pytest.raises(fa2.Fa2Error) as e:
+        fa2.num_splits(1, 1, 1, 1, 96, num_cus=CUS)
+    assert e.value.status == HEAD_DIM
