@@ -48,6 +48,12 @@ def _load():
     lib.oracle_merge_f64.argtypes = [_dp, _dp, _dp, _dp, _dp, _i, ctypes.c_int64, _i]
     lib.oracle_probs_f64.argtypes = [_dp, _dp, _dp, _i, _i, _i, _i, _i, _i, ctypes.c_double]
     lib.oracle_bf16_to_f64.argtypes = [_u16p, _dp, ctypes.c_int64]
+    lib.oracle_attention_window_f64.argtypes = [_dp, _dp, _dp, _dp, _dp, _i, _i, _i, _i, _i, _i, _i,
+                                                ctypes.c_double]
+    lib.oracle_attention_window_rows_bf16.argtypes = [_u16p, _u16p, _u16p, _i64p, ctypes.c_int64, _dp, _dp,
+                                                      _i, _i, _i, _i, _i, _i, _i, ctypes.c_double]
+    lib.oracle_window_pairs.argtypes = [_i, _i, _i, _i]
+    lib.oracle_window_pairs.restype = ctypes.c_int64
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -153,3 +159,43 @@ def probs(q, k, causal: bool, scale: float):
                                   int(bool(causal)), float(scale))
     _check(rc, "probs")
     return p
+
+
+def attention_window(q, k, v, window_left: int, window_right: int, scale: float):
+    """Sliding-window attention in fp64: key j is visible to query i iff j < N_k,
+    (window_left < 0 or j >= i - window_left) and (window_right < 0 or j <= i + window_right).
+    Rows that see no key get O = 0 and LSE = -inf."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, n_q, d = q.shape
+    n_k = k.shape[2]
+    assert k.shape == (B, H, n_k, d) and v.shape == (B, H, n_k, d)
+    o = np.empty((B, H, n_q, d), dtype=np.float64)
+    lse = np.empty((B, H, n_q), dtype=np.float64)
+    rc = _load().oracle_attention_window_f64(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(o, _dp),
+                                             _ptr(lse, _dp), B, H, n_q, n_k, d, int(window_left),
+                                             int(window_right), float(scale))
+    _check(rc, "attention_window")
+    return o, lse
+
+
+def attention_window_rows_bf16(q_bits, k_bits, v_bits, rows, window_left: int, window_right: int, scale: float):
+    """attention_window for selected flat rows of bf16 inputs given as uint16 bit arrays."""
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    k_bits = np.ascontiguousarray(k_bits, dtype=np.uint16)
+    v_bits = np.ascontiguousarray(v_bits, dtype=np.uint16)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    B, H, n_q, d = q_bits.shape
+    n_k = k_bits.shape[2]
+    o = np.empty((rows.size, d), dtype=np.float64)
+    lse = np.empty((rows.size,), dtype=np.float64)
+    rc = _load().oracle_attention_window_rows_bf16(_ptr(q_bits, _u16p), _ptr(k_bits, _u16p), _ptr(v_bits, _u16p),
+                                                   _ptr(rows, _i64p), rows.size, _ptr(o, _dp), _ptr(lse, _dp),
+                                                   B, H, n_q, n_k, d, int(window_left), int(window_right),
+                                                   float(scale))
+    _check(rc, "attention_window_rows_bf16")
+    return o, lse
+
+
+def window_pairs(n_q: int, n_k: int, window_left: int, window_right: int) -> int:
+    """Visible (query, key) pairs of one head under the window."""
+    return int(_load().oracle_window_pairs(int(n_q), int(n_k), int(window_left), int(window_right)))

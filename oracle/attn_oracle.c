@@ -28,6 +28,9 @@
  * as the online recurrence (walkthrough page, main-loop pseudocode).  An
  * empty key range yields m = -inf, l = 0, acc = 0 and contributes nothing.
  *
+ * The sliding-window functions at the end generalise the causal mask to a
+ * band of keys around each query row (see the comment there).
+ *
  * Parity pins: every function here is pinned by CPU tests (brute force at 50
  * digits, closed forms, invariants, torch's fp64 CPU attention, a float64
  * transcription of the pages' recurrence); none is "parity unpinned".
@@ -257,6 +260,105 @@ int oracle_probs_f64(const double* Q, const double* K, double* P, int B, int H, 
   }
   free(s);
   return 0;
+}
+
+/*
+ * Sliding-window attention (the synthesis page, section 5 item 4: extend the
+ * causal block skip to a sliding window).  Key j is visible to query i iff
+ *   j < N_k,  (wl < 0 or j >= i - wl)  and  (wr < 0 or j <= i + wr),
+ * with top-left alignment as for the causal mask: wl = wr = -1 is plain
+ * attention, wl = -1 and wr = 0 is the causal mask.  The visible keys of a row
+ * form one contiguous range [j0, j1).  A row that sees no key gets O = 0 and
+ * LSE = -inf (the empty sum).
+ */
+static void window_range(int64_t i, int64_t n_k, int wl, int wr, int64_t* j0, int64_t* j1) {
+  int64_t lo = 0, hi = n_k; /* [lo, hi) */
+  if (wl >= 0 && i - wl > lo) lo = i - wl;
+  if (wr >= 0 && i + wr + 1 < hi) hi = i + wr + 1;
+  if (hi < lo) hi = lo;
+  *j0 = lo;
+  *j1 = hi;
+}
+
+static void attend_range_row(const double* q, const double* K, const double* V, int64_t j0, int64_t j1, int d,
+                             double scale, double* s, double* o, double* lse) {
+  double m, l;
+  partial_row(q, K, V, j0, j1, d, scale, s, o, &m, &l);
+  if (j1 <= j0) {
+    *lse = -INFINITY; /* o is already zero */
+    return;
+  }
+  for (int c = 0; c < d; ++c) o[c] /= l;
+  *lse = m + log(l);
+}
+
+int oracle_attention_window_f64(const double* Q, const double* K, const double* V, double* O, double* LSE, int B,
+                                int H, int n_q, int n_k, int d, int wl, int wr, double scale) {
+  if (check_shape(B, H, n_q, n_k, d)) return -1;
+  const int64_t n_rows = (int64_t)B * H * n_q;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)n_k);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t row = 0; row < n_rows; ++row) {
+      const int64_t bh = row / n_q, i = row % n_q;
+      int64_t j0, j1;
+      window_range(i, n_k, wl, wr, &j0, &j1);
+      attend_range_row(Q + row * d, K + bh * (int64_t)n_k * d, V + bh * (int64_t)n_k * d, j0, j1, d, scale, s,
+                       O + row * d, LSE + row);
+    }
+    free(s);
+  }
+  return 0;
+}
+
+/* The windowed result for chosen rows of bf16 inputs (as oracle_attention_rows_bf16). */
+int oracle_attention_window_rows_bf16(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const int64_t* rows,
+                                      int64_t n_rows, double* O_rows, double* LSE_rows, int B, int H, int n_q,
+                                      int n_k, int d, int wl, int wr, double scale) {
+  if (check_shape(B, H, n_q, n_k, d)) return -1;
+  for (int64_t r = 0; r < n_rows; ++r)
+    if (rows[r] < 0 || rows[r] >= (int64_t)B * H * n_q) return -1;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)n_k);
+    double* q = (double*)malloc(sizeof(double) * (size_t)d);
+    double* Kh = (double*)malloc(sizeof(double) * (size_t)n_k * d);
+    double* Vh = (double*)malloc(sizeof(double) * (size_t)n_k * d);
+    int64_t cached_bh = -1;
+    if (!s || !q || !Kh || !Vh) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      if (failed) continue;
+      const int64_t bh = rows[r] / n_q, i = rows[r] % n_q;
+      if (bh != cached_bh) {
+        oracle_bf16_to_f64(K + bh * (int64_t)n_k * d, Kh, (int64_t)n_k * d);
+        oracle_bf16_to_f64(V + bh * (int64_t)n_k * d, Vh, (int64_t)n_k * d);
+        cached_bh = bh;
+      }
+      oracle_bf16_to_f64(Q + rows[r] * d, q, d);
+      int64_t j0, j1;
+      window_range(i, n_k, wl, wr, &j0, &j1);
+      attend_range_row(q, Kh, Vh, j0, j1, d, scale, s, O_rows + r * d, LSE_rows + r);
+    }
+    free(s); free(q); free(Kh); free(Vh);
+  }
+  return failed ? -1 : 0;
+}
+
+/* Number of visible (query, key) pairs of one head under the window (for FLOP counts). */
+int64_t oracle_window_pairs(int n_q, int n_k, int wl, int wr) {
+  int64_t total = 0;
+  for (int64_t i = 0; i < n_q; ++i) {
+    int64_t j0, j1;
+    window_range(i, n_k, wl, wr, &j0, &j1);
+    total += j1 - j0;
+  }
+  return total;
 }
 
 /* Threads the parallel regions above use (reported beside CPU timings). */

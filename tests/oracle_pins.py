@@ -18,6 +18,17 @@ disagrees with:
       (FlashAttention-2 walkthrough page, main-loop pseudocode) with random
       tile sizes.
 
+Sliding-window pins (the synthesis page, section 5 item 4), for key j visible
+to query i iff j < N_k, j >= i - wl (wl >= 0) and j <= i + wr (wr >= 0):
+
+  P11 brute force at 50 digits over the band, empty rows O = 0, LSE = -inf;
+  P12 special windows: (-1, -1) is plain attention, (-1, 0) the causal mask,
+      (0, 0) returns v_i with LSE = s_ii, and a window wider than the
+      sequence changes nothing;
+  P13 torch's fp64 CPU scaled_dot_product_attention with the band written
+      out as a boolean mask, and the visible-pair count against that mask;
+  P14 the tiled online recurrence of P10 with the band mask applied per tile.
+
 The definition pinned is exact attention with top-left causal masking
 (key j allowed for query i iff j <= i), scale applied to q.k before the
 softmax, and LSE the natural log of sum exp of the scaled, masked scores.
@@ -279,6 +290,150 @@ def pin_p10_recurrence(orc):
             assert np.max(np.abs(lse_r - lse)) <= 1e-12
 
 
+def _band(i, n_k, wl, wr):
+    lo = max(0, i - wl) if wl >= 0 else 0
+    hi = min(n_k, i + wr + 1) if wr >= 0 else n_k
+    return lo, max(lo, hi)
+
+
+def pin_p11_window_bruteforce(orc):
+    mpmath.mp.dps = 50
+    rng = RNG(1111)
+    for (n_q, n_k, d, wl, wr) in [(6, 6, 3, 1, 0), (7, 5, 2, 2, 1), (5, 8, 3, 0, 2), (8, 4, 2, 1, -1),
+                                  (4, 9, 3, -1, 3), (9, 3, 2, 0, 0)]:
+        q = rng.normal(size=(1, 1, n_q, d)) * 1.5
+        k = rng.normal(size=(1, 1, n_k, d)) * 1.5
+        v = rng.normal(size=(1, 1, n_k, d))
+        scale = 0.8
+        o, lse = orc.attention_window(q, k, v, wl, wr, scale)
+        for i in range(n_q):
+            lo, hi = _band(i, n_k, wl, wr)
+            if hi == lo:
+                assert np.all(o[0, 0, i] == 0) and np.isneginf(lse[0, 0, i]), (i, wl, wr)
+                continue
+            ex = []
+            for j in range(lo, hi):
+                s_ = mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(q[0, 0, i, c]) * mpmath.mpf(k[0, 0, j, c])
+                                                     for c in range(d))
+                ex.append(mpmath.e ** s_)
+            z = mpmath.fsum(ex)
+            for c in range(d):
+                ref = mpmath.fsum(ex[j - lo] * mpmath.mpf(v[0, 0, j, c]) for j in range(lo, hi)) / z
+                assert abs(o[0, 0, i, c] - float(ref)) <= 1e-13 * (1 + abs(float(ref))), (i, c, wl, wr)
+            assert abs(lse[0, 0, i] - float(mpmath.log(z))) <= 1e-13 * (1 + abs(float(mpmath.log(z))))
+
+
+def pin_p12_window_special(orc):
+    rng = RNG(1212)
+    q = rng.normal(size=(2, 2, 23, 5))
+    k = rng.normal(size=(2, 2, 19, 5))
+    v = rng.normal(size=(2, 2, 19, 5))
+    for causal, (wl, wr) in ((False, (-1, -1)), (True, (-1, 0))):
+        o_ref, lse_ref = orc.attention(q, k, v, causal, 0.6)
+        o, lse = orc.attention_window(q, k, v, wl, wr, 0.6)
+        assert np.array_equal(o, o_ref) and np.array_equal(lse, lse_ref)
+    o_ref, lse_ref = orc.attention(q, k, v, False, 0.6)
+    o, lse = orc.attention_window(q, k, v, 40, 40, 0.6)
+    assert np.array_equal(o, o_ref) and np.array_equal(lse, lse_ref)
+    o, lse = orc.attention_window(q, k, v, 0, 0, 0.6)
+    n = 19
+    assert np.array_equal(o[:, :, :n], v)
+    s_ii = 0.6 * np.einsum("bhid,bhid->bhi", q[:, :, :n], k)
+    assert np.max(np.abs(lse[:, :, :n] - s_ii)) <= 1e-14
+    assert np.all(o[:, :, n:] == 0) and np.all(np.isneginf(lse[:, :, n:]))
+    # the row-selected bf16 entry point equals the full one on bf16-exact values
+    tb = [torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v)]
+    bits = [t.contiguous().view(torch.int16).numpy().view(np.uint16) for t in tb]
+    vals = [t.to(torch.float64).numpy() for t in tb]
+    rows = np.array([0, 7, 22, 23, 60, 91], dtype=np.int64)
+    for wl, wr in ((4, 0), (2, 3), (0, 0)):
+        o_full, lse_full = orc.attention_window(*vals, wl, wr, 0.6)
+        o_r, lse_r = orc.attention_window_rows_bf16(*bits, rows, wl, wr, 0.6)
+        assert np.array_equal(o_r, o_full.reshape(-1, 5)[rows])
+        assert np.array_equal(lse_r, lse_full.reshape(-1)[rows])
+
+
+def pin_p13_window_torch(orc):
+    rng = RNG(1313)
+    for (n_q, n_k, d, wl, wr) in [(40, 40, 8, 7, 0), (40, 40, 8, 5, 3), (33, 50, 16, 10, -1), (50, 33, 16, -1, 4),
+                                  (31, 31, 8, 0, 6)]:
+        q = rng.normal(size=(2, 2, n_q, d))
+        k = rng.normal(size=(2, 2, n_k, d))
+        v = rng.normal(size=(2, 2, n_k, d))
+        scale = 1.0 / math.sqrt(d)
+        o, lse = orc.attention_window(q, k, v, wl, wr, scale)
+        ii = torch.arange(n_q)[:, None]
+        jj = torch.arange(n_k)[None, :]
+        mask = torch.ones(n_q, n_k, dtype=torch.bool)
+        if wl >= 0:
+            mask &= jj >= ii - wl
+        if wr >= 0:
+            mask &= jj <= ii + wr
+        assert orc.window_pairs(n_q, n_k, wl, wr) == int(mask.sum())
+        rows = mask.any(dim=1).numpy()
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale).numpy()
+        assert np.max(np.abs(ref[:, :, rows] - o[:, :, rows])) <= 1e-12
+        scores = (torch.matmul(tq, tk.transpose(-1, -2)) * scale).masked_fill(~mask, float("-inf"))
+        lse_ref = torch.logsumexp(scores, dim=-1).numpy()
+        assert np.max(np.abs(lse_ref[:, :, rows] - lse[:, :, rows])) <= 1e-12
+        assert np.all(np.isneginf(lse[:, :, ~rows])) and np.all(o[:, :, ~rows] == 0)
+
+
+def window_recurrence_model(q, k, v, wl, wr, scale, block_r, block_c):
+    """The tiled online recurrence of recurrence_model with the band mask applied
+    per tile; rows that never see a key end with O = 0 and LSE = -inf."""
+    B, H, n_q, d = q.shape
+    n_k = k.shape[2]
+    o = np.zeros((B, H, n_q, d))
+    lse = np.zeros((B, H, n_q))
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, n_q, block_r):
+                r1 = min(r0 + block_r, n_q)
+                m = np.full(r1 - r0, -np.inf)
+                l_ = np.zeros(r1 - r0)
+                acc = np.zeros((r1 - r0, d))
+                for c0 in range(0, n_k, block_c):
+                    c1 = min(c0 + block_c, n_k)
+                    s = scale * (q[b, h, r0:r1] @ k[b, h, c0:c1].T)
+                    rows = np.arange(r0, r1)[:, None]
+                    cols = np.arange(c0, c1)[None, :]
+                    vis = np.ones_like(s, dtype=bool)
+                    if wl >= 0:
+                        vis &= cols >= rows - wl
+                    if wr >= 0:
+                        vis &= cols <= rows + wr
+                    s = np.where(vis, s, -np.inf)
+                    m_new = np.maximum(m, s.max(axis=1))
+                    m_use = np.where(np.isneginf(m_new), 0.0, m_new)
+                    p = np.exp(s - m_use[:, None])
+                    alpha = np.exp(m - m_use)
+                    acc = acc * alpha[:, None] + p @ v[b, h, c0:c1]
+                    l_ = l_ * alpha + p.sum(axis=1)
+                    m = m_new
+                seen = l_ > 0
+                o[b, h, r0:r1] = np.where(seen[:, None], acc / np.where(seen, l_, 1.0)[:, None], 0.0)
+                lse[b, h, r0:r1] = np.where(seen, m + np.log(np.where(seen, l_, 1.0)), -np.inf)
+    return o, lse
+
+
+def pin_p14_window_recurrence(orc):
+    rng = RNG(1414)
+    q = rng.normal(size=(1, 2, 41, 8))
+    k = rng.normal(size=(1, 2, 37, 8))
+    v = rng.normal(size=(1, 2, 37, 8))
+    for wl, wr in [(9, 0), (3, 5), (0, 0), (-1, 2), (12, -1)]:
+        o, lse = orc.attention_window(q, k, v, wl, wr, 0.35)
+        for block_r, block_c in [(1, 1), (4, 7), (16, 5), (64, 64)]:
+            o_r, lse_r = window_recurrence_model(q, k, v, wl, wr, 0.35, block_r, block_c)
+            assert np.max(np.abs(o_r - o)) <= 1e-12
+            fin = np.isfinite(lse)
+            assert np.array_equal(fin, np.isfinite(lse_r))
+            assert np.max(np.abs(lse_r[fin] - lse[fin])) <= 1e-12
+
+
 ALL_PINS = [pin_p1_bruteforce, pin_p2_rows_sum_to_one, pin_p3_constant_v, pin_p4_causal_row0,
             pin_p5_uniform_scores, pin_p6_one_hot, pin_p7_lse_identity, pin_p8_torch_sdpa,
-            pin_p9_invariants, pin_p10_recurrence]
+            pin_p9_invariants, pin_p10_recurrence, pin_p11_window_bruteforce, pin_p12_window_special,
+            pin_p13_window_torch, pin_p14_window_recurrence]

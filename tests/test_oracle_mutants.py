@@ -26,6 +26,10 @@ MUTANTS = [
     ("merge_weights_dropped", "const double w = exp(mc - M);", "const double w = 1.0;"),
     ("feature_index_reversed", "for (int c = 0; c < d; ++c) dot += q[c] * kj[c];",
      "for (int c = 0; c < d; ++c) dot += q[c] * kj[d - 1 - c];"),
+    ("window_left_off_by_one", "if (wl >= 0 && i - wl > lo) lo = i - wl;", "if (wl >= 0 && i - wl + 1 > lo) lo = i - wl + 1;"),
+    ("window_right_off_by_one", "if (wr >= 0 && i + wr + 1 < hi) hi = i + wr + 1;", "if (wr >= 0 && i + wr < hi) hi = i + wr;"),
+    ("window_sides_swapped", "if (wl >= 0 && i - wl > lo) lo = i - wl;", "if (wr >= 0 && i - wr > lo) lo = i - wr;"),
+    ("window_empty_lse_zero", "*lse = -INFINITY; /* o is already zero */", "*lse = 0.0;"),
     ("first_key_skipped", "for (int64_t j = j0; j < j1; ++j) {\n    double p = exp", "for (int64_t j = j0 + 1; j < j1; ++j) {\n    double p = exp"),
 ]
 
