@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 import workloads  # noqa: E402
@@ -75,8 +76,6 @@ def cpu_baseline(w, causal: bool, q, k, v):
     """The fp64 oracle on a bounded sample of query rows of the workload, spread
     over all heads (about 15 s of host work), in TFLOP/s with the same FLOP count
     per row as the GPU figure."""
-    import numpy as np
-
     import oracle
 
     bits = [workloads.bf16_bits(t) for t in (q, k, v)]  # whole tensors on the host
@@ -184,6 +183,26 @@ def main():
             extra.append({"workload": wx.name, "causal": cx, "ms": round(msx, 4), "TFLOP/s": round(tf, 2),
                           "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
             log(f"{wx.name} causal={cx}: {msx:.3f} ms, {tf:.1f} TFLOP/s")
+            del qx, kx, vx, ox, lx
+        # sliding window on the long-sequence shape: causal attention over the last 4096 positions;
+        # FLOPs counted over the visible (query, key) pairs, 4*d per pair
+        for (wl, wr) in ((4095, 0),):
+            wx = workloads.C4
+            qx, kx, vx = workloads.make_qkv(wx, dev)
+            ox = torch.empty_like(qx)
+            lx = torch.empty((wx.B, wx.H, wx.n_q), dtype=torch.float32, device=dev)
+            msx = time_launches(lambda: fa2.forward_window(qx, kx, vx, wl, wr, scale=wx.scale, out=ox, lse=lx),
+                                steps_x, args.warmup)
+            i = np.arange(wx.n_q)
+            lo = np.maximum(0, i - wl) if wl >= 0 else np.zeros_like(i)
+            hi = np.minimum(wx.n_k, i + wr + 1) if wr >= 0 else np.full_like(i, wx.n_k)
+            pairs = int(np.maximum(hi - lo, 0).sum())
+            fl = 4.0 * wx.d * wx.B * wx.H * pairs
+            tf = fl / (msx * 1e-3) / 1e12
+            extra.append({"workload": f"{wx.name}_window_{wl}_{wr}", "window": [wl, wr], "ms": round(msx, 4),
+                          "TFLOP/s": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                          "visible_pairs_per_head": pairs})
+            log(f"{wx.name} window ({wl},{wr}): {msx:.3f} ms, {tf:.1f} TFLOP/s")
             del qx, kx, vx, ox, lx
         # split-KV decode: bound by streaming K and V from HBM
         wd = workloads.C5

@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     attention,
     forward,
     forward_splitkv,
+    forward_window,
     lib_path,
     load_library,
     num_splits,

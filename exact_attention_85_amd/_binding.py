@@ -45,6 +45,8 @@ def load_library():
     lib.fa2_splitkv_workspace_bytes.restype = ctypes.c_size_t
     lib.fa2_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, ctypes.c_size_t, vp]
     lib.fa2_fwd_splitkv.restype = i
+    lib.fa2_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.fa2_fwd_window.restype = i
     lib.fa2_num_splits.argtypes = [i, i, i, i, i, i]
     lib.fa2_num_splits.restype = i
     lib.fa2_status_string.argtypes = [i]
@@ -101,6 +103,23 @@ def forward(q, k, v, causal: bool = False, scale=None, out=None, lse=None):
         lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
     rc = lib.fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                      B, H, n_q, n_k, d, int(bool(causal)), _scale(scale, d), _stream_handle(q.device))
+    _check(rc)
+    return out, lse
+
+
+def forward_window(q, k, v, window_left: int, window_right: int, scale=None, out=None, lse=None):
+    """Sliding-window attention via fa2_fwd_window: key j visible to query i iff
+    (window_left < 0 or j >= i - window_left) and (window_right < 0 or j <= i + window_right).
+    Returns (o, lse); rows that see no key get O = 0 and LSE = -inf."""
+    lib = load_library()
+    B, H, n_q, n_k, d = _check_inputs(q, k, v)
+    if out is None:
+        out = torch.empty((B, H, n_q, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    rc = lib.fa2_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            B, H, n_q, n_k, d, int(window_left), int(window_right), _scale(scale, d),
+                            _stream_handle(q.device))
     _check(rc)
     return out, lse
 

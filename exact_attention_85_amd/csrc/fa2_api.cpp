@@ -11,6 +11,7 @@ namespace {
 
 constexpr long long kMaxGrid = (1LL << 31) - 1;
 constexpr long long kMaxHeadElems = (1LL << 30) - 1;  // one head's Q or K/V below 2^31 bytes
+constexpr int kMaxWindow = 1 << 30;                   // keeps row +- window inside int
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
@@ -64,7 +65,8 @@ fa2::FwdParams make_params(const void* Q, const void* K, const void* V, void* O,
   p.n_q = N_q;
   p.n_k = N_k;
   p.d = d;
-  p.causal = causal ? 1 : 0;
+  p.wl = -1;
+  p.wr = causal ? 0 : -1;
   p.scale = scale;
   p.num_splits = 1;
   p.split_len = N_k;
@@ -84,6 +86,23 @@ int fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   rc = check_alias(Q, K, V, O, LSE, B, H, N_q, N_k, d, nullptr, 0);
   if (rc != FA2_OK) return rc;
   const fa2::FwdParams p = make_params(Q, K, V, O, LSE, B, H, N_q, N_k, d, causal, scale);
+  if (fa2::launch_fwd(p, static_cast<hipStream_t>(stream)) != hipSuccess) return FA2_ERR_HIP;
+  return FA2_OK;
+}
+
+int fa2_fwd_window(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q,
+                   int N_k, int d, int window_left, int window_right, float scale, void* stream) {
+  int rc = check_common(Q, K, V, O, LSE, B, H, N_q, N_k, d, scale);
+  if (rc != FA2_OK) return rc;
+  if (window_left < -1 || window_right < -1 || window_left > kMaxWindow || window_right > kMaxWindow)
+    return FA2_ERR_WINDOW;
+  const int br = 128;
+  if ((long long)((N_q + br - 1) / br) * B * H > kMaxGrid) return FA2_ERR_BAD_SHAPE;
+  rc = check_alias(Q, K, V, O, LSE, B, H, N_q, N_k, d, nullptr, 0);
+  if (rc != FA2_OK) return rc;
+  fa2::FwdParams p = make_params(Q, K, V, O, LSE, B, H, N_q, N_k, d, 0, scale);
+  p.wl = window_left;
+  p.wr = window_right;
   if (fa2::launch_fwd(p, static_cast<hipStream_t>(stream)) != hipSuccess) return FA2_ERR_HIP;
   return FA2_OK;
 }
@@ -158,6 +177,7 @@ const char* fa2_status_string(int status) {
     case FA2_ERR_ALIAS: return "FA2_ERR_ALIAS: an output overlaps an input, another output or the workspace";
     case FA2_ERR_SPLITS: return "FA2_ERR_SPLITS: num_splits must be in [1, min(N_k, FA2_MAX_SPLITS)]";
     case FA2_ERR_HIP: return "FA2_ERR_HIP: the HIP runtime rejected a kernel launch";
+    case FA2_ERR_WINDOW: return "FA2_ERR_WINDOW: window sizes must be -1 (unbounded) or in [0, 2^30]";
     default: return "unknown fa2 status";
   }
 }

@@ -211,15 +211,17 @@ __device__ __forceinline__ void qk_tile(const WaveRows<D>& w, const LdsAddr<D>& 
   }
 }
 
-// -inf for keys past kend or, causal, above the query row.  Key k0 + 4hf + c
-// is visible iff c <= lim; c is a compile-time constant per register.
-__device__ __forceinline__ void mask_scores(f32x16& s0, f32x16& s1, int k0, int kend, int row, int causal, int hf) {
-  const int lim = (causal ? min(row, kend - 1) : kend - 1) - k0 - 4 * hf;
+// -inf for keys outside this lane's row band [row_lo, row_hi] (the band already
+// clipped to the key tail).  Key k0 + 4hf + c is visible iff lo <= c <= hi; c is
+// a compile-time constant per register.
+__device__ __forceinline__ void mask_scores(f32x16& s0, f32x16& s1, int k0, int row_lo, int row_hi, int hf) {
+  const int hi = row_hi - k0 - 4 * hf;
+  const int lo = row_lo - k0 - 4 * hf;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int c = 8 * (r >> 2) + (r & 3);
-    if (c > lim) s0[r] = -INFINITY;
-    if (c + 32 > lim) s1[r] = -INFINITY;
+    if (c > hi || c < lo) s0[r] = -INFINITY;
+    if (c + 32 > hi || c + 32 < lo) s1[r] = -INFINITY;
   }
 }
 
@@ -271,14 +273,14 @@ __device__ __forceinline__ float sum_bf16(const bf16x8 (&pb)[4], float acc) {
 constexpr float kLazyBound = 2048.f;
 
 template <int D, unsigned KOFF, unsigned VOFF>
-__device__ __forceinline__ void tile_step(WaveRows<D>& w, const LdsAddr<D>& la, bool need_mask, int k0, int kend,
-                                          int row, int causal, float sl2, int lane) {
+__device__ __forceinline__ void tile_step(WaveRows<D>& w, const LdsAddr<D>& la, bool need_mask, int k0, int row_lo,
+                                          int row_hi, float sl2, int lane) {
   constexpr int NB = D / 32;
   constexpr unsigned ROW = D * 2;
   const int hf = lane >> 5;
   f32x16 s0, s1;
   qk_tile<D, KOFF>(w, la, s0, s1);
-  if (need_mask) mask_scores(s0, s1, k0, kend, row, causal, hf);
+  if (need_mask) mask_scores(s0, s1, k0, row_lo, row_hi, hf);
 
   bool exact = __ballot(w.m_run == -INFINITY) != 0;  // some row has no reference yet
   float rs = 0.f;
@@ -287,7 +289,7 @@ __device__ __forceinline__ void tile_step(WaveRows<D>& w, const LdsAddr<D>& la, 
     if (__ballot(rs > kLazyBound)) {
       exact = true;
       qk_tile<D, KOFF>(w, la, s0, s1);  // scores again (the K tile is still in LDS)
-      if (need_mask) mask_scores(s0, s1, k0, kend, row, causal, hf);
+      if (need_mask) mask_scores(s0, s1, k0, row_lo, row_hi, hf);
     }
   }
   if (exact) {
@@ -372,7 +374,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
   }
   const int bh = L / n_qb;
   int qb = L % n_qb;
-  if (p.causal) qb = n_qb - 1 - qb;  // heaviest query blocks are dispatched first
+  const int wl = p.wl, wr = p.wr;  // key band [i - wl, i + wr] of query i; -1: unbounded
+  if (wl < 0 && wr >= 0) qb = n_qb - 1 - qb;  // causal-like band: heaviest query blocks first
   const int q0 = qb * BR;
   const int q0w = q0 + wave * 32;
   const int row = q0w + col;
@@ -383,13 +386,22 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
     kbeg = b < p.n_k ? (int)b : p.n_k;
     kend = kbeg + p.split_len < p.n_k ? kbeg + p.split_len : p.n_k;
   }
-  // keys below khi are visible to some row of the workgroup, below khi_w to some row of this wave
-  int khi = kend, khi_w = kend;
-  if (p.causal) {
-    khi = min(khi, q0 + BR);
-    khi_w = min(khi_w, q0w + 32);
+  // Keys in [klo, khi) are visible to some row of the workgroup, keys in
+  // [klo_w, khi_w) to some row of this wave, keys in [row_lo, row_hi] to this
+  // lane's row.  Tiles stay aligned to kbeg; the first one holds klo.
+  int klo = kbeg, khi = kend, klo_w = kbeg, khi_w = kend, row_lo = kbeg, row_hi = kend - 1;
+  if (wr >= 0) {
+    khi = min(khi, q0 + BR + wr);
+    khi_w = min(khi_w, q0w + 32 + wr);
+    row_hi = min(row_hi, row + wr);
   }
-  const int n_tiles = khi > kbeg ? (khi - kbeg + kBC - 1) / kBC : 0;
+  if (wl >= 0) {
+    klo = max(klo, q0 - wl);
+    klo_w = max(klo_w, q0w - wl);
+    row_lo = max(row_lo, row - wl);
+  }
+  const int kfirst = kbeg + (klo - kbeg) / kBC * kBC;
+  const int n_tiles = khi > kfirst ? (khi - kfirst + kBC - 1) / kBC : 0;
 
   const uint16_t* Qh = p.q + (long long)bh * p.n_q * D;
   const i32x4 krs = raw_rsrc(p.k + (long long)bh * p.n_k * D, (long long)khi * D * 2);
@@ -416,19 +428,22 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
   make_lds_addr<D>(la, (unsigned)(uintptr_t)(const lds_void*)&lds[0][0][0], lane);
   constexpr unsigned STAGE = 2 * TILE_BYTES;
 
-  // a tile needs masking when it crosses this wave's causal diagonal or the key tail
+  // A tile is skipped when no row of this wave sees any of its keys, and
+  // masked when it crosses either edge of the wave's band or the key tail.
 #define FA2_STEP(STG, k0_)                                                                             \
   do {                                                                                               \
     const int kk = (k0_);                                                                            \
-    if (kk < khi_w)                                                                                  \
+    if (kk < khi_w && kk + kBC > klo_w)                                                              \
       tile_step<D, STG * STAGE, STG * STAGE + TILE_BYTES>(                                           \
-          w, la, (kk + kBC > kend) || (p.causal && kk + kBC - 1 > q0w), kk, kend, row, p.causal, sl2, lane); \
+          w, la,                                                                                     \
+          (kk + kBC > kend) || (wr >= 0 && kk + kBC - 1 > q0w + wr) || (wl >= 0 && kk < q0w + 31 - wl), \
+          kk, row_lo, row_hi, sl2, lane);                                                            \
   } while (0)
 
   // unrolled by two so that each stage's LDS offsets are compile-time constants
-  if (n_tiles > 0) issue_tile<D, NW>(krs, vrs, lds[0][0], lds[0][1], kbeg, wave, lane);
+  if (n_tiles > 0) issue_tile<D, NW>(krs, vrs, lds[0][0], lds[0][1], kfirst, wave, lane);
   for (int j = 0; j < n_tiles; j += 2) {
-    const int k0 = kbeg + j * kBC;
+    const int k0 = kfirst + j * kBC;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (j + 1 < n_tiles) issue_tile<D, NW>(krs, vrs, lds[1][0], lds[1][1], k0 + kBC, wave, lane);
@@ -447,7 +462,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
   const float l16_tot = w.l16 + __shfl_xor(w.l16, 32);
   if (row >= p.n_q) return;
   if (!SPLIT) {
-    const float inv = 1.f / l16_tot;
+    const float inv = l16_tot > 0.f ? 1.f / l16_tot : 0.f;  // a row with no visible key: O = 0
     uint16_t* Orow = p.o + ((long long)bh * p.n_q + row) * D;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -459,7 +474,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
         const bf16x4 b4 = __builtin_convertvector(o4, bf16x4);
         *reinterpret_cast<u32x2*>(Orow + 32 * nb + 8 * g + 4 * hf) = __builtin_bit_cast(u32x2, b4);
       }
-    if (hf == 0) p.lse[(long long)bh * p.n_q + row] = (w.m_run + __log2f(l_tot)) * kLn2;
+    if (hf == 0) p.lse[(long long)bh * p.n_q + row] = l_tot > 0.f ? (w.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
     const long long R = (long long)p.B * p.H * p.n_q;
     const long long rg = (long long)bh * p.n_q + row;
@@ -515,7 +530,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(FwdParams p
   const long long b0 = (long long)split * p.split_len;
   const int kbeg = b0 < p.n_k ? (int)b0 : p.n_k;
   int kend = kbeg + p.split_len < p.n_k ? kbeg + p.split_len : p.n_k;
-  if (p.causal) kend = min(kend, 1);  // the single query row 0 sees key 0 only
+  if (p.wr >= 0) kend = min(kend, p.wr + 1);  // the single query row 0 sees keys 0 .. wr
 
   // loads past key kend return zero (range check on the per-lane offset)
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + (long long)bh * p.n_k * D, (long long)kend * D * 2);
@@ -663,14 +678,14 @@ __global__ void __launch_bounds__(256) splitkv_merge_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) o[i] += w * a[lane + 64 * i];
   }
-  const float inv = 1.f / lsum;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;  // no visible key in any chunk: O = 0, LSE = -inf
   uint16_t* orow = p.o + rg * D;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const __bf16 b = (__bf16)(o[i] * inv);
     orow[lane + 64 * i] = __builtin_bit_cast(uint16_t, b);
   }
-  if (lane == 0) p.lse[rg] = M + __logf(llsum);
+  if (lane == 0) p.lse[rg] = llsum > 0.f ? M + __logf(llsum) : -INFINITY;
 }
 
 // scale handling shared by all launches: fold |scale|*log2(e) into one positive

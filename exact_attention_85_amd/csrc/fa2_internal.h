@@ -20,7 +20,8 @@ struct FwdParams {
   float* ws_l;       // split mode: [S][R] sums of the probabilities as accumulated in acc
   float* ws_ll;      // split mode: [S][R] fp32 sums of the probabilities (for LSE)
   int B, H, n_q, n_k, d;
-  int causal;
+  int wl, wr;        // key band [i - wl, i + wr] of query i (top-left aligned); -1: unbounded.
+                     // Plain attention is (-1, -1), the causal mask (-1, 0).
   float scale;
   int num_splits;    // 1 in forward mode
   int split_len;     // keys per chunk (N_k in forward mode)

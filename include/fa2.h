@@ -51,7 +51,8 @@ typedef enum fa2_status {
   FA2_ERR_WORKSPACE = -5, /* split-KV workspace NULL or smaller than fa2_splitkv_workspace_bytes() */
   FA2_ERR_ALIAS = -6,     /* an output overlaps an input, another output or the workspace */
   FA2_ERR_SPLITS = -7,    /* num_splits outside [1, min(N_k, FA2_MAX_SPLITS)] */
-  FA2_ERR_HIP = -8        /* the HIP runtime rejected a kernel launch */
+  FA2_ERR_HIP = -8,       /* the HIP runtime rejected a kernel launch */
+  FA2_ERR_WINDOW = -9     /* a window size below -1 or above 2^30 */
 } fa2_status;
 
 /* Size limits (validated): N_k * d and N_q * d below 2^30 per head (one
@@ -80,6 +81,28 @@ typedef enum fa2_status {
  */
 int fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
             int B, int H, int N_q, int N_k, int d, int causal, float scale, void* stream);
+
+/*
+ * fa2_fwd_window — sliding-window (banded) attention forward (the synthesis
+ * page, section 5 item 4: the causal block skip generalised to a window).
+ *
+ * Key j is visible to query i iff j < N_k and
+ *   (window_left  < 0 or j >= i - window_left)  and
+ *   (window_right < 0 or j <= i + window_right),
+ * top-left aligned like the causal mask.  (-1, -1) is plain attention and
+ * (-1, 0) is fa2_fwd's causal mask; (w - 1, 0) is causal attention over the
+ * last w positions.  Each workgroup streams only the key tiles its rows can
+ * see; tiles wholly inside every row's band run unmasked, tiles crossing an
+ * edge are masked.  A row that sees no key (possible when N_q > N_k or the
+ * band misses every key) gets O = 0 and LSE = -inf.
+ *
+ * Arguments, layouts and errors as fa2_fwd, plus window_left, window_right:
+ * -1 (unbounded) or 0 .. 2^30, else FA2_ERR_WINDOW.  A single query row
+ * (N_q == 1) sees keys 0 .. window_right.
+ */
+int fa2_fwd_window(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                   int B, int H, int N_q, int N_k, int d, int window_left, int window_right,
+                   float scale, void* stream);
 
 /*
  * fa2_splitkv_workspace_bytes — bytes of caller-owned device workspace that

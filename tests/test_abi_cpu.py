@@ -12,7 +12,7 @@ import exact_attention_85_amd as fa2
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa2.h")
 
-OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, SPLITS, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, SPLITS, HIP, WINDOW = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
 
 def declared_functions():
@@ -22,8 +22,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa2_fwd", "fa2_fwd_splitkv", "fa2_num_splits", "fa2_splitkv_workspace_bytes",
-                                    "fa2_status_string"]
+    assert declared_functions() == ["fa2_fwd", "fa2_fwd_splitkv", "fa2_fwd_window", "fa2_num_splits",
+                                    "fa2_splitkv_workspace_bytes", "fa2_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in (OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, SPLITS, HIP):
+    for code in (OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, SPLITS, HIP, WINDOW):
         s = fa2.status_string(code)
         assert s and "unknown" not in s
     assert "unknown" in fa2.status_string(12345)
@@ -154,3 +154,18 @@ def test_num_splits_errors():
     with pytest.raises(fa2.Fa2Error) as e:
         fa2.num_splits(1, 1, 1, 1, 96, num_cus=CUS)
     assert e.value.status == HEAD_DIM
+
+
+def window(q=Q, k=K, v=V, o=O, l=L, B=1, H=2, nq=256, nk=256, d=64, wl=16, wr=0, scale=0.125):
+    lib = fa2.load_library()
+    return lib.fa2_fwd_window(q, k, v, o, l, B, H, nq, nk, d, wl, wr, scale, None)
+
+
+def test_window_validation():
+    for wl, wr in ((-2, 0), (0, -2), ((1 << 30) + 1, 0), (0, (1 << 30) + 1), (-7, -7)):
+        assert window(wl=wl, wr=wr) == WINDOW
+    assert window(q=None) == NULLPTR
+    assert window(d=96) == HEAD_DIM
+    assert window(nk=0) == BAD_SHAPE
+    assert window(scale=float("nan")) == BAD_SCALE
+    assert window(o=Q) == ALIAS
