@@ -54,6 +54,8 @@ def _load():
                                                       _i, _i, _i, _i, _i, _i, _i, ctypes.c_double]
     lib.oracle_window_pairs.argtypes = [_i, _i, _i, _i]
     lib.oracle_window_pairs.restype = ctypes.c_int64
+    lib.oracle_backward_f64.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _i, _i, _i, _i, _i, _i,
+                                        ctypes.c_double]
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -199,3 +201,21 @@ def attention_window_rows_bf16(q_bits, k_bits, v_bits, rows, window_left: int, w
 def window_pairs(n_q: int, n_k: int, window_left: int, window_right: int) -> int:
     """Visible (query, key) pairs of one head under the window."""
     return int(_load().oracle_window_pairs(int(n_q), int(n_k), int(window_left), int(window_right)))
+
+
+def backward(q, k, v, do, causal: bool, scale: float):
+    """Gradients (dQ, dK, dV) of exact attention for upstream gradient dO, in fp64:
+    P = softmax(scale Q K^T [+ causal mask]), dV = P^T dO, dS = P * (dO V^T - rowsum(dO * O)),
+    dQ = scale dS K, dK = scale dS^T Q."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, n_q, d = q.shape
+    n_k = k.shape[2]
+    assert k.shape == (B, H, n_k, d) and v.shape == (B, H, n_k, d) and do.shape == q.shape
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    rc = _load().oracle_backward_f64(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(do, _dp), _ptr(dq, _dp),
+                                     _ptr(dk, _dp), _ptr(dv, _dp), B, H, n_q, n_k, d, int(bool(causal)),
+                                     float(scale))
+    _check(rc, "backward")
+    return dq, dk, dv

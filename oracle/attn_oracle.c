@@ -361,6 +361,92 @@ int64_t oracle_window_pairs(int n_q, int n_k, int wl, int wr) {
   return total;
 }
 
+/*
+ * Backward pass (the synthesis page, section 3 item 1 and section 5 item 2:
+ * the gradients of exact attention from the stored LSE; FA2's five products).
+ * For a scalar loss with upstream gradient dO of the output O, per (b, h):
+ *   P_ij  = exp(s_ij - LSE_i) over allowed j, 0 elsewhere   (s_ij = scale q_i . k_j)
+ *   dV_j  = sum_i P_ij dO_i
+ *   dP_ij = dO_i . v_j
+ *   D_i   = sum_c dO_ic O_ic            (= sum_j P_ij dP_ij)
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = scale * sum_j dS_ij k_j
+ *   dK_j  = scale * sum_i dS_ij q_i
+ * O and LSE are recomputed here in fp64 (plain two-pass softmax) rather than
+ * taken from the caller, so the gradients are those of exact attention.
+ * Causal masking is top-left as in the forward.  Returns 0, or -1.
+ */
+int oracle_backward_f64(const double* Q, const double* K, const double* V, const double* dO, double* dQ,
+                        double* dK, double* dV, int B, int H, int n_q, int n_k, int d, int causal, double scale) {
+  if (check_shape(B, H, n_q, n_k, d)) return -1;
+  int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+    const double* q = Q + bh * (int64_t)n_q * d;
+    const double* k = K + bh * (int64_t)n_k * d;
+    const double* v = V + bh * (int64_t)n_k * d;
+    const double* go = dO + bh * (int64_t)n_q * d;
+    double* gq = dQ + bh * (int64_t)n_q * d;
+    double* gk = dK + bh * (int64_t)n_k * d;
+    double* gv = dV + bh * (int64_t)n_k * d;
+    double* P = (double*)malloc(sizeof(double) * (size_t)n_q * n_k);
+    double* dS = (double*)malloc(sizeof(double) * (size_t)n_q * n_k);
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!P || !dS || !o) {
+#pragma omp atomic write
+      failed = 1;
+      free(P); free(dS); free(o);
+      continue;
+    }
+    for (int64_t i = 0; i < n_q; ++i) {
+      const int64_t n_allowed = allowed_prefix(i, n_k, causal);
+      double* prow = P + i * n_k;
+      double m = -INFINITY;
+      for (int64_t j = 0; j < n_allowed; ++j) {
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c) dot += q[i * d + c] * k[j * d + c];
+        prow[j] = scale * dot;
+        if (prow[j] > m) m = prow[j];
+      }
+      double l = 0.0;
+      for (int64_t j = 0; j < n_allowed; ++j) l += exp(prow[j] - m);
+      const double lse = m + log(l);
+      for (int64_t j = 0; j < n_k; ++j) prow[j] = (j < n_allowed) ? exp(prow[j] - lse) : 0.0;
+      /* O_i and D_i */
+      for (int c = 0; c < d; ++c) o[c] = 0.0;
+      for (int64_t j = 0; j < n_allowed; ++j)
+        for (int c = 0; c < d; ++c) o[c] += prow[j] * v[j * d + c];
+      double Di = 0.0;
+      for (int c = 0; c < d; ++c) Di += go[i * d + c] * o[c];
+      /* dS_ij = P_ij (dO_i . v_j - D_i) */
+      for (int64_t j = 0; j < n_k; ++j) {
+        if (j >= n_allowed) { dS[i * n_k + j] = 0.0; continue; }
+        double dp = 0.0;
+        for (int c = 0; c < d; ++c) dp += go[i * d + c] * v[j * d + c];
+        dS[i * n_k + j] = prow[j] * (dp - Di);
+      }
+    }
+    for (int64_t i = 0; i < n_q; ++i)
+      for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < n_k; ++j) acc += dS[i * n_k + j] * k[j * d + c];
+        gq[i * d + c] = scale * acc;
+      }
+    for (int64_t j = 0; j < n_k; ++j)
+      for (int c = 0; c < d; ++c) {
+        double acck = 0.0, accv = 0.0;
+        for (int64_t i = 0; i < n_q; ++i) {
+          acck += dS[i * n_k + j] * q[i * d + c];
+          accv += P[i * n_k + j] * go[i * d + c];
+        }
+        gk[j * d + c] = scale * acck;
+        gv[j * d + c] = accv;
+      }
+    free(P); free(dS); free(o);
+  }
+  return failed ? -1 : 0;
+}
+
 /* Threads the parallel regions above use (reported beside CPU timings). */
 #ifdef _OPENMP
 #include <omp.h>

@@ -29,6 +29,15 @@ to query i iff j < N_k, j >= i - wl (wl >= 0) and j <= i + wr (wr >= 0):
       out as a boolean mask, and the visible-pair count against that mask;
   P14 the tiled online recurrence of P10 with the band mask applied per tile.
 
+Backward pins (gradients of exact attention for an upstream gradient dO):
+
+  P15 central finite differences of L = sum(dO * O(Q, K, V)) through the
+      pinned forward oracle, for every element of Q, K and V on tiny shapes;
+  P16 torch's fp64 CPU autograd through scaled_dot_product_attention;
+  P17 identities: sum_j dK_j = 0 (softmax is invariant to a shift of all
+      keys' scores of a row), sum_j dV_j = sum_i dO_i (rows of P sum to 1),
+      dV linear in dO, and all gradients zero for dO = 0.
+
 The definition pinned is exact attention with top-left causal masking
 (key j allowed for query i iff j <= i), scale applied to q.k before the
 softmax, and LSE the natural log of sum exp of the scaled, masked scores.
@@ -433,7 +442,66 @@ def pin_p14_window_recurrence(orc):
             assert np.max(np.abs(lse_r[fin] - lse[fin])) <= 1e-12
 
 
+def pin_p15_backward_finite_differences(orc):
+    rng = RNG(1515)
+    for (n_q, n_k, d, causal) in [(4, 5, 3, False), (5, 5, 3, True), (3, 6, 2, True)]:
+        q = rng.normal(size=(1, 1, n_q, d))
+        k = rng.normal(size=(1, 1, n_k, d))
+        v = rng.normal(size=(1, 1, n_k, d))
+        do = rng.normal(size=(1, 1, n_q, d))
+        scale = 0.7
+        dq, dk, dv = orc.backward(q, k, v, do, causal, scale)
+
+        def loss(qq, kk, vv):
+            o, _ = orc.attention(qq, kk, vv, causal, scale)
+            return float(np.sum(do * o))
+
+        h = 1e-6
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = [xp if name == n else a for n, a in (("q", q), ("k", k), ("v", v))]
+                args_m = [xm if name == n else a for n, a in (("q", q), ("k", k), ("v", v))]
+                fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+                assert abs(fd - g[idx]) <= 1e-7 * (1 + abs(fd)), (name, idx, causal, fd, g[idx])
+
+
+def pin_p16_backward_torch(orc):
+    rng = RNG(1616)
+    for (n_q, n_k, d, causal) in [(21, 21, 8, False), (21, 21, 8, True), (13, 30, 16, True), (30, 13, 16, True),
+                                  (17, 40, 8, False)]:
+        q, k, v = (rng.normal(size=(2, 2, n, d)) for n in (n_q, n_k, n_k))
+        do = rng.normal(size=(2, 2, n_q, d))
+        scale = 1.0 / math.sqrt(d)
+        dq, dk, dv = orc.backward(q, k, v, do, causal, scale)
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        mask = torch.ones(n_q, n_k, dtype=torch.bool).tril() if causal else None
+        o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale)
+        o.backward(torch.from_numpy(do))
+        for ref, got in ((tq.grad, dq), (tk.grad, dk), (tv.grad, dv)):
+            assert np.max(np.abs(ref.numpy() - got)) <= 1e-12
+
+
+def pin_p17_backward_identities(orc):
+    rng = RNG(1717)
+    q, k, v = (rng.normal(size=(1, 2, n, 6)) for n in (11, 14, 14))
+    do = rng.normal(size=(1, 2, 11, 6))
+    do2 = rng.normal(size=(1, 2, 11, 6))
+    for causal in (False, True):
+        dq, dk, dv = orc.backward(q, k, v, do, causal, 0.5)
+        assert np.max(np.abs(dk.sum(axis=2))) <= 1e-12
+        assert np.max(np.abs(dv.sum(axis=2) - do.sum(axis=2))) <= 1e-12
+        _, _, dv2 = orc.backward(q, k, v, do2, causal, 0.5)
+        _, _, dv3 = orc.backward(q, k, v, 2.0 * do - 0.5 * do2, causal, 0.5)
+        assert np.max(np.abs(dv3 - (2.0 * dv - 0.5 * dv2))) <= 1e-12
+        z = orc.backward(q, k, v, np.zeros_like(do), causal, 0.5)
+        assert all(np.all(g == 0) for g in z)
+
+
 ALL_PINS = [pin_p1_bruteforce, pin_p2_rows_sum_to_one, pin_p3_constant_v, pin_p4_causal_row0,
             pin_p5_uniform_scores, pin_p6_one_hot, pin_p7_lse_identity, pin_p8_torch_sdpa,
             pin_p9_invariants, pin_p10_recurrence, pin_p11_window_bruteforce, pin_p12_window_special,
-            pin_p13_window_torch, pin_p14_window_recurrence]
+            pin_p13_window_torch, pin_p14_window_recurrence, pin_p15_backward_finite_differences,
+            pin_p16_backward_torch, pin_p17_backward_identities]
