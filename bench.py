@@ -204,6 +204,22 @@ def main():
                           "visible_pairs_per_head": pairs})
             log(f"{wx.name} window ({wl},{wr}): {msx:.3f} ms, {tf:.1f} TFLOP/s")
             del qx, kx, vx, ox, lx
+        # backward (deterministic two-pass dQ): FLOPs 2.5x the forward's (five products instead of two)
+        for wx, cx in ((workloads.C3, False), (workloads.C3, True), (workloads.C4, False)):
+            qx, kx, vx = workloads.make_qkv(wx, dev)
+            dox = workloads.make_tensor(wx.index, 3, wx.B, wx.H, wx.n_q, wx.d, dev)
+            ox, lx = fa2.forward(qx, kx, vx, causal=cx, scale=wx.scale)
+            wsx = torch.empty(fa2.bwd_workspace_bytes(wx.B, wx.H, wx.n_q, wx.n_k, wx.d) // 4, dtype=torch.float32,
+                              device=dev)
+            gq, gk, gv = torch.empty_like(qx), torch.empty_like(kx), torch.empty_like(vx)
+            msx = time_launches(lambda: fa2.backward(qx, kx, vx, ox, lx, dox, causal=cx, scale=wx.scale,
+                                                     workspace=wsx, dq=gq, dk=gk, dv=gv), steps_x, args.warmup)
+            tf = 2.5 * wx.flop(cx) / (msx * 1e-3) / 1e12
+            extra.append({"workload": f"{wx.name}_backward", "causal": cx, "ms": round(msx, 4), "TFLOP/s": round(tf, 2),
+                          "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flop": 2.5 * wx.flop(cx),
+                          "workspace_bytes": wsx.numel() * 4})
+            log(f"{wx.name} backward causal={cx}: {msx:.3f} ms, {tf:.1f} TFLOP/s")
+            del qx, kx, vx, dox, ox, lx, wsx, gq, gk, gv
         # split-KV decode: bound by streaming K and V from HBM
         wd = workloads.C5
         qd, kd, vd = workloads.make_qkv(wd, dev)

@@ -9,6 +9,8 @@ from ._binding import (  # noqa: F401
     FA2_MAX_SPLITS,
     Fa2Error,
     attention,
+    backward,
+    bwd_workspace_bytes,
     forward,
     forward_splitkv,
     forward_window,

@@ -47,6 +47,10 @@ def load_library():
     lib.fa2_fwd_splitkv.restype = i
     lib.fa2_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     lib.fa2_fwd_window.restype = i
+    lib.fa2_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa2_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa2_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, ctypes.c_size_t, vp]
+    lib.fa2_bwd.restype = i
     lib.fa2_num_splits.argtypes = [i, i, i, i, i, i]
     lib.fa2_num_splits.restype = i
     lib.fa2_status_string.argtypes = [i]
@@ -172,3 +176,31 @@ def attention(q, k, v, causal: bool = False, scale=None):
         return forward(q, k, v, causal=causal, scale=scale)
     o, lse, _ = forward_splitkv(q, k, v, num_splits=s, causal=causal, scale=scale)
     return o, lse
+
+
+def bwd_workspace_bytes(B, H, n_q, n_k, d) -> int:
+    return int(load_library().fa2_bwd_workspace_bytes(B, H, n_q, n_k, d))
+
+
+def backward(q, k, v, o, lse, do, causal: bool = False, scale=None, workspace=None, dq=None, dk=None, dv=None):
+    """Gradients (dq, dk, dv) of O = forward(q, k, v, causal, scale) for upstream
+    gradient do, from that forward's o and lse, via fa2_bwd (deterministic)."""
+    lib = load_library()
+    B, H, n_q, n_k, d = _check_inputs(q, k, v)
+    for name, t, shape in (("o", o, (B, H, n_q, d)), ("do", do, (B, H, n_q, d))):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != shape or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous bf16 {shape} tensor on q's device")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, n_q) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N_q] tensor")
+    need = lib.fa2_bwd_workspace_bytes(B, H, n_q, n_k, d)
+    if workspace is None:
+        workspace = torch.empty((max(need, 4) + 3) // 4, dtype=torch.float32, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    rc = lib.fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, n_q, n_k, d, int(bool(causal)),
+                     _scale(scale, d), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                     _stream_handle(q.device))
+    _check(rc)
+    return dq, dk, dv

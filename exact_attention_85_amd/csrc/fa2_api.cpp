@@ -166,6 +166,62 @@ int fa2_num_splits(int B, int H, int N_q, int N_k, int d, int num_cus) {
   return (int)s;
 }
 
+size_t fa2_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d) {
+  if (B < 1 || H < 1 || N_q < 1 || N_k < 1 || d < 1) return 0;
+  const size_t R = (size_t)B * (size_t)H * (size_t)N_q;
+  const size_t n_kb = ((size_t)N_k + 127) / 128;
+  return (2 * R + n_kb * R * (size_t)d) * 4u;
+}
+
+int fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
+            void* dK, void* dV, int B, int H, int N_q, int N_k, int d, int causal, float scale, void* workspace,
+            size_t workspace_bytes, void* stream) {
+  if (!dO || !dQ || !dK || !dV) return FA2_ERR_NULLPTR;
+  // the forward's own checks on Q, K, V, O, LSE (LSE read-only here)
+  int rc = check_common(Q, K, V, O, LSE, B, H, N_q, N_k, d, scale);
+  if (rc != FA2_OK) return rc;
+  const long long n_kb = (N_k + 127) / 128;
+  if (n_kb * B * H > kMaxGrid) return FA2_ERR_BAD_SHAPE;
+  const size_t need = fa2_bwd_workspace_bytes(B, H, N_q, N_k, d);
+  if (!workspace || workspace_bytes < need) return FA2_ERR_WORKSPACE;
+  // outputs must not overlap any input, each other or the workspace
+  const long long bh = (long long)B * H;
+  const Range in[6] = {range_of(Q, bh * N_q * d * 2), range_of(K, bh * N_k * d * 2), range_of(V, bh * N_k * d * 2),
+                       range_of(O, bh * N_q * d * 2), range_of(dO, bh * N_q * d * 2), range_of(LSE, bh * N_q * 4)};
+  const Range out[4] = {range_of(dQ, bh * N_q * d * 2), range_of(dK, bh * N_k * d * 2),
+                        range_of(dV, bh * N_k * d * 2), range_of(workspace, (long long)need)};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 6; ++b)
+      if (overlap(out[a], in[b])) return FA2_ERR_ALIAS;
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(out[a], out[b])) return FA2_ERR_ALIAS;
+  }
+  fa2::BwdParams p{};
+  p.q = static_cast<const uint16_t*>(Q);
+  p.k = static_cast<const uint16_t*>(K);
+  p.v = static_cast<const uint16_t*>(V);
+  p.o = static_cast<const uint16_t*>(O);
+  p.dout = static_cast<const uint16_t*>(dO);
+  p.lse = LSE;
+  p.dq = static_cast<uint16_t*>(dQ);
+  p.dk = static_cast<uint16_t*>(dK);
+  p.dv = static_cast<uint16_t*>(dV);
+  const long long R = bh * N_q;
+  float* ws = static_cast<float*>(workspace);
+  p.l2vec = ws;
+  p.dvec = ws + R;
+  p.ws_dq = ws + 2 * R;
+  p.B = B;
+  p.H = H;
+  p.n_q = N_q;
+  p.n_k = N_k;
+  p.d = d;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  if (fa2::launch_bwd(p, static_cast<hipStream_t>(stream)) != hipSuccess) return FA2_ERR_HIP;
+  return FA2_OK;
+}
+
 const char* fa2_status_string(int status) {
   switch (status) {
     case FA2_OK: return "FA2_OK: success";

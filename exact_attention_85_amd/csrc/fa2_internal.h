@@ -27,11 +27,35 @@ struct FwdParams {
   int split_len;     // keys per chunk (N_k in forward mode)
 };
 
+// Arguments of the backward launches.  dq, dk, dv are bf16 outputs; the
+// workspace holds l2vec [R] (LSE * log2 e), dvec [R] (rowsum dO * O) and the
+// per-key-block dQ partials ws_dq [n_kb][R][d], R = B*H*N_q.
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* l2vec;
+  float* dvec;
+  float* ws_dq;
+  int B, H, n_q, n_k, d;
+  int causal;
+  float scale;
+};
+
 // Forward: O, LSE.  Returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
 
 // Split-KV pass 1 (partials into the workspace) and pass 2 (merge into O, LSE).
 hipError_t launch_splitkv_partial(const FwdParams& p, hipStream_t stream);
 hipError_t launch_splitkv_merge(const FwdParams& p, hipStream_t stream);
+
+// Backward: D and LSE*log2e, then dK, dV and the dQ partials, then the dQ reduction.
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 
 }  // namespace fa2

@@ -148,6 +148,46 @@ int fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float*
                     int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa2_bwd_workspace_bytes — bytes of caller-owned device workspace fa2_bwd
+ * needs: (2*R + ceil(N_k/128) * R * d) * 4 with R = B*H*N_q.  Returns 0 when
+ * an argument is out of range.
+ */
+size_t fa2_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d);
+
+/*
+ * fa2_bwd — gradients of the attention forward (the synthesis page, section 3
+ * item 1: FA2's backward as five matrix products from the stored LSE; section
+ * 5 item 2: a deterministic variant without atomic adds, in two passes).
+ *
+ * For an upstream gradient dO of O = fa2_fwd(Q, K, V, causal, scale) and that
+ * call's LSE:
+ *   P_ij  = exp(scale q_i . k_j - LSE_i) over visible keys (0 elsewhere)
+ *   D_i   = sum_c dO_ic O_ic
+ *   dV_j  = sum_i P_ij dO_i
+ *   dS_ij = P_ij (dO_i . v_j - D_i)
+ *   dK_j  = scale * sum_i dS_ij q_i
+ *   dQ_i  = scale * sum_j dS_ij k_j
+ * P is rounded to bf16 for dV, dS to bf16 for dK and dQ; products accumulate
+ * in fp32; dQ, dK, dV are written as bf16 (RNE).
+ *
+ * Passes: (1) D and LSE*log2(e) per row; (2) one workgroup per 128-key block
+ * computes dK and dV for its keys and writes its contribution to dQ for every
+ * query row into the workspace; (3) dQ = scale * the sum of the contributions
+ * in key-block order.  No atomics: results are bit-reproducible.
+ *
+ * Q, K, V, O, dO: bf16 [B][H][N][d] as in fa2_fwd; LSE: fp32 [B][H][N_q]
+ * (natural log, as fa2_fwd writes it).  dQ [B][H][N_q][d], dK and dV
+ * [B][H][N_k][d]: bf16 outputs that must not overlap any input, each other
+ * or the workspace.  workspace: device buffer of at least
+ * fa2_bwd_workspace_bytes(B, H, N_q, N_k, d) bytes (its contents on return
+ * are scratch).  causal, scale, stream and the remaining errors as fa2_fwd.
+ */
+int fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+            const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N_q, int N_k,
+            int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+            void* stream);
+
+/*
  * fa2_num_splits — a key-chunk count for fa2_fwd_splitkv that fills the chip
  * (the walkthrough page, "launch grid" section: the first version derives the
  * split count from batch x heads and the multiprocessor count so that

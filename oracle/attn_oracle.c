@@ -379,8 +379,13 @@ int64_t oracle_window_pairs(int n_q, int n_k, int wl, int wr) {
 int oracle_backward_f64(const double* Q, const double* K, const double* V, const double* dO, double* dQ,
                         double* dK, double* dV, int B, int H, int n_q, int n_k, int d, int causal, double scale) {
   if (check_shape(B, H, n_q, n_k, d)) return -1;
-  int failed = 0;
-#pragma omp parallel for schedule(dynamic, 1)
+  double* P = (double*)malloc(sizeof(double) * (size_t)n_q * n_k);
+  double* dS = (double*)malloc(sizeof(double) * (size_t)n_q * n_k);
+  if (!P || !dS) {
+    free(P); free(dS);
+    return -1;
+  }
+  /* heads one after another; the loops over rows inside a head run in parallel */
   for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
     const double* q = Q + bh * (int64_t)n_q * d;
     const double* k = K + bh * (int64_t)n_k * d;
@@ -389,15 +394,7 @@ int oracle_backward_f64(const double* Q, const double* K, const double* V, const
     double* gq = dQ + bh * (int64_t)n_q * d;
     double* gk = dK + bh * (int64_t)n_k * d;
     double* gv = dV + bh * (int64_t)n_k * d;
-    double* P = (double*)malloc(sizeof(double) * (size_t)n_q * n_k);
-    double* dS = (double*)malloc(sizeof(double) * (size_t)n_q * n_k);
-    double* o = (double*)malloc(sizeof(double) * (size_t)d);
-    if (!P || !dS || !o) {
-#pragma omp atomic write
-      failed = 1;
-      free(P); free(dS); free(o);
-      continue;
-    }
+#pragma omp parallel for schedule(dynamic, 8)
     for (int64_t i = 0; i < n_q; ++i) {
       const int64_t n_allowed = allowed_prefix(i, n_k, causal);
       double* prow = P + i * n_k;
@@ -412,12 +409,13 @@ int oracle_backward_f64(const double* Q, const double* K, const double* V, const
       for (int64_t j = 0; j < n_allowed; ++j) l += exp(prow[j] - m);
       const double lse = m + log(l);
       for (int64_t j = 0; j < n_k; ++j) prow[j] = (j < n_allowed) ? exp(prow[j] - lse) : 0.0;
-      /* O_i and D_i */
-      for (int c = 0; c < d; ++c) o[c] = 0.0;
-      for (int64_t j = 0; j < n_allowed; ++j)
-        for (int c = 0; c < d; ++c) o[c] += prow[j] * v[j * d + c];
+      /* D_i = dO_i . O_i with O_i = sum_j P_ij v_j */
       double Di = 0.0;
-      for (int c = 0; c < d; ++c) Di += go[i * d + c] * o[c];
+      for (int c = 0; c < d; ++c) {
+        double oc = 0.0;
+        for (int64_t j = 0; j < n_allowed; ++j) oc += prow[j] * v[j * d + c];
+        Di += go[i * d + c] * oc;
+      }
       /* dS_ij = P_ij (dO_i . v_j - D_i) */
       for (int64_t j = 0; j < n_k; ++j) {
         if (j >= n_allowed) { dS[i * n_k + j] = 0.0; continue; }
@@ -426,12 +424,14 @@ int oracle_backward_f64(const double* Q, const double* K, const double* V, const
         dS[i * n_k + j] = prow[j] * (dp - Di);
       }
     }
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n_q; ++i)
       for (int c = 0; c < d; ++c) {
         double acc = 0.0;
         for (int64_t j = 0; j < n_k; ++j) acc += dS[i * n_k + j] * k[j * d + c];
         gq[i * d + c] = scale * acc;
       }
+#pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < n_k; ++j)
       for (int c = 0; c < d; ++c) {
         double acck = 0.0, accv = 0.0;
@@ -442,9 +442,9 @@ int oracle_backward_f64(const double* Q, const double* K, const double* V, const
         gk[j * d + c] = scale * acck;
         gv[j * d + c] = accv;
       }
-    free(P); free(dS); free(o);
   }
-  return failed ? -1 : 0;
+  free(P); free(dS);
+  return 0;
 }
 
 /* Threads the parallel regions above use (reported beside CPU timings). */

@@ -90,3 +90,36 @@ def sample_rows(B, H, n_q, n, seed, block=128):
     while len(rows) < min(n + 24, B * H * n_q):
         rows.add((int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(n_q))))
     return sorted(rows)
+
+
+def bwd_bounds(q, k, v, o, do, causal, scale):
+    """Element-wise error bounds for bf16 backward outputs against the fp64
+    oracle's gradients, derived from the operand roundings of the GPU path:
+    P and dS are rounded to bf16 (relative error <= 2^-9) before their
+    products, O reaches D_i = sum dO_i O_i as bf16 (relative <= 2^-9), and the
+    outputs are stored as bf16.  With magnitudes
+        MV = P^T |dO|,   MK = scale (|dS|^T + P^T |Dabs|) |Q|,   MQ = scale (|dS| + P |Dabs|) |K|,
+    (Dabs_i = sum_c |dO_ic O_ic|), each bound is 2^-7 M + 2^-8 |ref| + 1e-6, a
+    factor 2 above the first-order sum of those roundings.  Inputs are fp64
+    arrays [B, H, N, d]; returns (bound_dq, bound_dk, bound_dv) and needs the
+    reference gradients only through |ref|, which the caller adds."""
+    p = oracle.probs(q, k, causal, scale)
+    dp = np.matmul(do, np.swapaxes(v, -1, -2))
+    dsum = np.sum(do * o, axis=-1, keepdims=True)
+    ds = np.abs(p * (dp - dsum))
+    dabs = np.sum(np.abs(do * o), axis=-1, keepdims=True)
+    mv = np.matmul(np.swapaxes(p, -1, -2), np.abs(do))
+    mk = scale * np.matmul(np.swapaxes(ds + p * dabs, -1, -2), np.abs(q))
+    mq = scale * np.matmul(ds + p * dabs, np.abs(k))
+    return 2.0 ** -7 * mq, 2.0 ** -7 * mk, 2.0 ** -7 * mv
+
+
+def assert_grads_close(got, ref, bounds, what=""):
+    for name, g, r, b in zip(("dQ", "dK", "dV"), got, ref, bounds):
+        tol = b + 2.0 ** -8 * np.abs(r) + 1e-6
+        err = np.abs(g - r)
+        bad = err > tol
+        if bad.any():
+            idx = np.unravel_index(np.argmax(err - tol), err.shape)
+            raise AssertionError(f"{what} {name}: {int(bad.sum())} elements out of bound; worst at {idx}: "
+                                 f"got {g[idx]:.6g} ref {r[idx]:.6g} err {err[idx]:.3g} tol {tol[idx]:.3g}")

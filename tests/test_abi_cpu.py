@@ -22,8 +22,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa2_fwd", "fa2_fwd_splitkv", "fa2_fwd_window", "fa2_num_splits",
-                                    "fa2_splitkv_workspace_bytes", "fa2_status_string"]
+    assert declared_functions() == ["fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_fwd", "fa2_fwd_splitkv",
+                                    "fa2_fwd_window", "fa2_num_splits", "fa2_splitkv_workspace_bytes",
+                                    "fa2_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -169,3 +170,32 @@ def test_window_validation():
     assert window(nk=0) == BAD_SHAPE
     assert window(scale=float("nan")) == BAD_SCALE
     assert window(o=Q) == ALIAS
+
+
+DO, DQ, DK, DV = (0x20000000000 + i * 64 * GB for i in range(4))
+
+
+def bwd(q=Q, k=K, v=V, o=O, do=DO, l=L, dq=DQ, dk=DK, dv=DV, B=1, H=2, nq=256, nk=200, d=64, causal=0, scale=0.125,
+        ws=W, ws_bytes=None):
+    lib = fa2.load_library()
+    if ws_bytes is None:
+        ws_bytes = lib.fa2_bwd_workspace_bytes(B, H, nq, nk, d)
+    return lib.fa2_bwd(q, k, v, o, do, l, dq, dk, dv, B, H, nq, nk, d, causal, scale, ws, ws_bytes, None)
+
+
+def test_bwd_validation():
+    lib = fa2.load_library()
+    R = 1 * 2 * 256
+    assert lib.fa2_bwd_workspace_bytes(1, 2, 256, 200, 64) == (2 * R + 2 * R * 64) * 4
+    assert lib.fa2_bwd_workspace_bytes(0, 2, 256, 200, 64) == 0
+    for name in ("q", "k", "v", "o", "do", "l", "dq", "dk", "dv"):
+        assert bwd(**{name: None}) == NULLPTR, name
+    assert bwd(d=96) == HEAD_DIM
+    assert bwd(nk=0) == BAD_SHAPE
+    assert bwd(scale=float("inf")) == BAD_SCALE
+    assert bwd(ws=None) == WORKSPACE
+    assert bwd(ws_bytes=16) == WORKSPACE
+    assert bwd(dq=Q) == ALIAS
+    assert bwd(dk=DO + 10) == ALIAS
+    assert bwd(dv=DQ) == ALIAS
+    assert bwd(ws=DK) == ALIAS

@@ -34,8 +34,7 @@ MUTANTS = [
     ("bwd_dq_scale_dropped", "gq[i * d + c] = scale * acc;", "gq[i * d + c] = acc;"),
     ("bwd_dk_from_p", "acck += dS[i * n_k + j] * q[i * d + c];", "acck += P[i * n_k + j] * q[i * d + c];"),
     ("bwd_dv_from_ds", "accv += P[i * n_k + j] * go[i * d + c];", "accv += dS[i * n_k + j] * go[i * d + c];"),
-    ("bwd_D_from_v", "for (int c = 0; c < d; ++c) Di += go[i * d + c] * o[c];",
-     "for (int c = 0; c < d; ++c) Di += go[i * d + c] * v[c];"),
+    ("bwd_D_from_v", "Di += go[i * d + c] * oc;", "Di += go[i * d + c] * v[c];"),
     ("bwd_causal_ignored", "const int64_t n_allowed = allowed_prefix(i, n_k, causal);\n      double* prow = P + i * n_k;",
      "const int64_t n_allowed = allowed_prefix(i, n_k, 0);\n      double* prow = P + i * n_k;"),
     ("first_key_skipped", "for (int64_t j = j0; j < j1; ++j) {\n    double p = exp", "for (int64_t j = j0 + 1; j < j1; ++j) {\n    double p = exp"),
