@@ -291,25 +291,27 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
       }
     // every wave's dS^T is in LDS
     __syncthreads();
-    // dQ contribution of this key block: rows 32(rb0 + r) .. +31, d columns 32cb .. +31
+    // dQ contribution of this key block, computed transposed (dQ^T = K^T dS^T)
+    // so that each lane holds one query row and 4 consecutive d per register
+    // group: rows 32(rb0 + r) + lane%32, d columns 32cb + 8g + 4hf + 0..3
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
-      f32x16 dq = f32x16{};
+      f32x16 dqt = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < kBK / 16; ++ks) {
-        const bf16x8 a = tr_pair(da[r][0] + ks * 16 * kBQ * 2, da[r][1] + ks * 16 * kBQ * 2);
-        const bf16x8 b = tr_pair(kba[0] + ks * 16 * ROW, kba[1] + ks * 16 * ROW);
-        dq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, dq, 0, 0, 0);
+        const bf16x8 dsT = tr_pair(da[r][0] + ks * 16 * kBQ * 2, da[r][1] + ks * 16 * kBQ * 2);
+        const bf16x8 kT = tr_pair(kba[0] + ks * 16 * ROW, kba[1] + ks * 16 * ROW);
+        dqt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kT, dsT, dqt, 0, 0, 0);
       }
       const long long R = (long long)p.B * p.H * p.n_q;
-      float* ws = p.ws_dq + ((long long)kb * R + hq) * D + 32 * cb + col;
+      const int row = i0 + 32 * (rb0 + r) + col;
+      if (row < p.n_q) {
+        float* ws = p.ws_dq + ((long long)kb * R + hq + row) * D + 32 * cb + 4 * hf;
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = i0 + 32 * (rb0 + r) + 8 * g + 4 * hf + e;
-          if (row < p.n_q) ws[(long long)row * D] = dq[4 * g + e];
-        }
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(ws + 8 * g) =
+              f32x4{dqt[4 * g], dqt[4 * g + 1], dqt[4 * g + 2], dqt[4 * g + 3]};
+      }
     }
   };
 
