@@ -56,6 +56,16 @@ def _load():
     lib.oracle_window_pairs.restype = ctypes.c_int64
     lib.oracle_backward_f64.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _i, _i, _i, _i, _i, _i,
                                         ctypes.c_double]
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_decode.restype = ctypes.c_double
+    lib.oracle_quantize_fp8.argtypes = [_u16p, ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_float),
+                                        _i, _i, _i, _i]
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    _u8p = ctypes.POINTER(ctypes.c_uint8)
+    _fp = ctypes.POINTER(ctypes.c_float)
+    lib.oracle_attention_fp8_rows.argtypes = [_u8p, _u8p, _u8p, _fp, _fp, _fp, _i64p, ctypes.c_int64, _dp, _dp,
+                                              _i, _i, _i, _i, _i, _i, ctypes.c_double]
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -219,3 +229,59 @@ def backward(q, k, v, do, causal: bool, scale: float):
                                      float(scale))
     _check(rc, "backward")
     return dq, dk, dv
+
+
+def e4m3_decode_table() -> np.ndarray:
+    """fp64 value of every e4m3fn code 0..255.  Codes 0x7f and 0xff are NaN in the format; the table
+    holds their bit pattern's arithmetic value, which no quantised code ever takes."""
+    lib = _load()
+    return np.array([lib.oracle_e4m3_decode(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3_encode(y: float) -> int:
+    """Round-to-nearest-even e4m3fn code of the fp32 value y (|y| <= 448)."""
+    return int(_load().oracle_e4m3_encode(float(np.float32(y))))
+
+
+def quantize_fp8(x_bits):
+    """Per-(batch, head) e4m3 quantisation of bf16 X (uint16 bit array [B, H, N, d]):
+    returns (codes uint8 [B, H, N, d], descale fp32 [B, H])."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    B, H, n, d = x_bits.shape
+    codes = np.empty((B, H, n, d), dtype=np.uint8)
+    descale = np.empty((B, H), dtype=np.float32)
+    rc = _load().oracle_quantize_fp8(_ptr(x_bits, _u16p), codes.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                     descale.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), B, H, n, d)
+    _check(rc, "quantize_fp8")
+    return codes, descale
+
+
+def dequantize_fp8(codes, descale):
+    """decode(code) * descale of each (batch, head) slice, in fp64."""
+    table = e4m3_decode_table()
+    return table[np.asarray(codes)] * np.asarray(descale, dtype=np.float64)[..., None, None]
+
+
+def attention_fp8(qc, kc, vc, dq, dk, dv, causal: bool, scale: float):
+    """Exact attention (fp64) of the dequantised FP8 inputs; codes [B, H, N, d] with V in row layout,
+    descales [B, H].  Returns (O, LSE)."""
+    return attention(dequantize_fp8(qc, dq), dequantize_fp8(kc, dk), dequantize_fp8(vc, dv), causal, scale)
+
+
+def attention_fp8_rows(qc, kc, vc, dq, dk, dv, rows, causal: bool, scale: float):
+    """attention_fp8 for the flattened rows (b*H + h)*N_q + i listed in `rows`: (O [n, d], LSE [n])."""
+    u8 = ctypes.POINTER(ctypes.c_uint8)
+    fp = ctypes.POINTER(ctypes.c_float)
+    qc, kc, vc = (np.ascontiguousarray(a, dtype=np.uint8) for a in (qc, kc, vc))
+    dq, dk, dv = (np.ascontiguousarray(a, dtype=np.float32) for a in (dq, dk, dv))
+    B, H, n_q, d = qc.shape
+    n_k = kc.shape[2]
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    O = np.empty((len(rows), d), dtype=np.float64)
+    L = np.empty(len(rows), dtype=np.float64)
+    rc = _load().oracle_attention_fp8_rows(qc.ctypes.data_as(u8), kc.ctypes.data_as(u8), vc.ctypes.data_as(u8),
+                                           dq.ctypes.data_as(fp), dk.ctypes.data_as(fp), dv.ctypes.data_as(fp),
+                                           _ptr(rows, _i64p), len(rows), _ptr(O, _dp), _ptr(L, _dp),
+                                           B, H, n_q, n_k, d, int(causal), float(scale))
+    _check(rc, "attention_fp8_rows")
+    return O, L

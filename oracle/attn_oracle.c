@@ -447,6 +447,125 @@ int oracle_backward_f64(const double* Q, const double* K, const double* V, const
   return 0;
 }
 
+/*
+ * FP8 (e4m3) inputs.  The improvements page (section 三 on FlashAttention-3,
+ * and section 四, point ③) says FP8 doubles matrix throughput and that the
+ * precision it loses must be controlled by scaling; it gives no recipe, so
+ * this is the plainest one.  The format is OCP e4m3fn: sign, 4 exponent bits
+ * (bias 7), 3 mantissa bits, subnormals, largest finite 448, no infinities
+ * (codes 0x7f and 0xff are NaN and are never produced here).
+ *
+ * Scaling is per (batch, head) tensor slice: amax = max |x| over the slice,
+ * inv = fp32(448 / amax) and descale = fp32(amax / 448) (both 1 when
+ * amax = 0).  The code of x is e4m3 round-to-nearest-even of the fp32
+ * product fp32(x) * inv; its value is decode(code) * descale.
+ *
+ * Attention on FP8 inputs is exact attention (the definition at the top of
+ * this file) applied to the dequantised values q = decode(Qc) * descale_q,
+ * k = decode(Kc) * descale_k, v = decode(Vc) * descale_v, in fp64.
+ */
+static uint8_t e4m3_rne(float y) {
+  /* round-to-nearest-even onto the e4m3fn grid, |y| <= 448 assumed */
+  const uint8_t sign = (y < 0.f || (y == 0.f && signbit(y))) ? 0x80 : 0;
+  double a = fabs((double)y);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);              /* a = f * 2^e, f in [0.5, 1) */
+  int E = e - 1;             /* a in [2^E, 2^(E+1)) */
+  if (E < -6) E = -6;        /* subnormal range shares the spacing of E = -6 */
+  const double ulp = ldexp(1.0, E - 3);
+  double q = a / ulp;        /* exact: a and ulp are binary */
+  double fl = floor(q);
+  double r = q - fl;
+  if (r > 0.5 || (r == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+  double v = fl * ulp;       /* rounded magnitude */
+  if (v > 448.0) v = 448.0;  /* not reached for |y| <= 448 */
+  /* encode v */
+  if (v < ldexp(1.0, -6)) return sign | (uint8_t)(int)(v / ldexp(1.0, -9)); /* subnormal: m * 2^-9 */
+  int ev;
+  double fv = frexp(v, &ev); /* v = fv * 2^ev, fv in [0.5, 1) */
+  const int expo = ev - 1 + 7;
+  const int mant = (int)((fv * 2.0 - 1.0) * 8.0 + 0.5);
+  return sign | (uint8_t)(expo << 3) | (uint8_t)mant;
+}
+
+uint8_t oracle_e4m3_encode(float y) { return e4m3_rne(y); }
+
+double oracle_e4m3_decode(uint8_t c) {
+  const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  const double v = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Per-head quantisation of bf16 X [B][H][N][d] into codes [B][H][N][d] and
+ * descale [B][H].  Returns 0. */
+int oracle_quantize_fp8(const uint16_t* X, uint8_t* codes, float* descale, int B, int H, int n, int d) {
+  for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+    const uint16_t* x = X + bh * (int64_t)n * d;
+    float amax = 0.f;
+    for (int64_t i = 0; i < (int64_t)n * d; ++i) {
+      const float a = fabsf((float)bf16_bits_to_double(x[i]));
+      if (a > amax) amax = a;
+    }
+    const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
+    descale[bh] = amax > 0.f ? amax / 448.0f : 1.0f;
+    for (int64_t i = 0; i < (int64_t)n * d; ++i) {
+      const float y = (float)bf16_bits_to_double(x[i]) * inv;
+      codes[bh * (int64_t)n * d + i] = e4m3_rne(y);
+    }
+  }
+  return 0;
+}
+
+/*
+ * Attention on FP8 inputs for a chosen set of rows.  Qc, Kc, Vc hold e4m3
+ * codes of the whole [B][H][N][d] tensors (V in the same row layout as K);
+ * descale_* are [B][H]; rows[r] = (b*H + h)*N_q + i; the visible keys of row i
+ * are j < N_k and, if causal, j <= i.  O_rows [n_rows][d], LSE_rows [n_rows].
+ * Returns 0, or -1 on a bad shape / row index.
+ */
+int oracle_attention_fp8_rows(const uint8_t* Qc, const uint8_t* Kc, const uint8_t* Vc, const float* descale_q,
+                              const float* descale_k, const float* descale_v, const int64_t* rows, int64_t n_rows,
+                              double* O_rows, double* LSE_rows, int B, int H, int n_q, int n_k, int d, int causal,
+                              double scale) {
+  if (check_shape(B, H, n_q, n_k, d)) return -1;
+  for (int64_t r = 0; r < n_rows; ++r)
+    if (rows[r] < 0 || rows[r] >= (int64_t)B * H * n_q) return -1;
+  double table[256];
+  for (int c = 0; c < 256; ++c) table[c] = oracle_e4m3_decode((uint8_t)c);
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)n_k);
+    double* q = (double*)malloc(sizeof(double) * (size_t)d);
+    double* Kh = (double*)malloc(sizeof(double) * (size_t)n_k * d);
+    double* Vh = (double*)malloc(sizeof(double) * (size_t)n_k * d);
+    int64_t cached_bh = -1;
+    if (!s || !q || !Kh || !Vh) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      if (failed) continue;
+      const int64_t bh = rows[r] / n_q, i = rows[r] % n_q;
+      if (bh != cached_bh) {
+        const uint8_t* kc = Kc + bh * (int64_t)n_k * d;
+        const uint8_t* vc = Vc + bh * (int64_t)n_k * d;
+        for (int64_t e = 0; e < (int64_t)n_k * d; ++e) {
+          Kh[e] = table[kc[e]] * (double)descale_k[bh];
+          Vh[e] = table[vc[e]] * (double)descale_v[bh];
+        }
+        cached_bh = bh;
+      }
+      for (int c = 0; c < d; ++c) q[c] = table[Qc[rows[r] * d + c]] * (double)descale_q[bh];
+      attend_row(q, Kh, Vh, allowed_prefix(i, n_k, causal), d, scale, s, O_rows + r * d, LSE_rows + r);
+    }
+    free(s); free(q); free(Kh); free(Vh);
+  }
+  return failed ? -1 : 0;
+}
+
 /* Threads the parallel regions above use (reported beside CPU timings). */
 #ifdef _OPENMP
 #include <omp.h>

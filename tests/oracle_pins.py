@@ -41,6 +41,24 @@ Backward pins (gradients of exact attention for an upstream gradient dO):
 The definition pinned is exact attention with top-left causal masking
 (key j allowed for query i iff j <= i), scale applied to q.k before the
 softmax, and LSE the natural log of sum exp of the scaled, masked scores.
+
+FP8 pins (OCP e4m3fn codes with per-(batch, head) scaling; the improvements
+page, section 四 point ③, asks for scaling without giving a recipe):
+
+  P18 the decode table against torch's float8_e4m3fn and the format's
+      published landmarks (1.0, largest finite 448, smallest normal 2^-6,
+      smallest subnormal 2^-9), monotone over the positive codes;
+  P19 the round-to-nearest-even encoder: every finite code round-trips,
+      midpoints go to the even code and one fp32 step either side to the
+      nearer code, and random values agree with torch's cast;
+  P20 the quantiser: the slice's amax maps to +-448, every dequantised value
+      lies within half a code step of its input, an all-zero slice gets
+      descale 1, and the codes equal torch's cast of fp32(x) * fp32(448/amax);
+  P21 attention on FP8 inputs: with power-of-two descales the dequantised
+      values are bf16 numbers, and the result equals the pinned bf16 row
+      oracle on them; the row function equals the full composition for
+      arbitrary descales; O scales with descale_v and the scores with
+      descale_q * descale_k.
 """
 import math
 
@@ -500,8 +518,116 @@ def pin_p17_backward_identities(orc):
         assert all(np.all(g == 0) for g in z)
 
 
+
+def _torch_e4m3(values_f32):
+    return torch.from_numpy(np.asarray(values_f32, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_p18_e4m3_decode(orc):
+    t = orc.e4m3_decode_table()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    finite = np.isfinite(ref)
+    assert list(np.where(~finite)[0]) == [0x7F, 0xFF]
+    assert np.array_equal(t[finite], ref[finite])
+    assert t[0x38] == 1.0 and t[0x7E] == 448.0 and t[0x08] == 2.0 ** -6 and t[0x01] == 2.0 ** -9
+    assert t[0x07] == 7 * 2.0 ** -9 and t[0xB8] == -1.0 and t[0x00] == 0.0
+    assert np.all(np.diff(t[:0x7F]) > 0)
+    assert np.array_equal(t[0x80:0xFF], -t[0x00:0x7F])
+
+
+def pin_p19_e4m3_encode(orc):
+    t = orc.e4m3_decode_table()
+    for c in list(range(0x7F)) + list(range(0x80, 0xFF)):
+        if c == 0x80:
+            continue  # -0 encodes to 0x80 as well; checked below
+        assert orc.e4m3_encode(t[c]) == c, hex(c)
+    assert orc.e4m3_encode(-0.0) == 0x80 and orc.e4m3_encode(0.0) == 0x00
+    for c in range(0x7E):
+        lo, hi = t[c], t[c + 1]
+        mid = np.float32((lo + hi) / 2)  # exact: codes have 4 significant bits
+        even = c if c % 2 == 0 else c + 1
+        assert orc.e4m3_encode(mid) == even, hex(c)
+        assert orc.e4m3_encode(np.nextafter(mid, np.float32(np.inf))) == c + 1
+        assert orc.e4m3_encode(np.nextafter(mid, np.float32(0))) == c
+        assert orc.e4m3_encode(-mid) == 0x80 | even
+    assert orc.e4m3_encode(np.float32(448.0) * np.float32(1 + 2.0 ** -20)) == 0x7E
+    rng = RNG(1919)
+    vals = (rng.standard_normal(4000) * 2.0 ** rng.integers(-12, 8, 4000)).astype(np.float32)
+    vals = vals[np.abs(vals) <= 448]
+    got = np.array([orc.e4m3_encode(v) for v in vals], dtype=np.uint8)
+    assert np.array_equal(got, _torch_e4m3(vals))
+
+
+def pin_p20_quantize(orc):
+    rng = RNG(2020)
+    t = orc.e4m3_decode_table()
+    x = torch.from_numpy(rng.standard_normal((2, 3, 37, 16)) * np.array([0.5, 3.0, 40.0])[None, :, None, None])
+    x[1, 2] = 0.0
+    xb = x.to(torch.bfloat16)
+    bits = xb.view(torch.int16).numpy().view(np.uint16)
+    codes, ds = orc.quantize_fp8(bits)
+    xf = xb.to(torch.float32).numpy()
+    amax = np.abs(xf).max(axis=(2, 3))
+    assert ds[1, 2] == 1.0 and np.all(codes[1, 2] == 0)
+    for b in range(2):
+        for h in range(3):
+            if amax[b, h] == 0:
+                continue
+            assert ds[b, h] == np.float32(amax[b, h] / np.float32(448.0))
+            at = np.abs(xf[b, h]) == amax[b, h]
+            assert np.all(np.isin(codes[b, h][at], [0x7E, 0xFE]))
+            inv = np.float32(448.0) / np.float32(amax[b, h])
+            y = xf[b, h] * inv
+            assert np.array_equal(codes[b, h], _torch_e4m3(y))
+            xh = t[codes[b, h]] * np.float64(ds[b, h])
+            err = np.abs(xh - xf[b, h].astype(np.float64))
+            step = np.maximum(2.0 ** -4 * np.abs(xf[b, h]), 2.0 ** -10 * np.float64(ds[b, h]) * 1.01)
+            assert np.all(err <= step * (1 + 2.0 ** -18)), float(np.max(err / step))
+    assert not np.any((codes & 0x7F) == 0x7F)
+
+
+def pin_p21_fp8_attention(orc):
+    rng = RNG(2121)
+    B, H, n_q, n_k, d = 2, 2, 23, 31, 16
+
+    def codes(n):
+        c = rng.integers(0x20, 0x7E, (B, H, n, d)).astype(np.uint8)
+        return c | (rng.integers(0, 2, c.shape).astype(np.uint8) << 7)
+
+    qc, kc, vc = codes(n_q), codes(n_k), codes(n_k)
+    rows = np.arange(B * H * n_q)
+    # power-of-two descales: the dequantised values are bf16 numbers
+    dq = np.float32(2.0 ** rng.integers(-9, -5, (B, H)))
+    dk = np.float32(2.0 ** rng.integers(-9, -5, (B, H)))
+    dv = np.float32(2.0 ** rng.integers(-8, -2, (B, H)))
+    for causal in (False, True):
+        o8, l8 = orc.attention_fp8_rows(qc, kc, vc, dq, dk, dv, rows, causal, 0.3)
+        deq = [orc.dequantize_fp8(c, s) for c, s in ((qc, dq), (kc, dk), (vc, dv))]
+        bits = []
+        for a in deq:
+            tb = torch.from_numpy(a).to(torch.bfloat16)
+            assert np.array_equal(tb.to(torch.float64).numpy(), a)
+            bits.append(tb.view(torch.int16).numpy().view(np.uint16))
+        o16, l16 = orc.attention_rows_bf16(bits[0], bits[1], bits[2], rows, causal, 0.3)
+        assert np.max(np.abs(o8 - o16)) <= 1e-13 and np.max(np.abs(l8 - l16)) <= 1e-13
+    # arbitrary descales: the row function against the composition
+    dq, dk, dv = (np.float32(rng.uniform(0.001, 0.02, (B, H))) for _ in range(3))
+    for causal in (False, True):
+        O, L = orc.attention_fp8(qc, kc, vc, dq, dk, dv, causal, 0.7)
+        sel = rng.choice(B * H * n_q, 20, replace=False)
+        o8, l8 = orc.attention_fp8_rows(qc, kc, vc, dq, dk, dv, sel, causal, 0.7)
+        assert np.max(np.abs(O.reshape(-1, d)[sel] - o8)) <= 1e-12
+        assert np.max(np.abs(L.reshape(-1)[sel] - l8)) <= 1e-12
+        # O is linear in descale_v; descale_q * descale_k only scales the scores
+        o2, l2 = orc.attention_fp8_rows(qc, kc, vc, dq, dk, 2 * dv, sel, causal, 0.7)
+        assert np.max(np.abs(o2 - 2 * o8)) <= 1e-12 and np.max(np.abs(l2 - l8)) <= 1e-12
+        o3, l3 = orc.attention_fp8_rows(qc, kc, vc, 2 * dq, dk, dv, sel, causal, 0.35)
+        assert np.max(np.abs(o3 - o8)) <= 1e-12 and np.max(np.abs(l3 - l8)) <= 1e-12
+
+
 ALL_PINS = [pin_p1_bruteforce, pin_p2_rows_sum_to_one, pin_p3_constant_v, pin_p4_causal_row0,
             pin_p5_uniform_scores, pin_p6_one_hot, pin_p7_lse_identity, pin_p8_torch_sdpa,
             pin_p9_invariants, pin_p10_recurrence, pin_p11_window_bruteforce, pin_p12_window_special,
             pin_p13_window_torch, pin_p14_window_recurrence, pin_p15_backward_finite_differences,
-            pin_p16_backward_torch, pin_p17_backward_identities]
+            pin_p16_backward_torch, pin_p17_backward_identities, pin_p18_e4m3_decode, pin_p19_e4m3_encode,
+            pin_p20_quantize, pin_p21_fp8_attention]

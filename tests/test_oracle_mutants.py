@@ -37,6 +37,17 @@ MUTANTS = [
     ("bwd_D_from_v", "Di += go[i * d + c] * oc;", "Di += go[i * d + c] * v[c];"),
     ("bwd_causal_ignored", "const int64_t n_allowed = allowed_prefix(i, n_k, causal);\n      double* prow = P + i * n_k;",
      "const int64_t n_allowed = allowed_prefix(i, n_k, 0);\n      double* prow = P + i * n_k;"),
+    ("e4m3_bias_8", "ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    ("e4m3_subnormal_scale", "ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    ("e4m3_ties_away", "if (r > 0.5 || (r == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;", "if (r >= 0.5) fl += 1.0;"),
+    ("e4m3_truncate", "if (r > 0.5 || (r == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;", ""),
+    ("quant_range_240", "const float inv = amax > 0.f ? 448.0f / amax : 1.0f;",
+     "const float inv = amax > 0.f ? 240.0f / amax : 1.0f;"),
+    ("quant_descale_inverted", "descale[bh] = amax > 0.f ? amax / 448.0f : 1.0f;",
+     "descale[bh] = amax > 0.f ? 448.0f / amax : 1.0f;"),
+    ("fp8_v_descale_from_k", "Vh[e] = table[vc[e]] * (double)descale_v[bh];", "Vh[e] = table[vc[e]] * (double)descale_k[bh];"),
+    ("fp8_q_descale_head0", "q[c] = table[Qc[rows[r] * d + c]] * (double)descale_q[bh];",
+     "q[c] = table[Qc[rows[r] * d + c]] * (double)descale_q[0];"),
     ("first_key_skipped", "for (int64_t j = j0; j < j1; ++j) {\n    double p = exp", "for (int64_t j = j0 + 1; j < j1; ++j) {\n    double p = exp"),
 ]
 
