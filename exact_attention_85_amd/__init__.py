@@ -12,11 +12,14 @@ from ._binding import (  # noqa: F401
     backward,
     bwd_workspace_bytes,
     forward,
+    forward_fp8,
     forward_splitkv,
     forward_window,
+    fp8_vt_stride,
     lib_path,
     load_library,
     num_splits,
+    quantize_fp8,
     splitkv_workspace_bytes,
     status_string,
 )

@@ -53,6 +53,12 @@ def load_library():
     lib.fa2_bwd.restype = i
     lib.fa2_num_splits.argtypes = [i, i, i, i, i, i]
     lib.fa2_num_splits.restype = i
+    lib.fa2_fp8_vt_stride.argtypes = [i]
+    lib.fa2_fp8_vt_stride.restype = i
+    lib.fa2_quantize_fp8.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
+    lib.fa2_quantize_fp8.restype = i
+    lib.fa2_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa2_fwd_fp8.restype = i
     lib.fa2_status_string.argtypes = [i]
     lib.fa2_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -204,3 +210,63 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale=None, workspace=No
                      _stream_handle(q.device))
     _check(rc)
     return dq, dk, dv
+
+
+def fp8_vt_stride(n_k: int) -> int:
+    """Row stride (keys) of a transposed V code tensor: n_k rounded up to a multiple of 16."""
+    rc = int(load_library().fa2_fp8_vt_stride(int(n_k)))
+    if rc < 0:
+        _check(rc)
+    return rc
+
+
+def quantize_fp8(x, transposed: bool = False):
+    """Per-(batch, head) e4m3 quantisation of bf16 x [B, H, N, d] via fa2_quantize_fp8.
+
+    Returns (codes, descale): codes uint8 [B, H, N, d], or [B, H, d, fp8_vt_stride(N)] when
+    transposed (the V layout fa2_fwd_fp8 takes); descale fp32 [B, H] = amax / 448."""
+    lib = load_library()
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.bfloat16 or x.device.type != "cuda":
+        raise TypeError("x must be a bfloat16 tensor on the GPU")
+    if x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, H, N, d] tensor")
+    B, H, n, d = x.shape
+    if transposed:
+        codes = torch.empty((B, H, d, fp8_vt_stride(n)), dtype=torch.uint8, device=x.device)
+    else:
+        codes = torch.empty((B, H, n, d), dtype=torch.uint8, device=x.device)
+    descale = torch.empty((B, H), dtype=torch.float32, device=x.device)
+    rc = lib.fa2_quantize_fp8(x.data_ptr(), codes.data_ptr(), descale.data_ptr(), B, H, n, d,
+                              int(bool(transposed)), _stream_handle(x.device))
+    _check(rc)
+    return codes, descale
+
+
+def forward_fp8(qc, kc, vt, descale_q, descale_k, descale_v, causal: bool = False, scale=None, out=None,
+                lse=None):
+    """Attention forward on e4m3 codes via fa2_fwd_fp8.
+
+    qc [B, H, N_q, d], kc [B, H, N_k, d] uint8 codes; vt [B, H, d, fp8_vt_stride(N_k)] codes of V
+    transposed; descales fp32 [B, H].  Returns (o bf16 [B, H, N_q, d], lse fp32 [B, H, N_q])."""
+    lib = load_library()
+    for name, t in (("qc", qc), ("kc", kc), ("vt", vt)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or t.device.type != "cuda":
+            raise TypeError(f"{name} must be a uint8 tensor on the GPU")
+        if t.dim() != 4 or not t.is_contiguous() or t.device != qc.device:
+            raise ValueError(f"{name} must be a contiguous 4-d tensor on qc's device")
+    B, H, n_q, d = qc.shape
+    n_k = kc.shape[2]
+    if tuple(kc.shape) != (B, H, n_k, d) or tuple(vt.shape) != (B, H, d, fp8_vt_stride(n_k)):
+        raise ValueError("kc must be [B, H, N_k, d] and vt [B, H, d, fp8_vt_stride(N_k)]")
+    for name, t in (("descale_q", descale_q), ("descale_k", descale_k), ("descale_v", descale_v)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, H) or not t.is_contiguous() or t.device != qc.device:
+            raise ValueError(f"{name} must be a contiguous fp32 [B, H] tensor on qc's device")
+    if out is None:
+        out = torch.empty((B, H, n_q, d), dtype=torch.bfloat16, device=qc.device)
+    if lse is None:
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=qc.device)
+    rc = lib.fa2_fwd_fp8(qc.data_ptr(), kc.data_ptr(), vt.data_ptr(), descale_q.data_ptr(), descale_k.data_ptr(),
+                         descale_v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, n_q, n_k, d,
+                         int(bool(causal)), _scale(scale, d), _stream_handle(qc.device))
+    _check(rc)
+    return out, lse

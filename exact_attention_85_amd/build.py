@@ -7,7 +7,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa2.so")
-SOURCES = [os.path.join(CSRC, "fa2_fwd.hip"), os.path.join(CSRC, "fa2_bwd.hip"), os.path.join(CSRC, "fa2_api.cpp")]
+SOURCES = [os.path.join(CSRC, n) for n in ("fa2_fwd.hip", "fa2_bwd.hip", "fa2_fp8.hip", "fa2_api.cpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -52,6 +52,8 @@ int check_alias(const void* Q, const void* K, const void* V, const void* O, cons
   return FA2_OK;
 }
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 fa2::FwdParams make_params(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q,
                            int N_k, int d, int causal, float scale) {
   fa2::FwdParams p{};
@@ -222,6 +224,78 @@ int fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const vo
   return FA2_OK;
 }
 
+int fa2_fp8_vt_stride(int N_k) {
+  if (N_k < 1 || N_k > (1 << 30)) return FA2_ERR_BAD_SHAPE;
+  return (N_k + 15) / 16 * 16;
+}
+
+int fa2_quantize_fp8(const void* X, void* codes, float* descale, int B, int H, int N, int d, int transposed,
+                     void* stream) {
+  if (!X || !codes || !descale) return FA2_ERR_NULLPTR;
+  if (B < 1 || H < 1 || N < 1) return FA2_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return FA2_ERR_HEAD_DIM;
+  if ((long long)N * d > kMaxHeadElems || (long long)B * H > 65535) return FA2_ERR_BAD_SHAPE;
+  if (!aligned16(X) || !aligned16(codes) || !aligned16(descale)) return FA2_ERR_ALIGN;
+  const long long bh = (long long)B * H;
+  const int stride = fa2_fp8_vt_stride(N);
+  const long long code_bytes = transposed ? bh * d * stride : bh * N * d;
+  const Range x = range_of(X, bh * N * d * 2), c = range_of(codes, code_bytes), s = range_of(descale, bh * 4);
+  if (overlap(c, x) || overlap(s, x) || overlap(s, c)) return FA2_ERR_ALIAS;
+  fa2::QuantParams p{};
+  p.x = static_cast<const uint16_t*>(X);
+  p.codes = static_cast<uint8_t*>(codes);
+  p.descale = descale;
+  p.B = B;
+  p.H = H;
+  p.n = N;
+  p.d = d;
+  p.transposed = transposed ? 1 : 0;
+  p.vt_stride = stride;
+  if (fa2::launch_quantize_fp8(p, static_cast<hipStream_t>(stream)) != hipSuccess) return FA2_ERR_HIP;
+  return FA2_OK;
+}
+
+int fa2_fwd_fp8(const void* Qc, const void* Kc, const void* Vt, const float* descale_q, const float* descale_k,
+                const float* descale_v, void* O, float* LSE, int B, int H, int N_q, int N_k, int d, int causal,
+                float scale, void* stream) {
+  if (!descale_q || !descale_k || !descale_v) return FA2_ERR_NULLPTR;
+  int rc = check_common(Qc, Kc, Vt, O, LSE, B, H, N_q, N_k, d, scale);
+  if (rc != FA2_OK) return rc;
+  const int br = 128;
+  if ((long long)((N_q + br - 1) / br) * B * H > kMaxGrid) return FA2_ERR_BAD_SHAPE;
+  const void* ptrs[8] = {Qc, Kc, Vt, descale_q, descale_k, descale_v, O, LSE};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return FA2_ERR_ALIGN;
+  const long long bh = (long long)B * H;
+  const int stride = fa2_fp8_vt_stride(N_k);
+  const Range in[6] = {range_of(Qc, bh * N_q * d), range_of(Kc, bh * N_k * d), range_of(Vt, bh * d * stride),
+                       range_of(descale_q, bh * 4), range_of(descale_k, bh * 4), range_of(descale_v, bh * 4)};
+  const Range o = range_of(O, bh * N_q * d * 2), l = range_of(LSE, bh * N_q * 4);
+  if (overlap(o, l)) return FA2_ERR_ALIAS;
+  for (const Range& r : in)
+    if (overlap(o, r) || overlap(l, r)) return FA2_ERR_ALIAS;
+  fa2::Fp8Params p{};
+  p.q = static_cast<const uint8_t*>(Qc);
+  p.k = static_cast<const uint8_t*>(Kc);
+  p.vt = static_cast<const uint8_t*>(Vt);
+  p.dsq = descale_q;
+  p.dsk = descale_k;
+  p.dsv = descale_v;
+  p.o = static_cast<uint16_t*>(O);
+  p.lse = LSE;
+  p.B = B;
+  p.H = H;
+  p.n_q = N_q;
+  p.n_k = N_k;
+  p.d = d;
+  p.vt_stride = stride;
+  p.wl = -1;
+  p.wr = causal ? 0 : -1;
+  p.scale = scale;
+  if (fa2::launch_fwd_fp8(p, static_cast<hipStream_t>(stream)) != hipSuccess) return FA2_ERR_HIP;
+  return FA2_OK;
+}
+
 const char* fa2_status_string(int status) {
   switch (status) {
     case FA2_OK: return "FA2_OK: success";
@@ -234,6 +308,7 @@ const char* fa2_status_string(int status) {
     case FA2_ERR_SPLITS: return "FA2_ERR_SPLITS: num_splits must be in [1, min(N_k, FA2_MAX_SPLITS)]";
     case FA2_ERR_HIP: return "FA2_ERR_HIP: the HIP runtime rejected a kernel launch";
     case FA2_ERR_WINDOW: return "FA2_ERR_WINDOW: window sizes must be -1 (unbounded) or in [0, 2^30]";
+    case FA2_ERR_ALIGN: return "FA2_ERR_ALIGN: FP8 entry points need 16-byte aligned tensor pointers";
     default: return "unknown fa2 status";
   }
 }

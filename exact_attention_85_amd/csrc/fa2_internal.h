@@ -48,6 +48,32 @@ struct BwdParams {
   float scale;
 };
 
+// Arguments of the FP8 forward: e4m3 codes of Q, K (row layout) and V
+// (transposed, row stride vt_stride), per-(batch, head) descales.
+struct Fp8Params {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* vt;
+  const float* dsq;
+  const float* dsk;
+  const float* dsv;
+  uint16_t* o;
+  float* lse;
+  int B, H, n_q, n_k, d, vt_stride;
+  int wl, wr;
+  float scale;
+};
+
+// Arguments of the quantiser; descale holds the amax bit patterns between its kernels.
+struct QuantParams {
+  const uint16_t* x;
+  uint8_t* codes;
+  float* descale;
+  int B, H, n, d;
+  int transposed;
+  int vt_stride;
+};
+
 // Forward: O, LSE.  Returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
 
@@ -57,5 +83,9 @@ hipError_t launch_splitkv_merge(const FwdParams& p, hipStream_t stream);
 
 // Backward: D and LSE*log2e, then dK, dV and the dQ partials, then the dQ reduction.
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+
+// FP8 forward and the quantiser that prepares its inputs.
+hipError_t launch_fwd_fp8(const Fp8Params& p, hipStream_t stream);
+hipError_t launch_quantize_fp8(const QuantParams& p, hipStream_t stream);
 
 }  // namespace fa2

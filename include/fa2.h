@@ -52,7 +52,8 @@ typedef enum fa2_status {
   FA2_ERR_ALIAS = -6,     /* an output overlaps an input, another output or the workspace */
   FA2_ERR_SPLITS = -7,    /* num_splits outside [1, min(N_k, FA2_MAX_SPLITS)] */
   FA2_ERR_HIP = -8,       /* the HIP runtime rejected a kernel launch */
-  FA2_ERR_WINDOW = -9     /* a window size below -1 or above 2^30 */
+  FA2_ERR_WINDOW = -9,    /* a window size below -1 or above 2^30 */
+  FA2_ERR_ALIGN = -10     /* an FP8 entry point's tensor pointer is not 16-byte aligned */
 } fa2_status;
 
 /* Size limits (validated): N_k * d and N_q * d below 2^30 per head (one
@@ -210,6 +211,66 @@ int fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const vo
  * enqueued.
  */
 int fa2_num_splits(int B, int H, int N_q, int N_k, int d, int num_cus);
+
+/*
+ * FP8 forward (the improvements page: section 三 credits FlashAttention-3 with
+ * FP8 tensor-core support, and section 四 point ③ says FP8 doubles matrix
+ * throughput while its precision loss must be held in check by scaling; the
+ * pages give no scaling recipe).  The recipe here: each (batch, head) slice of
+ * Q, K and V is scaled so that its largest magnitude becomes 448, the largest
+ * OCP e4m3 (e4m3fn) value, and rounded to nearest even; descale = amax / 448
+ * per slice is applied back in fp32.  Both products run on the 8-bit matrix
+ * unit; the probabilities are scaled by 2^7 and rounded to e4m3 for the P.V
+ * product, O is divided by the sum of those rounded probabilities, and LSE
+ * uses the sum of the fp32 probabilities.  The result approximates exact
+ * attention of the dequantised inputs decode(code) * descale.
+ *
+ * Codes are bytes (e4m3fn: sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; 0x7f and 0xff are NaN and must not appear).  Every tensor pointer of
+ * these entry points must be 16-byte aligned (FA2_ERR_ALIGN otherwise).
+ */
+
+/*
+ * fa2_fp8_vt_stride — row stride, in bytes (= keys), of a transposed V code
+ * tensor: N_k rounded up to a multiple of 16.  Returns FA2_ERR_BAD_SHAPE for
+ * N_k < 1 or N_k > 2^30.
+ */
+int fa2_fp8_vt_stride(int N_k);
+
+/*
+ * fa2_quantize_fp8 — per-(batch, head) e4m3 quantisation of a bf16 tensor.
+ *
+ * X: bf16 [B][H][N][d].  descale: fp32 [B][H] output, fp32(amax / 448) of the
+ * slice (1 for an all-zero slice).  codes: output, code = e4m3 RNE of
+ * fp32(x) * fp32(448 / amax):
+ *   transposed == 0: [B][H][N][d]                     (layout of Q and K)
+ *   transposed != 0: [B][H][d][fa2_fp8_vt_stride(N)]  (layout of V for
+ *                    fa2_fwd_fp8; columns N .. stride-1 are written as 0)
+ * X must hold finite values.  codes and descale must not overlap X or each
+ * other.  d: 64 or 128; B, H, N >= 1 with N * d below 2^30.  Four kernels are
+ * enqueued on `stream`; descale holds intermediate values until the last.
+ * Returns FA2_OK or a negative fa2_status.
+ */
+int fa2_quantize_fp8(const void* X, void* codes, float* descale, int B, int H, int N, int d,
+                     int transposed, void* stream);
+
+/*
+ * fa2_fwd_fp8 — attention forward on FP8 inputs.
+ *
+ * Qc [B][H][N_q][d] and Kc [B][H][N_k][d] codes; Vt [B][H][d][stride] codes of
+ * V transposed, stride = fa2_fp8_vt_stride(N_k) (fa2_quantize_fp8 with
+ * transposed != 0 writes it).  descale_q, descale_k, descale_v: fp32 [B][H],
+ * positive and finite.  O bf16 [B][H][N_q][d] and LSE fp32 [B][H][N_q] as in
+ * fa2_fwd, with
+ *   s_ij = scale * (descale_q * descale_k) * sum_c decode(Qc[i][c]) decode(Kc[j][c])
+ *   O[i] = descale_v * sum_j softmax_j(s_ij) decode(V[j])
+ * over the visible keys (causal as in fa2_fwd).  Rows are never empty; O and
+ * LSE must not overlap any input or each other.  Launch shape, work order and
+ * the remaining errors as fa2_fwd.
+ */
+int fa2_fwd_fp8(const void* Qc, const void* Kc, const void* Vt, const float* descale_q,
+                const float* descale_k, const float* descale_v, void* O, float* LSE, int B, int H,
+                int N_q, int N_k, int d, int causal, float scale, void* stream);
 
 /* fa2_status_string — static, human-readable text for a status code. */
 const char* fa2_status_string(int status);

@@ -123,3 +123,76 @@ def assert_grads_close(got, ref, bounds, what=""):
             idx = np.unravel_index(np.argmax(err - tol), err.shape)
             raise AssertionError(f"{what} {name}: {int(bad.sum())} elements out of bound; worst at {idx}: "
                                  f"got {g[idx]:.6g} ref {r[idx]:.6g} err {err[idx]:.3g} tol {tol[idx]:.3g}")
+
+
+# ---- FP8 forward ----
+# Error of the 8-bit matrix product relative to sum |a_k b_k| of its terms, with margin over
+# the worst case seen on the hardware (2^-11.7 over random codes of every exponent); the
+# probabilities are scaled by 2^7 before rounding to e4m3 (3 mantissa bits: relative error
+# 2^-4, subnormal spacing 2^-9 below 2^-6).
+FP8_EPS_MMA = 2.0 ** -10
+FP8_U = 2.0 ** -4
+FP8_PSCALE = 2.0 ** 7
+
+
+def fp8_head_bounds(qh, kh, vh, rows_i, causal, scale, o_ref, lse_ref):
+    """Error bounds for the FP8 forward of one head's rows against the fp64 oracle.
+
+    qh [n, d]: dequantised Q rows (indices rows_i); kh, vh [n_k, d] dequantised K, V; o_ref,
+    lse_ref: the oracle's result for those rows.  Returns (bound_o [n, d], var_o [n, d],
+    bound_lse [n]):
+      * each probability p_j reaches the P.V product with relative error t_j = u_j + 2 E_j:
+        u_j from rounding to e4m3 (2^-4, or the subnormal floor) and E_j the score error of
+        the 8-bit product; the output row is a convex combination of V rows, so
+        |O - O_ref| <= sum_j p_j (t_j + tbar) |v_j - O_ref| / (1 - tbar), tbar = sum_j p_j t_j,
+        plus the product error of P.V and of the row sum, and the bf16 output rounding;
+      * var_o: the expected squared error if the rounding errors are independent (used by an
+        RMS check that a systematic mistake would fail);
+      * |LSE - LSE_ref| <= sum_j p_j E_j plus fp32 summation and logarithm rounding."""
+    n_k = kh.shape[0]
+    s = scale * (qh @ kh.T)
+    if causal:
+        s = np.where(np.arange(n_k)[None, :] > np.asarray(rows_i)[:, None], -np.inf, s)
+    p = np.exp(s - lse_ref[:, None])
+    E = FP8_EPS_MMA * abs(scale) * (np.abs(qh) @ np.abs(kh).T) + 2.0 ** -20 * np.abs(np.where(np.isfinite(s), s, 0))
+    E = np.where(p > 0, E, 0.0)
+    smax = np.max(s, axis=1)
+    Z = np.exp(lse_ref - smax - E.max(axis=1))  # lower bound of the kernel's final sum of exp(s - m)
+    normal = FP8_PSCALE * p * Z[:, None] >= 2.0 ** -6
+    pu = np.where(normal, FP8_U * p, np.minimum(p, 2.0 ** -10 / (FP8_PSCALE * Z[:, None])))
+    pt = pu + p * (2 * E + 2.0 ** -20)
+    tbar = pt.sum(axis=1)
+    assert np.all(tbar < 0.5), "bound derivation assumes small perturbations"
+    vabs = np.abs(vh)
+    n, d = o_ref.shape
+    bound = np.empty((n, d))
+    var = np.empty((n, d))
+    for r in range(n):
+        dev = np.abs(vh - o_ref[r][None, :])
+        b1 = (pt[r] + p[r] * tbar[r]) @ dev / (1 - tbar[r])
+        b2 = 2.5 * FP8_EPS_MMA * (p[r] @ vabs) / (1 - tbar[r])
+        bound[r] = b1 + b2 + 2.0 ** -8 * np.abs(o_ref[r]) + 1e-6 * vabs.max()
+        var[r] = (pu[r] ** 2 / 3 + (2 * p[r] * E[r]) ** 2) @ dev ** 2 + (2.0 ** -7 * o_ref[r]) ** 2 / 12
+    bound_lse = (p * E).sum(axis=1) + 2.0 ** -20 * (1 + np.abs(lse_ref)) + n_k * 2.0 ** -23
+    return bound, var, bound_lse
+
+
+def assert_fp8_close(o_gpu, lse_gpu, o_ref, lse_ref, bound, var, bound_lse, what=""):
+    """Element-wise |O - O_ref| <= bound and |LSE - LSE_ref| <= bound_lse, and the RMS check
+    sum (O - O_ref)^2 <= 4 sum var (the expected squared error of independent roundings,
+    with margin)."""
+    o_gpu = np.asarray(o_gpu, dtype=np.float64)
+    lse_gpu = np.asarray(lse_gpu, dtype=np.float64)
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu)), f"{what}: non-finite output"
+    err = np.abs(o_gpu - o_ref)
+    el = np.abs(lse_gpu - lse_ref)
+    ratio = err / bound
+    io = np.unravel_index(np.argmax(ratio), err.shape)
+    il = int(np.argmax(el / bound_lse))
+    rms = float(np.sum(err ** 2) / np.sum(var))
+    msg = (f"{what}: max|dO|={err.max():.3e}, worst/bound {ratio[io]:.3f} at {io} (ref {o_ref[io]:.4f}, "
+           f"bound {bound[io]:.3e}); mean|dO| {err.mean():.2e}; sum dO^2 / sum var = {rms:.3f}; "
+           f"max|dLSE|={el.max():.3e}, worst/bound {el[il] / bound_lse[il]:.3f}")
+    print(msg, flush=True)
+    assert ratio[io] <= 1 and el[il] <= bound_lse[il] and rms <= 4.0, msg
+    return rms

@@ -12,7 +12,8 @@ import exact_attention_85_amd as fa2
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa2.h")
 
-OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, SPLITS, HIP, WINDOW = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, SPLITS, HIP, WINDOW, ALIGN = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10)
 
 
 def declared_functions():
@@ -22,9 +23,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_fwd", "fa2_fwd_splitkv",
-                                    "fa2_fwd_window", "fa2_num_splits", "fa2_splitkv_workspace_bytes",
-                                    "fa2_status_string"]
+    assert declared_functions() == ["fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_fp8_vt_stride", "fa2_fwd",
+                                    "fa2_fwd_fp8", "fa2_fwd_splitkv", "fa2_fwd_window", "fa2_num_splits",
+                                    "fa2_quantize_fp8", "fa2_splitkv_workspace_bytes", "fa2_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -34,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in (OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, SPLITS, HIP, WINDOW):
+    for code in (OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, SPLITS, HIP, WINDOW, ALIGN):
         s = fa2.status_string(code)
         assert s and "unknown" not in s
     assert "unknown" in fa2.status_string(12345)
@@ -199,3 +200,61 @@ def test_bwd_validation():
     assert bwd(dk=DO + 10) == ALIAS
     assert bwd(dv=DQ) == ALIAS
     assert bwd(ws=DK) == ALIAS
+
+
+# ---- FP8 entry points ----
+SQ, SK, SV = (0x10000000000 + (6 + i) * 64 * GB for i in range(3))  # descale arrays
+
+
+def fwd8(q=Q, k=K, v=V, dq=SQ, dk=SK, dv=SV, o=O, l=L, B=1, H=2, nq=256, nk=256, d=64, causal=0, scale=0.125):
+    lib = fa2.load_library()
+    return lib.fa2_fwd_fp8(q, k, v, dq, dk, dv, o, l, B, H, nq, nk, d, causal, scale, None)
+
+
+def quant8(x=Q, c=K, s=L, B=1, H=2, n=256, d=64, t=0):
+    return fa2.load_library().fa2_quantize_fp8(x, c, s, B, H, n, d, t, None)
+
+
+def test_fp8_vt_stride():
+    lib = fa2.load_library()
+    assert [lib.fa2_fp8_vt_stride(n) for n in (1, 15, 16, 17, 100, 4096)] == [16, 16, 16, 32, 112, 4096]
+    assert lib.fa2_fp8_vt_stride(0) == BAD_SHAPE and lib.fa2_fp8_vt_stride((1 << 30) + 1) == BAD_SHAPE
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "dq", "dk", "dv", "o", "l"])
+def test_fp8_null_pointers(which):
+    assert fwd8(**{which: None}) == NULLPTR
+
+
+@pytest.mark.parametrize("which", ["x", "c", "s"])
+def test_quant8_null_pointers(which):
+    assert quant8(**{which: None}) == NULLPTR
+
+
+def test_fp8_shapes_and_scale():
+    assert fwd8(nq=0) == BAD_SHAPE and fwd8(nk=0) == BAD_SHAPE and fwd8(B=0) == BAD_SHAPE
+    assert fwd8(d=96) == HEAD_DIM and quant8(d=32) == HEAD_DIM
+    assert quant8(n=0) == BAD_SHAPE and quant8(B=256, H=256) == BAD_SHAPE
+    assert fwd8(scale=float("nan")) == BAD_SCALE
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "dq", "o", "l"])
+def test_fp8_alignment(which):
+    base = dict(q=Q, k=K, v=V, dq=SQ, o=O, l=L)
+    assert fwd8(**{which: base[which] + 8}) == ALIGN
+
+
+def test_quant8_alignment_and_alias():
+    assert quant8(x=Q + 2) == ALIGN and quant8(c=K + 4) == ALIGN
+    # codes overlapping X, descale overlapping codes
+    assert quant8(c=Q + 256) == ALIAS
+    assert quant8(s=K + 16) == ALIAS
+    # transposed codes are d * stride per head: a descale right after the row-layout size overlaps
+    assert quant8(n=100, s=K + 2 * 100 * 64, t=1) == ALIAS
+
+
+def test_fp8_alias():
+    # O over the transposed V codes (d * stride bytes per head), LSE over a descale
+    assert fwd8(o=V + 64 * 256 * 2 - 16) == ALIAS
+    assert fwd8(l=SK) == ALIAS
+    assert fwd8(o=L) == ALIAS

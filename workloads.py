@@ -106,3 +106,21 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
 def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact fp64 values of a bf16 tensor."""
     return t.detach().cpu().to(torch.float64).numpy()
+
+
+def make_fp8_codes(shape, seed: int, exp_lo: int = 9, exp_hi: int = 14) -> np.ndarray:
+    """Random e4m3 byte codes: sign uniform, exponent field uniform in [exp_lo, exp_hi]
+    (exp_hi <= 14 keeps clear of the NaN pattern), mantissa field uniform in 0..7.
+    With the defaults the magnitudes are log-uniform over [4, 240]."""
+    assert 0 <= exp_lo <= exp_hi <= 14
+    g = np.random.default_rng(seed)
+    sign = g.integers(0, 2, shape, dtype=np.uint8)
+    e = g.integers(exp_lo, exp_hi + 1, shape, dtype=np.uint8)
+    m = g.integers(0, 8, shape, dtype=np.uint8)
+    return (sign << 7) | (e << 3) | m
+
+
+def make_fp8_descales(B: int, H: int, seed: int, lo: float = 0.008, hi: float = 0.016) -> np.ndarray:
+    """fp32 [B, H] descales drawn log-uniformly from [lo, hi]."""
+    g = np.random.default_rng(seed)
+    return np.exp(g.uniform(np.log(lo), np.log(hi), (B, H))).astype(np.float32)
