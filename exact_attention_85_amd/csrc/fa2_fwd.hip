@@ -26,10 +26,14 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace fa2 {
 namespace {
 
 constexpr int kBC = 64;  // keys per K/V tile
+constexpr int kPingPongMinRows = 2048;        // unbanded attention: ping-pong kernel from here
+constexpr int kPingPongMinRowsBanded = 8192;  // causal or windowed
 
 // Per-wave state of one 32-row query block: the Q fragment (B operand of
 // S^T = K Q^T; lane holds Q[row][16t + 8hf .. +7]), the O^T accumulator
@@ -560,6 +564,255 @@ __global__ void __launch_bounds__(256) splitkv_merge_kernel(FwdParams p) {
   if (lane == 0) p.lse[rg] = llsum > 0.f ? M + __logf(llsum) : -INFINITY;
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong forward: 8 waves, 256 query rows (synthesis page, section 2: the
+// HipKittens paragraph replaces producer/consumer wave specialisation by an
+// 8-wave ping-pong in which every wave computes and wave priorities order the
+// two halves; the FlashAttention-3 paragraph credits its speedup to
+// overlapping matrix work with the softmax).  Waves w and w+4 share a SIMD;
+// group 0 (waves 0-3) runs one phase ahead of group 1 (waves 4-7), so that on
+// every SIMD one wave issues its matrix products (at raised priority) while
+// the other computes its softmax.  Per tile j and wave, the phases are
+//   matrix phase:  O += P_{j-1} V_{j-1};  S_j = K_j Q^T
+//   vector phase:  P_j from S_j (online softmax)
+// and every phase ends at a workgroup barrier.  Group 0 runs the matrix phase
+// of tile j in global phase 2j and the vector phase in 2j+1; group 1 one phase
+// later.  K_j and V_{j-1} are read in phases 2j and 2j+1; K_{j+1} and V_j
+// stream into the other buffers meanwhile (issued at the start of 2j, waited
+// for at the end of 2j+1).  The raw scores stay in registers through the
+// vector phase, so the exact redo of a tile never reads K again.
+template <int D, int NW>
+__device__ __forceinline__ void issue_one(i32x4 rs, const char* dst, int k0, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int NLD = kBC * CPR / (64 * NW);
+  const unsigned toff = (unsigned)k0 * D * 2;
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int s = (i * NW + wave) * 64 + lane;
+    const int r = s / CPR;
+    const int c = (s % CPR) ^ (swz<D>(r, 0) - r * CPR);
+    const unsigned off = (unsigned)((r * D + c * 8) * 2) + toff;
+    lds_dma16(rs, dst + (i * NW + wave) * 64 * 16, off);
+  }
+}
+
+template <int D, unsigned VOFF>
+__device__ __forceinline__ void pv_tile(WaveRows<D>& w, const LdsAddr<D>& la, const bf16x8 (&pb)[4]) {
+  constexpr int NB = D / 32;
+  constexpr unsigned ROW = D * 2;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const unsigned roff = VOFF + (kb * 32 + 16 * t) * ROW;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<lds_i16x4*>((uintptr_t)(la.va[2 * nb] + roff)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<lds_i16x4*>((uintptr_t)(la.va[2 * nb + 1] + roff)));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        w.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[2 * kb + t], w.acc[nb], 0, 0, 0);
+      }
+    }
+}
+
+// exp2(s * sl2 - m) of one 8-register slice, converted to bf16; adds to the sums
+__device__ __forceinline__ bf16x8 exp_slice(const f32x16& s, int half, float sl2, float m, float& rs) {
+  f32x8 e;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * half + r], sl2, -m));
+    rs += e[r];
+  }
+  return cvt_bf16x8(e);
+}
+
+template <int D>
+__device__ __forceinline__ void softmax_pp(WaveRows<D>& w, f32x16& s0, f32x16& s1, bf16x8 (&pb)[4], bool need_mask,
+                                           int k0, int row_lo, int row_hi, float sl2, int lane) {
+  constexpr int NB = D / 32;
+  const int hf = lane >> 5;
+  if (need_mask) mask_scores(s0, s1, k0, row_lo, row_hi, hf);
+  bool exact = __ballot(w.m_run == -INFINITY) != 0;
+  float rs = 0.f;
+  if (!exact) {
+    pb[0] = exp_slice(s0, 0, sl2, w.m_run, rs);
+    pb[1] = exp_slice(s0, 1, sl2, w.m_run, rs);
+    pb[2] = exp_slice(s1, 0, sl2, w.m_run, rs);
+    pb[3] = exp_slice(s1, 1, sl2, w.m_run, rs);
+    exact = __ballot(rs > kLazyBound) != 0;
+  }
+  if (exact) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    const float m_new = fmaxf(w.m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_use);
+    w.l_run *= alpha;
+    w.l16 *= alpha;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) w.acc[nb] *= alpha;
+    w.m_run = m_new;
+    rs = 0.f;
+    pb[0] = exp_slice(s0, 0, sl2, m_use, rs);
+    pb[1] = exp_slice(s0, 1, sl2, m_use, rs);
+    pb[2] = exp_slice(s1, 0, sl2, m_use, rs);
+    pb[3] = exp_slice(s1, 1, sl2, m_use, rs);
+  }
+  w.l_run += rs;
+  w.l16 = sum_bf16(pb, w.l16);
+}
+
+template <int D>
+__global__ void __launch_bounds__(512, 1) fwd_pp_kernel(FwdParams p, float sl2, unsigned qsign) {
+  constexpr int NW = 8;
+  constexpr int BR = 32 * NW;
+  constexpr int KT = D / 16;
+  constexpr int NB = D / 32;
+  constexpr int TILE_BYTES = kBC * D * 2;
+  constexpr unsigned STAGE = 2 * TILE_BYTES;
+
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][TILE_BYTES];  // [stage][K=0 / V=1]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int hf = lane >> 5;
+  const int col = lane & 31;
+
+  const int n_qb = (p.n_q + BR - 1) / BR;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = L / n_qb;
+  int qb = L % n_qb;
+  const int wl = p.wl, wr = p.wr;
+  if (wl < 0 && wr >= 0) qb = n_qb - 1 - qb;
+  const int q0 = qb * BR;
+  const int q0w = q0 + wave * 32;
+  const int row = q0w + col;
+
+  int klo = 0, khi = p.n_k, klo_w = 0, khi_w = p.n_k, row_lo = 0, row_hi = p.n_k - 1;
+  if (wr >= 0) {
+    khi = min(khi, q0 + BR + wr);
+    khi_w = min(khi_w, q0w + 32 + wr);
+    row_hi = min(row_hi, row + wr);
+  }
+  if (wl >= 0) {
+    klo = max(klo, q0 - wl);
+    klo_w = max(klo_w, q0w - wl);
+    row_lo = max(row_lo, row - wl);
+  }
+  const int kfirst = klo / kBC * kBC;
+  const int n_tiles = khi > kfirst ? (khi - kfirst + kBC - 1) / kBC : 0;
+
+  const uint16_t* Qh = p.q + (long long)bh * p.n_q * D;
+  const i32x4 krs = raw_rsrc(p.k + (long long)bh * p.n_k * D, (long long)khi * D * 2);
+  const i32x4 vrs = raw_rsrc(p.v + (long long)bh * p.n_k * D, (long long)khi * D * 2);
+
+  WaveRows<D> w;
+  {
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qh, (long long)p.n_q * D * 2);
+    const u32x4 sign = {qsign, qsign, qsign, qsign};
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      const u32x4 raw = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, (unsigned)((row * D + 16 * t + 8 * hf) * 2), 0, 0));
+      w.qf[t] = as_bf16x8(raw ^ sign);
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) w.acc[nb] = f32x16{};
+  w.m_run = -INFINITY;
+  w.l_run = 0.f;
+  w.l16 = 0.f;
+
+  LdsAddr<D> la;
+  make_lds_addr<D>(la, (unsigned)(uintptr_t)(const lds_void*)&lds[0][0][0], lane);
+
+  f32x16 s0 = {}, s1 = {};
+  bf16x8 pb[4];
+
+  auto act = [&](int j) {
+    const int kk = kfirst + j * kBC;
+    return j >= 0 && j < n_tiles && kk < khi_w && kk + kBC > klo_w;
+  };
+  auto need_mask = [&](int j) {
+    const int kk = kfirst + j * kBC;
+    return (kk + kBC > p.n_k) || (wr >= 0 && kk + kBC - 1 > q0w + wr) || (wl >= 0 && kk < q0w + 31 - wl);
+  };
+  // matrix phase of tile j: O += P_{j-1} V_{j-1}, then S_j = K_j Q^T.  KST: stage of K_j.
+  auto mat = [&](int j, auto kst) {
+    constexpr unsigned KS = decltype(kst)::value;
+    __builtin_amdgcn_s_setprio(1);
+    if (act(j - 1)) pv_tile<D, (1 - KS) * STAGE + TILE_BYTES>(w, la, pb);
+    __builtin_amdgcn_sched_barrier(0);
+    if (act(j)) qk_tile<D, KS * STAGE>(w, la, s0, s1);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto vec = [&](int j) {
+    if (act(j)) softmax_pp(w, s0, s1, pb, need_mask(j), kfirst + j * kBC, row_lo, row_hi, sl2, lane);
+  };
+  // tile iteration j: phases 2j and 2j+1.  KST = j % 2.  Group 0 runs (matrix j, vector j),
+  // group 1 (vector j-1, matrix j); each group has its own loop so that its phases are
+  // straight-line code.  Both execute the same barriers.
+  auto issue = [&](int j, auto kst) {
+    constexpr unsigned KS = decltype(kst)::value;
+    if (j + 1 < n_tiles) issue_one<D, NW>(krs, lds[1 - KS][0], kfirst + (j + 1) * kBC, wave, lane);
+    if (j < n_tiles) issue_one<D, NW>(vrs, lds[KS][1], kfirst + j * kBC, wave, lane);
+  };
+  auto iter0 = [&](int j, auto kst) {
+    issue(j, kst);
+    mat(j, kst);
+    __syncthreads();
+    vec(j);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  auto iter1 = [&](int j, auto kst) {
+    issue(j, kst);
+    vec(j - 1);
+    __syncthreads();
+    mat(j, kst);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  if (n_tiles > 0) issue_one<D, NW>(krs, lds[0][0], kfirst, wave, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (grp == 0) {
+    for (int j = 0; j <= n_tiles; j += 2) {
+      iter0(j, std::integral_constant<unsigned, 0>{});
+      if (j + 1 <= n_tiles) iter0(j + 1, std::integral_constant<unsigned, 1>{});
+    }
+  } else {
+    for (int j = 0; j <= n_tiles; j += 2) {
+      iter1(j, std::integral_constant<unsigned, 0>{});
+      if (j + 1 <= n_tiles) iter1(j + 1, std::integral_constant<unsigned, 1>{});
+    }
+  }
+
+  const float l_tot = w.l_run + __shfl_xor(w.l_run, 32);
+  const float l16_tot = w.l16 + __shfl_xor(w.l16, 32);
+  if (row >= p.n_q) return;
+  const float inv = l16_tot > 0.f ? 1.f / l16_tot : 0.f;
+  uint16_t* Orow = p.o + ((long long)bh * p.n_q + row) * D;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 o4 = {w.acc[nb][4 * g] * inv, w.acc[nb][4 * g + 1] * inv, w.acc[nb][4 * g + 2] * inv,
+                        w.acc[nb][4 * g + 3] * inv};
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      const bf16x4 b4 = __builtin_convertvector(o4, bf16x4);
+      *reinterpret_cast<u32x2*>(Orow + 32 * nb + 8 * g + 4 * hf) = __builtin_bit_cast(u32x2, b4);
+    }
+  if (hf == 0) p.lse[(long long)bh * p.n_q + row] = l_tot > 0.f ? (w.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
 // scale handling shared by all launches: fold |scale|*log2(e) into one positive
 // multiplier and move the sign into Q
 void fold_scale(float scale, float* sl2, unsigned* qsign) {
@@ -598,6 +851,16 @@ hipError_t launch_decode(const FwdParams& p, hipStream_t stream) {
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   // one query row per head: the streaming decode kernel over the whole key range
   if (p.n_q == 1) return launch_decode<true>(p, stream);
+  // long sequences at d = 128: the ping-pong kernel (256-row blocks); it loses on shorter
+  // banded or causal sequences, where a 256-row block wastes more work at the band edges
+  if (p.d == 128 && p.n_q >= (p.wl < 0 && p.wr < 0 ? kPingPongMinRows : kPingPongMinRowsBanded)) {
+    float sl2;
+    unsigned qsign;
+    fold_scale(p.scale, &sl2, &qsign);
+    const unsigned grid = (unsigned)((long long)((p.n_q + 255) / 256) * p.B * p.H);
+    hipLaunchKernelGGL(fwd_pp_kernel<128>, dim3(grid), dim3(512), 0, stream, p, sl2, qsign);
+    return hipGetLastError();
+  }
   if (p.d == 128) return launch_tile<128, 4, false>(p, stream);
   return launch_tile<64, 4, false>(p, stream);
 }

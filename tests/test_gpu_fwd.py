@@ -7,6 +7,7 @@ import pytest
 import torch
 
 import exact_attention_85_amd as fa2
+import oracle
 import workloads
 from tests import gpu_util as gu
 
@@ -141,3 +142,39 @@ def test_errors_raise():
     q, k, v = workloads.make_qkv_shape(1, 1, 8, 8, 64, 1, DEV)
     with pytest.raises(fa2.Fa2Error):
         fa2.forward(q, k, v, scale=float("nan"))
+
+
+# Shapes at d = 128 that take the 8-wave ping-pong kernel (256-row blocks): unbanded attention
+# from N_q = 2048, causal or windowed from N_q = 8192.  Ragged query and key tails included.
+PINGPONG_FULL = [(2048, 2048), (2049, 777), (2300, 3001), (2111, 64), (2048, 1)]
+
+
+@pytest.mark.parametrize("nq,nk", PINGPONG_FULL)
+def test_pingpong_full_parity(nq, nk):
+    print(f"case pingpong nq={nq} nk={nk}", flush=True)
+    q, k, v = workloads.make_qkv_shape(1, 2, nq, nk, 128, seed=nq + 3 * nk, device=DEV)
+    o, lse = _run(q, k, v, False, 1.0 / math.sqrt(128))
+    o_ref, lse_ref = gu.oracle_full(q, k, v, False, 1.0 / math.sqrt(128))
+    gu.assert_close(o.float().cpu().double().numpy(), lse.cpu().double().numpy(), o_ref, lse_ref,
+                    what=f"pingpong nq={nq} nk={nk}")
+
+
+@pytest.mark.parametrize("nq,nk,window", [(8192, 8192, None), (8300, 8300, None), (8200, 5000, None),
+                                          (8450, 8450, (1000, 0)), (8192, 9000, (300, 300))])
+def test_pingpong_banded_sampled(nq, nk, window):
+    print(f"case pingpong banded nq={nq} nk={nk} window={window}", flush=True)
+    q, k, v = workloads.make_qkv_shape(1, 2, nq, nk, 128, seed=nq + nk, device=DEV)
+    scale = 1.0 / math.sqrt(128)
+    if window is None:
+        o, lse = _run(q, k, v, True, scale)
+        wl, wr = -1, 0
+    else:
+        wl, wr = window
+        o, lse = fa2.forward_window(q, k, v, wl, wr, scale=scale)
+        torch.cuda.synchronize()
+    rows = gu.sample_rows(1, 2, nq, 120, seed=nq, block=256)
+    flat = np.array([h * nq + i for (_, h, i) in rows], dtype=np.int64)
+    o_ref, lse_ref = oracle.attention_window_rows_bf16(workloads.bf16_bits(q), workloads.bf16_bits(k),
+                                                       workloads.bf16_bits(v), flat, wl, wr, scale)
+    o_g, l_g = gu.gpu_rows(o, lse, rows)
+    gu.assert_close(o_g, l_g, o_ref, lse_ref, what=f"pingpong banded nq={nq} nk={nk} window={window}")
