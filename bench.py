@@ -28,6 +28,7 @@ import torch  # noqa: E402
 import workloads  # noqa: E402
 
 PEAK_BF16_TFLOPS = 256 * 4 * 1024 * 2.4e9 / 1e12   # 2516.6: 256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS              # 5033.2: the 8-bit matrix rate is twice the bf16 rate
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd TFLOP/s (bf16, causal/non-causal) and % of MI355X MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -220,6 +221,34 @@ def main():
                           "workspace_bytes": wsx.numel() * 4})
             log(f"{wx.name} backward causal={cx}: {msx:.3f} ms, {tf:.1f} TFLOP/s")
             del qx, kx, vx, dox, ox, lx, wsx, gq, gk, gv
+        # FP8 forward: inputs quantised per (batch, head) outside the timed region (the quantiser
+        # is timed on its own: it reads bf16 and writes one byte per element)
+        for wx, cx in ((workloads.C4, False), (workloads.C4, True), (workloads.C3, False)):
+            qx, kx, vx = workloads.make_qkv(wx, dev)
+            qc, dq = fa2.quantize_fp8(qx)
+            kc, dk = fa2.quantize_fp8(kx)
+            vt, dv = fa2.quantize_fp8(vx, transposed=True)
+            ox = torch.empty_like(qx)
+            lx = torch.empty((wx.B, wx.H, wx.n_q), dtype=torch.float32, device=dev)
+            msx = time_launches(lambda: fa2.forward_fp8(qc, kc, vt, dq, dk, dv, causal=cx, scale=wx.scale, out=ox,
+                                                        lse=lx), steps_x, args.warmup)
+            tf = wx.flop(cx) / (msx * 1e-3) / 1e12
+            row = {"workload": f"{wx.name}_fp8", "causal": cx, "dtype": "fp8_e4m3", "ms": round(msx, 4),
+                   "TFLOP/s": round(tf, 2), "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                   "speedup_vs_bf16_kernel_same_shape": None}
+            if wx is workloads.C4 and not cx:
+                msq = time_launches(lambda: fa2.quantize_fp8(vx, transposed=True), steps_x, args.warmup)
+                nbytes = 3 * wx.B * wx.H * wx.n_k * wx.d
+                row["quantize_v_transposed"] = {"ms": round(msq, 4), "GB/s": round(nbytes / (msq * 1e-3) / 1e9, 1)}
+            extra.append(row)
+            log(f"{wx.name} fp8 causal={cx}: {msx:.3f} ms, {tf:.1f} TFLOP/s")
+            del qx, kx, vx, qc, kc, vt, ox, lx
+        bf16_ms = {(e["workload"], e["causal"]): e["ms"] for e in extra if "dtype" not in e and "ms" in e}
+        bf16_ms[(w.name, causal)] = ms
+        for e in extra:
+            if e.get("dtype") == "fp8_e4m3":
+                ref = bf16_ms.get((e["workload"][:-4], e["causal"]))
+                e["speedup_vs_bf16_kernel_same_shape"] = round(ref / e["ms"], 3) if ref else None
         # split-KV decode: bound by streaming K and V from HBM
         wd = workloads.C5
         qd, kd, vd = workloads.make_qkv(wd, dev)

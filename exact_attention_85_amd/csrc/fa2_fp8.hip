@@ -43,7 +43,6 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kBC8 = 64;             // keys per tile
 constexpr float kPLog2 = 7.f;        // probabilities are scaled by 2^7 before rounding
-constexpr float kCodeMax = 448.f;    // largest finite e4m3 value
 constexpr unsigned kOnes = 0x38383838u;  // four e4m3 ones
 
 __device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
@@ -158,40 +157,28 @@ __device__ __forceinline__ int pack4(float a, float b, float c, float d) {
 }
 
 // One 64-key tile for one wave.  The probabilities are formed against the
-// reference maximum m_run and scaled by 2^7; they must not exceed 448 to be
-// representable.  That holds when the lane's fp32 sum stays below 448, else
-// when the lane's largest probability does; otherwise (and while some row has
-// no reference yet) the tile is redone exactly: new maximum, rescale of the
-// accumulators and both sums, probabilities again (then each is <= 2^7).
-template <int D, unsigned KOFF, unsigned VOFF>
-__device__ __forceinline__ void tile8(Fp8Rows<D>& w, const Fp8Addr<D>& la, bool need_mask, int k0, int row_lo,
-                                      int row_hi, float sl2, int lane) {
+// reference maximum m_run and scaled by 2^7; to be representable they must not
+// exceed 448, i.e. no score may exceed the reference by more than log2(3.5).
+// The tile's row maxima are taken from the raw scores first; only when some
+// row of the wave exceeds its reference by more than kHead (and while a row
+// has no reference yet) are the references raised to the tile maxima and the
+// accumulators and sums rescaled.  Each probability is then at most
+// 2^(7 + kHead) < 448, and the exponentials are computed once.
+constexpr float kHead = 1.75f;
+
+// Softmax of one tile from its raw scores: P (scaled by 2^7, rounded to e4m3)
+// packed as the B operand of the second product.
+template <int D>
+__device__ __forceinline__ void softmax8(Fp8Rows<D>& w, f32x16& s0, f32x16& s1, i32x8& pw, bool need_mask, int k0,
+                                         int row_lo, int row_hi, float sl2, int lane) {
   constexpr int NB = D / 32;
   const int hf = lane >> 5;
-  f32x16 s0, s1;
-  qk8<D, KOFF>(w, la, s0, s1);
   if (need_mask) mask8(s0, s1, k0, row_lo, row_hi, hf);
-
-  bool exact = __ballot(w.m_run == -INFINITY) != 0;
-  float rs = 0.f;
-  if (!exact) {
-    rs = exp8(s0, s1, sl2, w.m_run - kPLog2);
-    if (__ballot(rs > kCodeMax)) {
-      float mp = 0.f;
+  float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mp = fmaxf(mp, fmaxf(s0[r], s1[r]));
-      if (__ballot(mp > kCodeMax)) {
-        exact = true;
-        qk8<D, KOFF>(w, la, s0, s1);  // scores again (the K tile is still in LDS)
-        if (need_mask) mask8(s0, s1, k0, row_lo, row_hi, hf);
-      }
-    }
-  }
-  if (exact) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+  if (__ballot(mx > w.m_run + kHead)) {
     const float m_new = fmaxf(w.m_run, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_use);
@@ -200,25 +187,36 @@ __device__ __forceinline__ void tile8(Fp8Rows<D>& w, const Fp8Addr<D>& la, bool 
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) w.acc[nb] *= alpha;
     w.m_run = m_new;
-    rs = exp8(s0, s1, sl2, m_use - kPLog2);
   }
-  w.l_run += rs;
-
-  i32x8 pw;
+  const float m_use = w.m_run == -INFINITY ? 0.f : w.m_run;  // all scores so far masked: they stay -inf
+  w.l_run += exp8(s0, s1, sl2, m_use - kPLog2);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     pw[i] = pack4(s0[4 * i], s0[4 * i + 1], s0[4 * i + 2], s0[4 * i + 3]);
     pw[4 + i] = pack4(s1[4 * i], s1[4 * i + 1], s1[4 * i + 2], s1[4 * i + 3]);
   }
-  const i32x8 ones = {(int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes,
-                      (int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes};
+}
+
+// O^T += V^T P^T and the row sums of the rounded P (against a block of ones).
+template <int D, unsigned VOFF>
+__device__ __forceinline__ void pv8(Fp8Rows<D>& w, const Fp8Addr<D>& la, i32x8 ones, const i32x8& pw) {
   w.lsum = mfma8(ones, pw, w.lsum);
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+  for (int nb = 0; nb < D / 32; ++nb) {
     const i32x8 a = cat8(lds_load<u32x4>(la.va[0] + VOFF + nb * 32 * 64),
                          lds_load<u32x4>(la.va[1] + VOFF + nb * 32 * 64));
     w.acc[nb] = mfma8(a, pw, w.acc[nb]);
   }
+}
+
+template <int D, unsigned KOFF, unsigned VOFF>
+__device__ __forceinline__ void tile8(Fp8Rows<D>& w, const Fp8Addr<D>& la, i32x8 ones, bool need_mask, int k0,
+                                      int row_lo, int row_hi, float sl2, int lane) {
+  f32x16 s0, s1;
+  i32x8 pw;
+  qk8<D, KOFF>(w, la, s0, s1);
+  softmax8(w, s0, s1, pw, need_mask, k0, row_lo, row_hi, sl2, lane);
+  pv8<D, VOFF>(w, la, ones, pw);
 }
 
 // Forward kernel.  Workgroup = NW waves = 32*NW query rows of one (batch, head);
@@ -305,13 +303,15 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_fp8_kernel(Fp8Params p) {
     asm volatile("" : "+v"(la.va[0]), "+v"(la.va[1]));
   }
   constexpr unsigned STAGE = 2 * TILE;
+  i32x8 ones = {(int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes};
+  asm volatile("" : "+v"(ones));  // kept in registers rather than rebuilt per tile
 
 #define FA2_STEP8(STG, k0_)                                                                            \
   do {                                                                                               \
     const int kk = (k0_);                                                                            \
     if (kk < khi_w && kk + kBC8 > klo_w)                                                             \
       tile8<D, STG * STAGE, STG * STAGE>(                                                            \
-          w, la,                                                                                     \
+          w, la, ones,                                                                               \
           (kk + kBC8 > p.n_k) || (wr >= 0 && kk + kBC8 - 1 > q0w + wr) || (wl >= 0 && kk < q0w + 31 - wl), \
           kk, row_lo, row_hi, sl2, lane);                                                            \
   } while (0)
