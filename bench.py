@@ -4,11 +4,12 @@ A step is one fa2_fwd call over one batch of the long-sequence workload
 B=1, H=32, N_q=N_k=16384, d=128 (bf16, non-causal, scale 1/sqrt(d)), inputs
 resident in HBM.  Throughput counts 4*B*H*N_q*N_k*d FLOP per step (halved for
 causal).  The same run also times the other named workloads (the causal
-variants, the d=64 and d=128 training shapes, and the split-KV decode) and the
-fp64 oracle on a bounded sample of the headline workload, and prints ONE JSON
-line.
+variants, the d=64 and d=128 training shapes, sliding window, backward, the
+FP8 forward and the split-KV decode) and the fp64 oracle on a bounded sample of
+the headline workload, and prints ONE JSON line.  With --fp8 the timed step is
+the FP8 forward of the same workload (for its own profile).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu] [--calib-copy]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu] [--calib-copy] [--fp8]
 """
 import argparse
 import hashlib
@@ -33,18 +34,20 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd TFLOP/s (bf16, causal/non-causal) and % of MI355X MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "exact_attention_85_amd", "csrc", "fa2_fwd.hip")
+FP8_SRC = os.path.join(ROOT, "exact_attention_85_amd", "csrc", "fa2_fp8.hip")
+METRIC_FP8 = "attention fwd TFLOP/s (fp8 e4m3 inputs, per-head scaling) and % of MI355X fp8 MFMA peak"
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_sha(path: str = KERNEL_SRC) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(key: str):
+def measured_traffic(key: str, src: str = KERNEL_SRC):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None when
     absent or taken on a different kernel source."""
     try:
@@ -53,7 +56,7 @@ def measured_traffic(key: str):
     except (OSError, ValueError):
         return None
     e = t.get(key)
-    if not e or e.get("kernel_source_sha") != kernel_source_sha():
+    if not e or e.get("kernel_source_sha") != kernel_source_sha(src):
         return None
     return e.get("hbm_bytes_per_launch")
 
@@ -107,6 +110,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the FP8 forward on the same workload instead (inputs quantised per head "
+                         "before the timed region)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB read + 1 GiB write elementwise kernel (counter calibration)")
     args = ap.parse_args()
@@ -136,8 +142,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step():
-        fa2.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse)
+    if args.fp8:
+        qc, dq = fa2.quantize_fp8(q)
+        kc, dk = fa2.quantize_fp8(k)
+        vt, dv = fa2.quantize_fp8(v, transposed=True)
+
+        def step():
+            fa2.forward_fp8(qc, kc, vt, dq, dk, dv, causal=causal, scale=w.scale, out=o, lse=lse)
+    else:
+        def step():
+            fa2.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -154,20 +168,25 @@ def main():
     flop = w.flop(causal)
     tflops = flop / (ms * 1e-3) / 1e12
     assert torch.isfinite(lse).all().item(), "non-finite LSE"
-    log(f"{w.name} non-causal: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% "
-        f"of {PEAK_BF16_TFLOPS:.1f}), wall {t_wall:.2f} s")
+    log(f"{w.name} non-causal{' fp8' if args.fp8 else ''}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s, wall {t_wall:.2f} s")
 
-    traffic = measured_traffic(f"fwd_kernel:{w.name}:noncausal")
+    peak = PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
+    if args.fp8:
+        kname, traffic = "fwd_fp8_kernel<128,4>", measured_traffic(f"fwd_fp8_kernel:{w.name}:noncausal", FP8_SRC)
+        alg_bytes = w.B * w.H * (w.n_q * w.d + 2 * w.n_k * w.d + 2 * w.n_q * w.d + 4 * w.n_q)  # 1-byte Q, K, V codes
+    else:
+        kname, traffic = "fwd_pp_kernel<128>", measured_traffic(f"fwd_pp_kernel:{w.name}:noncausal")
+        alg_bytes = w.io_bytes()
     result = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "metric": METRIC_FP8 if args.fp8 else METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3" if args.fp8 else "bf16", "data": "synthetic",
         "config": {"workload": f"{w.name}_noncausal", "B": w.B, "H": w.H, "N_q": w.n_q, "N_k": w.n_k, "d": w.d,
                    "causal": False, "scale": w.scale, "inputs": "iid N(0,1) fp32 -> bf16 RNE, seeded"},
-        "roofline": {"kernel": "fwd_kernel<128,4,false>", "bound": "mfma", "achieved": round(tflops, 2),
-                     "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "algorithmic_flop_per_launch": flop, "algorithmic_bytes_per_launch": w.io_bytes()},
+        "roofline": {"kernel": kname, "bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": round(peak, 1), "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": traffic,
+                     "algorithmic_flop_per_launch": flop, "algorithmic_bytes_per_launch": alg_bytes},
     }
 
     if not args.no_extra:
@@ -243,8 +262,9 @@ def main():
             extra.append(row)
             log(f"{wx.name} fp8 causal={cx}: {msx:.3f} ms, {tf:.1f} TFLOP/s")
             del qx, kx, vx, qc, kc, vt, ox, lx
-        bf16_ms = {(e["workload"], e["causal"]): e["ms"] for e in extra if "dtype" not in e and "ms" in e}
-        bf16_ms[(w.name, causal)] = ms
+        bf16_ms = {(e["workload"], e.get("causal")): e["ms"] for e in extra if "dtype" not in e and "ms" in e}
+        if not args.fp8:
+            bf16_ms[(w.name, causal)] = ms
         for e in extra:
             if e.get("dtype") == "fp8_e4m3":
                 ref = bf16_ms.get((e["workload"][:-4], e["causal"]))
@@ -283,7 +303,7 @@ def main():
         del qd, kd, vd, od, ld, ws
         result["workloads"] = extra
 
-    if not args.no_cpu:
+    if not args.no_cpu and not args.fp8:  # the oracle baseline is the bf16 definition
         result["cpu_baseline"] = cpu_baseline(w, causal, q, k, v)
         log(f"oracle: {result['cpu_baseline']}")
     print(json.dumps(result), flush=True)
