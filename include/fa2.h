@@ -247,7 +247,8 @@ int fa2_fp8_vt_stride(int N_k);
  *   transposed != 0: [B][H][d][fa2_fp8_vt_stride(N)]  (layout of V for
  *                    fa2_fwd_fp8; columns N .. stride-1 are written as 0)
  * X must hold finite values.  codes and descale must not overlap X or each
- * other.  d: 64 or 128; B, H, N >= 1 with N * d below 2^30.  Four kernels are
+ * other.  d: 64 or 128; B, H, N >= 1 with N * d below 2^30 and B * H at most
+ * 65535 (FA2_ERR_BAD_SHAPE otherwise).  Four kernels are
  * enqueued on `stream`; descale holds intermediate values until the last.
  * Returns FA2_OK or a negative fa2_status.
  */
