@@ -174,10 +174,12 @@ __device__ __forceinline__ void softmax8(Fp8Rows<D>& w, f32x16& s0, f32x16& s1, 
   constexpr int NB = D / 32;
   const int hf = lane >> 5;
   if (need_mask) mask8(s0, s1, k0, row_lo, row_hi, hf);
+  // IEEE maximum (NaN-propagating): gfx950 folds it into v_maximum3_f32 without the
+  // canonicalising copies that fmaxf needs on matrix-product results
   float mx = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+  for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[r], s1[r]));
+  mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32)) * sl2;
   if (__ballot(mx > w.m_run + kHead)) {
     const float m_new = fmaxf(w.m_run, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
