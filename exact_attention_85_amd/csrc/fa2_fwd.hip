@@ -89,6 +89,38 @@ __device__ __forceinline__ void qk_tile(const WaveRows<D>& w, const LdsAddr<D>& 
   }
 }
 
+
+// S^T = K Q^T with the K operands read PF pairs ahead of their products.  Left
+// to itself the scheduler keeps one pair in flight, and an LDS read takes longer
+// than the two products it feeds (64 cycles), so every pair stalled; the
+// scheduling-group barriers pin the order (PF pairs of reads, then per step two
+// products and the next pair of reads).
+template <int D, unsigned KOFF, int PF>
+__device__ __forceinline__ void qk_tile_pf(const WaveRows<D>& w, const LdsAddr<D>& la, f32x16& s0, f32x16& s1) {
+  constexpr unsigned ROW = D * 2;
+  constexpr int KT = D / 16;
+  bf16x8 a[PF][2];
+#pragma unroll
+  for (int t = 0; t < PF; ++t) {
+    a[t][0] = lds_load<bf16x8>(la.ka[t] + KOFF);
+    a[t][1] = lds_load<bf16x8>(la.ka[t] + KOFF + 32 * ROW);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+  s0 = f32x16{};
+  s1 = f32x16{};
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t % PF][0], w.qf[t], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t % PF][1], w.qf[t], s1, 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    if (t + PF < KT) {
+      a[t % PF][0] = lds_load<bf16x8>(la.ka[t + PF] + KOFF);
+      a[t % PF][1] = lds_load<bf16x8>(la.ka[t + PF] + KOFF + 32 * ROW);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  }
+}
+
 // -inf for keys outside this lane's row band [row_lo, row_hi] (the band already
 // clipped to the key tail).  Key k0 + 4hf + c is visible iff lo <= c <= hi; c is
 // a compile-time constant per register.
@@ -157,7 +189,7 @@ __device__ __forceinline__ void tile_step(WaveRows<D>& w, const LdsAddr<D>& la, 
   constexpr unsigned ROW = D * 2;
   const int hf = lane >> 5;
   f32x16 s0, s1;
-  qk_tile<D, KOFF>(w, la, s0, s1);
+  qk_tile_pf<D, KOFF, 2>(w, la, s0, s1);
   if (need_mask) mask_scores(s0, s1, k0, row_lo, row_hi, hf);
 
   bool exact = __ballot(w.m_run == -INFINITY) != 0;  // some row has no reference yet
@@ -749,7 +781,7 @@ __global__ void __launch_bounds__(512, 1) fwd_pp_kernel(FwdParams p, float sl2, 
     __builtin_amdgcn_s_setprio(1);
     if (act(j - 1)) pv_tile<D, (1 - KS) * STAGE + TILE_BYTES>(w, la, pb);
     __builtin_amdgcn_sched_barrier(0);
-    if (act(j)) qk_tile<D, KS * STAGE>(w, la, s0, s1);
+    if (act(j)) qk_tile_pf<D, KS * STAGE, 2>(w, la, s0, s1);
     __builtin_amdgcn_s_setprio(0);
   };
   auto vec = [&](int j) {
