@@ -317,6 +317,11 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
 
   // two LDS stages, unrolled by two so that every offset is an immediate
   for (int qi = qb0; qi < n_qb; qi += 2) {
+    // keep the dV^T / dK^T accumulators in AGPRs across iterations: otherwise the
+    // loop-carried values are assigned VGPRs and each iteration copies all 128 of
+    // them out of and back into the AGPRs the products accumulate in
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(dvt[nb]), "+a"(dkt[nb]));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // stage 0 published; dS^T and stage 1 free
     if (qi + 1 < n_qb) issue_q(1, qi + 1);
