@@ -223,16 +223,33 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
 
     // S = Q K^T and dP = dO V^T for two 32-row halves
     f32x16 s[2], dp[2];
+    {
+      // operands read PF steps ahead of their products (LDS latency exceeds two products)
+      constexpr int PF = 2;
+      constexpr int NST = 2 * KT;  // steps (qh, t)
+      bf16x8 ra[PF][2];
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-      s[qh] = f32x16{};
-      dp[qh] = f32x16{};
+      for (int st = 0; st < PF; ++st) {
+        ra[st][0] = lds_load<bf16x8>(la.ka[st % KT] + QOFF + (st / KT) * 32 * ROW);
+        ra[st][1] = lds_load<bf16x8>(la.ka[st % KT] + DOFF + (st / KT) * 32 * ROW);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
 #pragma unroll
-      for (int t = 0; t < KT; ++t) {
-        const bf16x8 qa = lds_load<bf16x8>(la.ka[t] + QOFF + qh * 32 * ROW);
-        const bf16x8 da2 = lds_load<bf16x8>(la.ka[t] + DOFF + qh * 32 * ROW);
-        s[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[t], s[qh], 0, 0, 0);
-        dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da2, vf[t], dp[qh], 0, 0, 0);
+      for (int st = 0; st < NST; ++st) {
+        const int qh = st / KT, t = st % KT;
+        if (t == 0) {
+          s[qh] = f32x16{};
+          dp[qh] = f32x16{};
+        }
+        s[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[st % PF][0], kf[t], s[qh], 0, 0, 0);
+        dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[st % PF][1], vf[t], dp[qh], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (st + PF < NST) {
+          const int s2 = st + PF;
+          ra[st % PF][0] = lds_load<bf16x8>(la.ka[s2 % KT] + QOFF + (s2 / KT) * 32 * ROW);
+          ra[st % PF][1] = lds_load<bf16x8>(la.ka[s2 % KT] + DOFF + (s2 / KT) * 32 * ROW);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
       }
     }
     // P = exp2(s * scale*log2e - LSE*log2e), dS = P (dP - D); row of register r:
