@@ -93,10 +93,13 @@ def cpu_baseline(w, causal: bool, q, k, v):
         oracle.attention_rows_bf16(*bits, rows, causal, w.scale)
         return time.perf_counter() - t0
 
-    probe = min(total_rows, 2048)
-    per_row = max(run(probe) / probe, 1e-7)
-    n_rows = int(min(total_rows, max(probe, 15.0 / per_row)))
+    # grow the sample until one run takes about 10-30 s (a small sample over-states the cost
+    # per row: each thread converts the K/V heads its rows touch)
+    n_rows = min(total_rows, 2048)
     dt = run(n_rows)
+    while dt < 10.0 and n_rows < total_rows:
+        n_rows = int(min(total_rows, n_rows * min(8.0, 15.0 / max(dt, 1e-3))))
+        dt = run(n_rows)
     return {"value": n_rows * flop_row / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"{n_rows} random query rows (all heads) of {w.name}, "
@@ -156,15 +159,19 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event between consecutive launches: the mean is first-to-last, and the
+    # per-launch times give the median and minimum
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t_wall = time.perf_counter()
-    start.record()
-    for _ in range(args.steps):
+    events[0].record()
+    for i in range(args.steps):
         step()
-    stop.record()
+        events[i + 1].record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms = start.elapsed_time(stop) / args.steps
+    ms = events[0].elapsed_time(events[-1]) / args.steps
+    per_launch = sorted(events[i].elapsed_time(events[i + 1]) for i in range(args.steps))
+    ms_median, ms_min = per_launch[len(per_launch) // 2], per_launch[0]
     flop = w.flop(causal)
     tflops = flop / (ms * 1e-3) / 1e12
     assert torch.isfinite(lse).all().item(), "non-finite LSE"
@@ -179,7 +186,8 @@ def main():
         alg_bytes = w.io_bytes()
     result = {
         "metric": METRIC_FP8 if args.fp8 else METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(ms_median, 4), "ms_per_step_min": round(ms_min, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3" if args.fp8 else "bf16", "data": "synthetic",
         "config": {"workload": f"{w.name}_noncausal", "B": w.B, "H": w.H, "N_q": w.n_q, "N_k": w.n_k, "d": w.d,
                    "causal": False, "scale": w.scale, "inputs": "iid N(0,1) fp32 -> bf16 RNE, seeded"},
