@@ -326,8 +326,8 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
         float* ws = p.ws_dq + ((long long)kb * R + hq + row) * D + 32 * cb + 4 * hf;
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-          *reinterpret_cast<f32x4*>(ws + 8 * g) =
-              f32x4{dqt[4 * g], dqt[4 * g + 1], dqt[4 * g + 2], dqt[4 * g + 3]};
+          __builtin_nontemporal_store(f32x4{dqt[4 * g], dqt[4 * g + 1], dqt[4 * g + 2], dqt[4 * g + 3]},
+                                      reinterpret_cast<f32x4*>(ws + 8 * g));
       }
     }
   };
@@ -385,7 +385,10 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
   // query block qi was processed by key blocks kb with kb*128 <= qi*64 + 63 (causal)
   const int kb_end = p.causal ? min(n_kb, (i / kBQ * kBQ + kBQ - 1) / kBK + 1) : n_kb;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int kb = 0; kb < kb_end; ++kb) acc += *reinterpret_cast<const f32x4*>(p.ws_dq + (long long)kb * R * D + idx);
+  // the partials are written once and read once: non-temporal on both sides
+#pragma unroll 4
+  for (int kb = 0; kb < kb_end; ++kb)
+    acc += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.ws_dq + (long long)kb * R * D + idx));
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   *reinterpret_cast<u32x2*>(p.dq + idx) = __builtin_bit_cast(u32x2, __builtin_convertvector(acc * p.scale, bf16x4));
 }
