@@ -121,7 +121,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the attention forward "
-              f"shards over heads with no exchange; see DESIGN.md)", file=sys.stderr)
+              f"shards over heads with no exchange, so the one-GPU figure is the per-GPU throughput)",
+              file=sys.stderr)
         sys.exit(2)
 
     import exact_attention_85_amd as fa2
