@@ -309,7 +309,19 @@ def main():
         extra.append({"workload": wd.name.replace("_s16", "_auto"), "num_splits": s_auto, "causal": False,
                       "ms": round(msa, 4), "GB/s": round(gba, 1), "frac_of_hbm_peak": round(gba / PEAK_HBM_GBS, 4)})
         log(f"decode with fa2_num_splits -> {s_auto}: {msa:.3f} ms, {gba:.0f} GB/s")
-        del qd, kd, vd, od, ld, ws
+        # the same decode over an FP8 K/V cache (codes quantised per head before the timed region)
+        qc8, dq8 = fa2.quantize_fp8(qd)
+        kc8, dk8 = fa2.quantize_fp8(kd)
+        vc8, dv8 = fa2.quantize_fp8(vd)
+        ms8 = time_launches(lambda: fa2.decode_fp8(qc8, kc8, vc8, dq8, dk8, dv8, scale=wd.scale, out=od, lse=ld),
+                            steps_x, args.warmup)
+        bytes8 = wd.B * wd.H * (2 * wd.n_k * wd.d + wd.d + 2 * wd.d + 4)  # K, V and Q codes in; O, LSE out
+        gb8 = bytes8 / (ms8 * 1e-3) / 1e9
+        extra.append({"workload": wd.name.replace("_s16", "_fp8"), "dtype": "fp8_e4m3", "causal": False,
+                      "ms": round(ms8, 4), "GB/s": round(gb8, 1), "frac_of_hbm_peak": round(gb8 / PEAK_HBM_GBS, 4),
+                      "algorithmic_bytes": bytes8, "speedup_vs_bf16_decode": round(msa / ms8, 3)})
+        log(f"decode over FP8 K/V: {ms8:.3f} ms, {gb8:.0f} GB/s, {msa / ms8:.2f}x the bf16 decode")
+        del qd, kd, vd, od, ld, ws, qc8, kc8, vc8
         result["workloads"] = extra
 
     if not args.no_cpu and not args.fp8:  # the oracle baseline is the bf16 definition

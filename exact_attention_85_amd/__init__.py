@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     attention,
     backward,
     bwd_workspace_bytes,
+    decode_fp8,
     forward,
     forward_fp8,
     forward_splitkv,

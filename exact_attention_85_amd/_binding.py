@@ -59,6 +59,8 @@ def load_library():
     lib.fa2_quantize_fp8.restype = i
     lib.fa2_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     lib.fa2_fwd_fp8.restype = i
+    lib.fa2_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, vp]
+    lib.fa2_decode_fp8.restype = i
     lib.fa2_status_string.argtypes = [i]
     lib.fa2_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -268,5 +270,34 @@ def forward_fp8(qc, kc, vt, descale_q, descale_k, descale_v, causal: bool = Fals
     rc = lib.fa2_fwd_fp8(qc.data_ptr(), kc.data_ptr(), vt.data_ptr(), descale_q.data_ptr(), descale_k.data_ptr(),
                          descale_v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, n_q, n_k, d,
                          int(bool(causal)), _scale(scale, d), _stream_handle(qc.device))
+    _check(rc)
+    return out, lse
+
+
+def decode_fp8(qc, kc, vc, descale_q, descale_k, descale_v, scale=None, out=None, lse=None):
+    """One decode step over an FP8 K/V cache via fa2_decode_fp8.
+
+    qc [B, H, 1, d], kc and vc [B, H, N_k, d] uint8 codes in row layout; descales fp32 [B, H].
+    Returns (o bf16 [B, H, 1, d], lse fp32 [B, H, 1])."""
+    lib = load_library()
+    for name, t in (("qc", qc), ("kc", kc), ("vc", vc)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or t.device.type != "cuda":
+            raise TypeError(f"{name} must be a uint8 tensor on the GPU")
+        if t.dim() != 4 or not t.is_contiguous() or t.device != qc.device:
+            raise ValueError(f"{name} must be a contiguous 4-d tensor on qc's device")
+    B, H, n_q, d = qc.shape
+    n_k = kc.shape[2]
+    if n_q != 1 or tuple(kc.shape) != (B, H, n_k, d) or tuple(vc.shape) != (B, H, n_k, d):
+        raise ValueError("qc must be [B, H, 1, d] and kc, vc [B, H, N_k, d]")
+    for name, t in (("descale_q", descale_q), ("descale_k", descale_k), ("descale_v", descale_v)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, H) or not t.is_contiguous() or t.device != qc.device:
+            raise ValueError(f"{name} must be a contiguous fp32 [B, H] tensor on qc's device")
+    if out is None:
+        out = torch.empty((B, H, 1, d), dtype=torch.bfloat16, device=qc.device)
+    if lse is None:
+        lse = torch.empty((B, H, 1), dtype=torch.float32, device=qc.device)
+    rc = lib.fa2_decode_fp8(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), descale_q.data_ptr(),
+                            descale_k.data_ptr(), descale_v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            B, H, n_k, d, _scale(scale, d), _stream_handle(qc.device))
     _check(rc)
     return out, lse

@@ -296,6 +296,43 @@ int fa2_fwd_fp8(const void* Qc, const void* Kc, const void* Vt, const float* des
   return FA2_OK;
 }
 
+int fa2_decode_fp8(const void* Qc, const void* Kc, const void* Vc, const float* descale_q, const float* descale_k,
+                   const float* descale_v, void* O, float* LSE, int B, int H, int N_k, int d, float scale,
+                   void* stream) {
+  if (!descale_q || !descale_k || !descale_v) return FA2_ERR_NULLPTR;
+  int rc = check_common(Qc, Kc, Vc, O, LSE, B, H, 1, N_k, d, scale);
+  if (rc != FA2_OK) return rc;
+  const void* ptrs[8] = {Qc, Kc, Vc, descale_q, descale_k, descale_v, O, LSE};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return FA2_ERR_ALIGN;
+  const long long bh = (long long)B * H;
+  const Range in[6] = {range_of(Qc, bh * d), range_of(Kc, bh * N_k * d), range_of(Vc, bh * N_k * d),
+                       range_of(descale_q, bh * 4), range_of(descale_k, bh * 4), range_of(descale_v, bh * 4)};
+  const Range o = range_of(O, bh * d * 2), l = range_of(LSE, bh * 4);
+  if (overlap(o, l)) return FA2_ERR_ALIAS;
+  for (const Range& r : in)
+    if (overlap(o, r) || overlap(l, r)) return FA2_ERR_ALIAS;
+  fa2::Fp8Params p{};
+  p.q = static_cast<const uint8_t*>(Qc);
+  p.k = static_cast<const uint8_t*>(Kc);
+  p.v = static_cast<const uint8_t*>(Vc);
+  p.dsq = descale_q;
+  p.dsk = descale_k;
+  p.dsv = descale_v;
+  p.o = static_cast<uint16_t*>(O);
+  p.lse = LSE;
+  p.B = B;
+  p.H = H;
+  p.n_q = 1;
+  p.n_k = N_k;
+  p.d = d;
+  p.wl = -1;
+  p.wr = -1;
+  p.scale = scale;
+  if (fa2::launch_decode_fp8(p, static_cast<hipStream_t>(stream)) != hipSuccess) return FA2_ERR_HIP;
+  return FA2_OK;
+}
+
 const char* fa2_status_string(int status) {
   switch (status) {
     case FA2_OK: return "FA2_OK: success";

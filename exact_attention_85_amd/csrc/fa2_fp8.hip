@@ -357,6 +357,148 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_fp8_kernel(Fp8Params p) {
 }
 
 // ---------------------------------------------------------------------------
+// Single-query decode over an FP8 K/V cache: one workgroup (4 waves) per
+// (batch, head) streams the head's K and V codes (both in row layout) from HBM.
+// With one query row both products are matrix-vector shaped, so the kernel
+// uses VALU dot products in fp32 on the decoded codes, like the bf16 decode
+// kernel: D/16 lanes share one key row (16 codes each), every lane keeps
+// kDec8U keys' K and V loads in flight, each wave runs its own online softmax
+// over the steps it owns, and the four wave partials are merged at the end.
+// The probabilities stay fp32 (only the inputs are 8-bit).
+constexpr int kDec8Threads = 256;
+constexpr int kDec8U = 16;
+constexpr int kNt = 2;  // buffer-load cache policy: non-temporal (each code is read once)
+
+__device__ __forceinline__ void decode16(u32x4 w, float (&f)[16]) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned wi = w[i];  // named copy: bit-casting a vector element in place reads element 0
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wi, false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wi, true);
+    f[4 * i] = lo.x;
+    f[4 * i + 1] = lo.y;
+    f[4 * i + 2] = hi.x;
+    f[4 * i + 3] = hi.y;
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kDec8Threads) decode_fp8_kernel(Fp8Params p) {
+  constexpr int LPK = D / 16;          // lanes per key row
+  constexpr int KPW = 64 / LPK;        // key rows per wave-wide load
+  constexpr int STEP = KPW * kDec8U;   // keys per wave step
+  constexpr int NWAVE = kDec8Threads / 64;
+  __shared__ float part_acc[NWAVE][D];
+  __shared__ float part_m[NWAVE], part_l[NWAVE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sub = lane % LPK, kg = lane / LPK;
+  const int bh = xcd_remap(blockIdx.x, gridDim.x);
+  const int kend = p.n_k;
+
+  const float sl2 = fmaxf(fabsf(p.scale) * kLog2e * p.dsq[bh] * p.dsk[bh], FLT_MIN);
+  const float dsv = p.dsv[bh];
+  // loads past key kend return zero (range check on the per-lane offset)
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + (long long)bh * p.n_k * D, (long long)kend * D);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + (long long)bh * p.n_k * D, (long long)kend * D);
+
+  float qv[16];
+  decode16(*reinterpret_cast<const u32x4*>(p.q + (long long)bh * D + sub * 16), qv);
+  if (p.scale < 0.f) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) qv[e] = -qv[e];  // keep the folded multiplier positive
+  }
+
+  float acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  float m_run = -INFINITY;  // log2 units, uniform over the wave
+  float l_run = 0.f;        // this key group's share
+
+  for (int k0 = wave * STEP; k0 < kend; k0 += NWAVE * STEP) {
+    u32x4 kr[kDec8U], vr[kDec8U];
+#pragma unroll
+    for (int u = 0; u < kDec8U; ++u) {
+      const unsigned off = (unsigned)((k0 + u * KPW + kg) * D + sub * 16);
+      kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, kNt));
+      vr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, kNt));
+    }
+    float sc[kDec8U];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kDec8U; ++u) {
+      float kf[16];
+      decode16(kr[u], kf);
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dot = __builtin_fmaf(qv[e], kf[e], dot);
+#pragma unroll
+      for (int x = LPK / 2; x >= 1; x >>= 1) dot += __shfl_xor(dot, x);
+      sc[u] = (k0 + u * KPW + kg < kend) ? dot * sl2 : -INFINITY;
+      mloc = fmaxf(mloc, sc[u]);
+    }
+#pragma unroll
+    for (int x = LPK; x < 64; x <<= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, x));
+    const float m_new = fmaxf(m_run, mloc);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int u = 0; u < kDec8U; ++u) {
+      const float pk = __builtin_amdgcn_exp2f(sc[u] - m_use);
+      ps += pk;
+      float vf[16];
+      decode16(vr[u], vf);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = __builtin_fmaf(pk, vf[e], acc[e]);
+    }
+    l_run = l_run * alpha + ps;
+  }
+
+  // fold the key groups of the wave (lanes with equal `sub`)
+#pragma unroll
+  for (int x = LPK; x < 64; x <<= 1) {
+    l_run += __shfl_xor(l_run, x);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] += __shfl_xor(acc[e], x);
+  }
+  if (kg == 0) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) part_acc[wave][sub * 16 + e] = acc[e];
+  }
+  if (lane == 0) {
+    part_m[wave] = m_run;
+    part_l[wave] = l_run;
+  }
+  __syncthreads();
+
+  // merge the wave partials (log2 units); the single query row sees key 0, so lsum > 0
+  float M = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < NWAVE; ++v) M = fmaxf(M, part_m[v]);
+  float wgt[NWAVE];
+  float lsum = 0.f;
+#pragma unroll
+  for (int v = 0; v < NWAVE; ++v) {
+    wgt[v] = part_m[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(part_m[v] - M);
+    lsum += wgt[v] * part_l[v];
+  }
+  const float inv = dsv / lsum;
+  for (int dd = tid; dd < D; dd += kDec8Threads) {
+    float t = 0.f;
+#pragma unroll
+    for (int v = 0; v < NWAVE; ++v) t += wgt[v] * part_acc[v][dd];
+    p.o[(long long)bh * D + dd] = __builtin_bit_cast(uint16_t, (__bf16)(t * inv));
+  }
+  if (tid == 0) p.lse[bh] = (M + __log2f(lsum)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
 // Quantiser.  Four launches on the caller's stream:
 //   clear     amax[bh] = 0 (the descale array holds amax bit patterns until the end)
 //   amax      per-workgroup max |x| of a chunk, folded in with an atomic max on the
@@ -486,6 +628,15 @@ hipError_t launch_fwd_fp8(const Fp8Params& p, hipStream_t stream) {
     hipLaunchKernelGGL((fwd_fp8_kernel<128, NW>), grid, dim3(64 * NW), 0, stream, p);
   else
     hipLaunchKernelGGL((fwd_fp8_kernel<64, NW>), grid, dim3(64 * NW), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_fp8(const Fp8Params& p, hipStream_t stream) {
+  const dim3 grid((unsigned)((long long)p.B * p.H));
+  if (p.d == 128)
+    hipLaunchKernelGGL(decode_fp8_kernel<128>, grid, dim3(kDec8Threads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(decode_fp8_kernel<64>, grid, dim3(kDec8Threads), 0, stream, p);
   return hipGetLastError();
 }
 

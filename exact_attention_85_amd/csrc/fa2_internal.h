@@ -53,7 +53,8 @@ struct BwdParams {
 struct Fp8Params {
   const uint8_t* q;
   const uint8_t* k;
-  const uint8_t* vt;
+  const uint8_t* vt;  // forward: V transposed [B][H][d][vt_stride]
+  const uint8_t* v;   // decode: V in row layout [B][H][N_k][d]
   const float* dsq;
   const float* dsk;
   const float* dsv;
@@ -87,5 +88,6 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 // FP8 forward and the quantiser that prepares its inputs.
 hipError_t launch_fwd_fp8(const Fp8Params& p, hipStream_t stream);
 hipError_t launch_quantize_fp8(const QuantParams& p, hipStream_t stream);
+hipError_t launch_decode_fp8(const Fp8Params& p, hipStream_t stream);
 
 }  // namespace fa2

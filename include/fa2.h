@@ -273,6 +273,23 @@ int fa2_fwd_fp8(const void* Qc, const void* Kc, const void* Vt, const float* des
                 const float* descale_k, const float* descale_v, void* O, float* LSE, int B, int H,
                 int N_q, int N_k, int d, int causal, float scale, void* stream);
 
+/*
+ * fa2_decode_fp8 — one decode step (a single query row per head) over an FP8
+ * K/V cache (the walkthrough page, "launch grid" section, and the synthesis
+ * page, section 5 item 5, single-query decode; FP8 inputs as above).
+ *
+ * Qc [B][H][1][d], Kc and Vc [B][H][N_k][d] e4m3 codes, all in row layout
+ * (fa2_quantize_fp8 with transposed == 0 writes them); descales fp32 [B][H],
+ * positive and finite.  O bf16 [B][H][1][d], LSE fp32 [B][H][1].  Every key
+ * is visible.  One workgroup per (batch, head) streams that head's codes once;
+ * the codes are decoded to fp32 in registers and the probabilities stay fp32,
+ * so only the inputs are 8-bit.  Pointers 16-byte aligned; O and LSE must not
+ * overlap any input or each other; the remaining errors as fa2_fwd.
+ */
+int fa2_decode_fp8(const void* Qc, const void* Kc, const void* Vc, const float* descale_q,
+                   const float* descale_k, const float* descale_v, void* O, float* LSE, int B, int H,
+                   int N_k, int d, float scale, void* stream);
+
 /* fa2_status_string — static, human-readable text for a status code. */
 const char* fa2_status_string(int status);
 

@@ -23,7 +23,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_fp8_vt_stride", "fa2_fwd",
+    assert declared_functions() == ["fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_decode_fp8", "fa2_fp8_vt_stride", "fa2_fwd",
                                     "fa2_fwd_fp8", "fa2_fwd_splitkv", "fa2_fwd_window", "fa2_num_splits",
                                     "fa2_quantize_fp8", "fa2_splitkv_workspace_bytes", "fa2_status_string"]
 
@@ -258,3 +258,18 @@ def test_fp8_alias():
     assert fwd8(o=V + 64 * 256 * 2 - 16) == ALIAS
     assert fwd8(l=SK) == ALIAS
     assert fwd8(o=L) == ALIAS
+
+
+def dec8(q=Q, k=K, v=V, dq=SQ, dk=SK, dv=SV, o=O, l=L, B=2, H=3, nk=500, d=128, scale=0.1):
+    return fa2.load_library().fa2_decode_fp8(q, k, v, dq, dk, dv, o, l, B, H, nk, d, scale, None)
+
+
+def test_decode_fp8_validation():
+    for name in ("q", "k", "v", "dq", "dk", "dv", "o", "l"):
+        assert dec8(**{name: None}) == NULLPTR, name
+    assert dec8(nk=0) == BAD_SHAPE and dec8(B=0) == BAD_SHAPE
+    assert dec8(d=96) == HEAD_DIM
+    assert dec8(scale=float("inf")) == BAD_SCALE
+    assert dec8(v=V + 4) == ALIGN
+    assert dec8(o=K + 64) == ALIAS
+    assert dec8(l=SV) == ALIAS

@@ -185,3 +185,49 @@ def test_fwd_fp8_full_size_sampled(w, causal):
     q, k, v = workloads.make_qkv(w, DEV)
     rows = gu.sample_rows(w.B, w.H, w.n_q, 48, seed=w.index * 10 + int(causal) + 500)
     _end_to_end(q, k, v, causal, w.scale, rows, f"{w.name} causal={causal}")
+
+
+# ---------------------------------------------------------------- FP8 decode (one query row)
+# The probabilities stay fp32 here, so the bf16 path's tolerance applies: |dO| <= 1e-2 plus half a bf16
+# ulp of the reference (outputs reach |O| > 4 with these codes) and |dLSE| <= 1e-3.
+DECODE_SHAPES = [(2, 3, 1, 64), (2, 3, 17, 128), (1, 4, 1000, 64), (3, 2, 4097, 128), (2, 2, 300, 128),
+                 (1, 1, 8192, 128)]
+
+
+@pytest.mark.parametrize("shape", DECODE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("scale", [0.09, -0.3])
+def test_decode_fp8_parity(shape, scale):
+    B, H, n_k, d = shape
+    print(f"case fp8 decode shape={shape} scale={scale}", flush=True)
+    qc, kc, vc, dq, dk, dv = _codes_case(B, H, 1, n_k, d, seed=n_k + d + B)
+    o, lse = fa2.decode_fp8(_dev(qc), _dev(kc), _dev(vc), _dev(dq), _dev(dk), _dev(dv), scale=scale)
+    torch.cuda.synchronize()
+    rows = np.arange(B * H, dtype=np.int64)
+    o_ref, lse_ref = oracle.attention_fp8_rows(qc, kc, vc, dq, dk, dv, rows, False, scale)
+    gu.assert_close(o.float().reshape(B * H, d).cpu().double().numpy(), lse.reshape(-1).cpu().double().numpy(),
+                    o_ref, lse_ref, what=f"fp8 decode {shape} scale={scale}", out_grid=True)
+
+
+def test_decode_fp8_full_size_sampled():
+    """The decode workload's shape (B64 H32 N_k 8192 d128), bf16 inputs quantised on both sides."""
+    w = workloads.C5
+    print(f"case fp8 decode {w.name}", flush=True)
+    q, k, v = workloads.make_qkv(w, DEV)
+    qc, dq = fa2.quantize_fp8(q)
+    kc, dk = fa2.quantize_fp8(k)
+    vc, dv = fa2.quantize_fp8(v)
+    o, lse = fa2.decode_fp8(qc, kc, vc, dq, dk, dv, scale=w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(55)
+    heads = sorted(set(map(tuple, rng.integers(0, [w.B, w.H], (24, 2)).tolist())) | {(0, 0), (w.B - 1, w.H - 1)})
+    o_ref = np.empty((len(heads), w.d))
+    lse_ref = np.empty(len(heads))
+    for n, (b, h) in enumerate(heads):
+        codes = [oracle.quantize_fp8(workloads.bf16_bits(t[b, h][None, None])) for t in (q, k, v)]
+        orow, lrow = oracle.attention_fp8_rows(codes[0][0], codes[1][0], codes[2][0], codes[0][1], codes[1][1],
+                                               codes[2][1], np.array([0]), False, w.scale)
+        o_ref[n], lse_ref[n] = orow[0], lrow[0]
+    idx = torch.tensor([b * w.H + h for b, h in heads], device=DEV)
+    og = o.float().reshape(w.B * w.H, w.d)[idx].cpu().double().numpy()
+    lg = lse.reshape(-1)[idx].cpu().double().numpy()
+    gu.assert_close(og, lg, o_ref, lse_ref, what="fp8 decode C5", out_grid=True)
