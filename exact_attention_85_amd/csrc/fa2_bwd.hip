@@ -147,7 +147,7 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + hk * D, (long long)p.n_k * D * 2);
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-      const unsigned off = (unsigned)((key * D + 16 * t + 8 * hf) * 2);
+      const unsigned off = ((unsigned)key * D + 16 * t + 8 * hf) * 2u;
       kf[t] = as_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0)));
       vf[t] = as_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0)));
     }
@@ -161,7 +161,7 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
       const int s = (i * 4 + wave) * 64 + lane;
       const int r = s / CPR;
       const int c = (s % CPR) ^ (swz<D>(r, 0) - r * CPR);
-      lds_dma16(krs, kblk + (i * 4 + wave) * 64 * 16, (unsigned)(((k0 + r) * D + c * 8) * 2));
+      lds_dma16(krs, kblk + (i * 4 + wave) * 64 * 16, ((unsigned)(k0 + r) * D + c * 8) * 2u);
     }
   }
 
