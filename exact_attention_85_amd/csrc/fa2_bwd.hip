@@ -211,6 +211,14 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
       lds_dma16(dvrs, reinterpret_cast<const char*>(&rowv[stage][1][0]) - 256, (unsigned)(r0 * 4 + (lane - 16) * 16));
   };
 
+  // K^T fragments of this wave's d columns for the dQ product: the key block is the
+  // same for every query block, so they are read from LDS once and kept in registers
+  bf16x8 kTr[kBK / 16];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // the key block is in LDS
+#pragma unroll
+  for (int ks = 0; ks < kBK / 16; ++ks) kTr[ks] = tr_pair(kba[0] + ks * 16 * ROW, kba[1] + ks * 16 * ROW);
+
   if (qb0 < n_qb) issue_q(0, qb0);
 
   // one query block; STG is the LDS stage (compile-time so that offsets are immediates)
@@ -317,8 +325,7 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
 #pragma unroll
       for (int ks = 0; ks < kBK / 16; ++ks) {
         const bf16x8 dsT = tr_pair(da[r][0] + ks * 16 * kBQ * 2, da[r][1] + ks * 16 * kBQ * 2);
-        const bf16x8 kT = tr_pair(kba[0] + ks * 16 * ROW, kba[1] + ks * 16 * ROW);
-        dqt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kT, dsT, dqt, 0, 0, 0);
+        dqt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kTr[ks], dsT, dqt, 0, 0, 0);
       }
       const long long R = (long long)p.B * p.H * p.n_q;
       const int row = i0 + 32 * (rb0 + r) + col;
