@@ -300,41 +300,77 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
         *reinterpret_cast<__attribute__((address_space(3))) u32x2*>((uintptr_t)addr) = w2;
       }
     }
-    // dV^T += dO^T P and dK^T += Q^T dS over the 64 rows (4 k-steps of 16)
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
+    // dV^T += dO^T P and dK^T += Q^T dS over the 64 rows (4 k-steps of 16), steps
+    // (qh, t, nb) in that order; the transposed operands are read PF steps ahead of
+    // their products (one LDS read outlasts the two products it feeds)
+    {
+      constexpr int NST = 4 * NB;
+      constexpr int PF = 3;
+      bf16x8 rdo[PF], rq[PF];
+      auto load = [&](int st) {
+        const int qh = st / (2 * NB), t = (st / NB) % 2, nb = st % NB;
         const unsigned roff = (32 * qh + 16 * t) * ROW;
+        rdo[st % PF] = tr_pair(la.va[2 * nb] + DOFF + roff, la.va[2 * nb + 1] + DOFF + roff);
+        rq[st % PF] = tr_pair(la.va[2 * nb] + QOFF + roff, la.va[2 * nb + 1] + QOFF + roff);
+      };
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const bf16x8 doT = tr_pair(la.va[2 * nb] + DOFF + roff, la.va[2 * nb + 1] + DOFF + roff);
-          const bf16x8 qT = tr_pair(la.va[2 * nb] + QOFF + roff, la.va[2 * nb + 1] + QOFF + roff);
-          dvt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doT, pb[qh][t], dvt[nb], 0, 0, 0);
-          dkt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT, db[qh][t], dkt[nb], 0, 0, 0);
+      for (int st = 0; st < PF; ++st) load(st);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * PF, 0);
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int qh = st / (2 * NB), t = (st / NB) % 2, nb = st % NB;
+        dvt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rdo[st % PF], pb[qh][t], dvt[nb], 0, 0, 0);
+        dkt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq[st % PF], db[qh][t], dkt[nb], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (st + PF < NST) {
+          load(st + PF);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
         }
       }
+    }
     // every wave's dS^T is in LDS
     __syncthreads();
     // dQ contribution of this key block, computed transposed (dQ^T = K^T dS^T)
     // so that each lane holds one query row and 4 consecutive d per register
     // group: rows 32(rb0 + r) + lane%32, d columns 32cb + 8g + 4hf + 0..3
+    // Steps (ks, r): consecutive products accumulate into different row groups, and
+    // the dS^T operands are read PF steps ahead.
+    {
+      constexpr int NST = (kBK / 16) * RB;
+      constexpr int PF = 3;
+      f32x16 dqt[RB];
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      f32x16 dqt = f32x16{};
+      for (int r = 0; r < RB; ++r) dqt[r] = f32x16{};
+      bf16x8 rds[PF];
+      auto load = [&](int st) {
+        const int ks = st / RB, r = st % RB;
+        rds[st % PF] = tr_pair(da[r][0] + ks * 16 * kBQ * 2, da[r][1] + ks * 16 * kBQ * 2);
+      };
 #pragma unroll
-      for (int ks = 0; ks < kBK / 16; ++ks) {
-        const bf16x8 dsT = tr_pair(da[r][0] + ks * 16 * kBQ * 2, da[r][1] + ks * 16 * kBQ * 2);
-        dqt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kTr[ks], dsT, dqt, 0, 0, 0);
+      for (int st = 0; st < PF; ++st) load(st);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int ks = st / RB, r = st % RB;
+        dqt[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kTr[ks], rds[st % PF], dqt[r], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (st + PF < NST) {
+          load(st + PF);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
       }
       const long long R = (long long)p.B * p.H * p.n_q;
-      const int row = i0 + 32 * (rb0 + r) + col;
-      if (row < p.n_q) {
-        float* ws = p.ws_dq + ((long long)kb * R + hq + row) * D + 32 * cb + 4 * hf;
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          __builtin_nontemporal_store(f32x4{dqt[4 * g], dqt[4 * g + 1], dqt[4 * g + 2], dqt[4 * g + 3]},
-                                      reinterpret_cast<f32x4*>(ws + 8 * g));
+      for (int r = 0; r < RB; ++r) {
+        const int row = i0 + 32 * (rb0 + r) + col;
+        if (row < p.n_q) {
+          float* ws = p.ws_dq + ((long long)kb * R + hq + row) * D + 32 * cb + 4 * hf;
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            __builtin_nontemporal_store(
+                f32x4{dqt[r][4 * g], dqt[r][4 * g + 1], dqt[r][4 * g + 2], dqt[r][4 * g + 3]},
+                reinterpret_cast<f32x4*>(ws + 8 * g));
+        }
       }
     }
   };
