@@ -18,7 +18,10 @@ from ._binding import (  # noqa: F401
     forward_window,
     fp8_vt_stride,
     lib_path,
+    library_at,
     load_library,
+    open_library,
+    poison_lib_path,
     num_splits,
     quantize_fp8,
     splitkv_workspace_bytes,

@@ -4,6 +4,7 @@ Argument marshalling only: dtype/device/contiguity checks, output and
 workspace allocation with torch, and the raw stream handle.  Every step of the
 attention computation runs in the library's kernels.
 """
+import contextlib
 import ctypes
 import math
 import os
@@ -12,6 +13,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa2.so")
+# the race-check build (LDS slots filled with NaN before each asynchronous load)
+_POISON_LIB_PATH = os.path.join(_PKG, "libfa2_poison.so")
 FA2_MAX_SPLITS = 256
 
 _lib = None
@@ -29,15 +32,38 @@ def lib_path() -> str:
     return _LIB_PATH
 
 
+def poison_lib_path() -> str:
+    return _POISON_LIB_PATH
+
+
 def load_library():
     """Loads libfa2.so (built by __graft_entry__.build() or exact_attention_85_amd/build.py).
     Raises if it is missing: there is no fallback path."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
-        raise RuntimeError(f"{_LIB_PATH} is not built; run exact_attention_85_amd/build.py first")
-    lib = ctypes.CDLL(_LIB_PATH)
+    _lib = open_library(_LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def library_at(path: str):
+    """Routes this module's calls to the build at `path` (such as the race-check
+    build) inside the block; the default library is used again afterwards."""
+    global _lib
+    saved = load_library()
+    _lib = open_library(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
+
+
+def open_library(path: str):
+    """A handle on the build at `path` with the C signatures of include/fa2.h declared."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run exact_attention_85_amd/build.py first")
+    lib = ctypes.CDLL(path)
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     lib.fa2_fwd.restype = i
@@ -63,7 +89,6 @@ def load_library():
     lib.fa2_decode_fp8.restype = i
     lib.fa2_status_string.argtypes = [i]
     lib.fa2_status_string.restype = ctypes.c_char_p
-    _lib = lib
     return lib
 
 

@@ -7,6 +7,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa2.so")
+# race-check build: every LDS slot is filled with NaN before its asynchronous load
+POISON_LIB = os.path.join(PKG, "libfa2_poison.so")
 SOURCES = [os.path.join(CSRC, n) for n in ("fa2_fwd.hip", "fa2_bwd.hip", "fa2_fp8.hip", "fa2_api.cpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -19,8 +21,10 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    cmd = [HIPCC] + FLAGS + list(extra_flags) + SOURCES + ["-o", LIB + ".tmp"]
+def build(verbose: bool = False, extra_flags=(), poison: bool = False) -> str:
+    lib = POISON_LIB if poison else LIB
+    extra = list(extra_flags) + (["-DFA2_POISON_LDS"] if poison else [])
+    cmd = [HIPCC] + FLAGS + extra + SOURCES + ["-o", lib + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
@@ -31,9 +35,11 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True, extra_flags=[a for a in sys.argv[1:] if a.startswith("-")])
+    args = sys.argv[1:]
+    build(verbose=True, extra_flags=[a for a in args if a.startswith("-") and a != "--poison"],
+          poison="--poison" in args)

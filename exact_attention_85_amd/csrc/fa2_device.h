@@ -84,8 +84,19 @@ __device__ __forceinline__ i32x4 raw_rsrc(const void* base, long long bytes) {
 // order later LDS reads of the other stage behind it; the kernel waits for
 // these loads itself (s_waitcnt vmcnt(0) before the barrier that publishes a
 // tile).
+//
+// Built with FA2_POISON_LDS (the race-check build), each lane first fills its
+// 16 destination bytes with 0x7fff7fff, a NaN as bf16, fp32 and e4m3 alike, and
+// waits for that store.  A read of the slot that is not ordered after the load's
+// wait and barrier then sees NaN (or the load's data where an overwrite races a
+// reader), so a missing wait or barrier shows up as NaN or as a changed result.
 __device__ __forceinline__ void lds_dma16(i32x4 rs, const char* dst, unsigned voff) {
   const unsigned m0v = (unsigned)(uintptr_t)(const lds_void*)dst;
+#ifdef FA2_POISON_LDS
+  *reinterpret_cast<__attribute__((address_space(3))) u32x4*>((uintptr_t)(m0v + 16u * (threadIdx.x & 63u))) =
+      u32x4{0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu};
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#endif
   unsigned saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
