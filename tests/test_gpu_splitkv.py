@@ -30,15 +30,28 @@ def _partials(ws, S, R, d):
                                      (130, 300, 4), (64, 64, 64), (257, 1000, 3)])
 def test_splitkv_parity_and_partials(nq, nk, S, causal, d):
     print(f"case splitkv nq={nq} nk={nk} S={S} d={d} causal={causal}", flush=True)
+    _check_splitkv(2, 3, nq, nk, S, causal, d, nq * 131 + nk + S)
+
+
+# thousands of single-query chunks at once: ragged chunk lengths, an empty last
+# chunk, and under the causal mask every chunk but the first empty
+@pytest.mark.parametrize("B,H,nk,S,d,causal", [(64, 32, 1000, 5, 128, False), (64, 32, 1000, 5, 128, True),
+                                               (64, 32, 9, 4, 64, False), (128, 16, 333, 4, 64, False)])
+def test_splitkv_decode_many_chunks(B, H, nk, S, d, causal):
+    print(f"case splitkv decode many chunks B={B} H={H} nk={nk} S={S} d={d} causal={causal}", flush=True)
+    _check_splitkv(B, H, 1, nk, S, causal, d, B * 7 + nk + S)
+
+
+def _check_splitkv(B, H, nq, nk, S, causal, d, seed):
     scale = 1.0 / math.sqrt(d)
-    q, k, v = workloads.make_qkv_shape(2, 3, nq, nk, d, nq * 131 + nk + S, DEV)
+    q, k, v = workloads.make_qkv_shape(B, H, nq, nk, d, seed, DEV)
     o, lse, ws = fa2.forward_splitkv(q, k, v, num_splits=S, causal=causal, scale=scale)
     torch.cuda.synchronize()
     o_ref, lse_ref = gu.oracle_full(q, k, v, causal, scale)
     gu.assert_close(o.float().cpu().double().numpy(), lse.cpu().double().numpy(), o_ref, lse_ref,
                     what="merged", out_grid=True)
     # per-chunk partials: compare the chunk's normalised output and its log-sum-exp
-    R = 2 * 3 * nq
+    R = B * H * nq
     acc, m, l_, l_lse = (t.cpu().double().numpy() for t in _partials(ws, S, R, d))
     qd, kd, vd = (workloads.bf16_to_f64(t) for t in (q, k, v))
     L = -(-nk // S)
