@@ -37,7 +37,7 @@ def poison_lib_path() -> str:
 
 
 def load_library():
-    """Loads libfa2.so (built by __graft_entry__.build() or exact_attention_85_amd/build.py).
+    """Loads libfa2.so (built by exact_attention_85_amd/build.py).
     Raises if it is missing: there is no fallback path."""
     global _lib
     if _lib is not None:
