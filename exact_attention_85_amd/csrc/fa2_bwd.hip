@@ -14,14 +14,19 @@
 //
 // Three launches:
 //   bwd_prep_kernel    D_i and LSE_i * log2(e) for every query row
-//   bwd_kv_kernel      one workgroup per 128-key block (one wave per 32 keys):
-//                      streams 64-row query blocks through LDS and runs the
-//                      five products on the matrix cores; dK and dV stay in
-//                      registers, and the block's dQ contribution for each
-//                      query block is written to the workspace
-//   bwd_dq_kernel      dQ_i = scale * sum over key blocks, in block order
-// No atomics: every output element is written by exactly one thread, and the
-// dQ sum runs in a fixed order, so the result is bit-reproducible.
+//   bwd_kv_kernel      one workgroup per pair of 128-key blocks, taken one
+//                      after the other (one wave per 32 keys): streams 64-row
+//                      query blocks through LDS and runs the five products on
+//                      the matrix cores; dK and dV stay in registers.  The
+//                      pair shares one workspace slot for its dQ contribution:
+//                      the first block stores it, and for the second block
+//                      each thread's dQ accumulators start from the values it
+//                      stored itself, so the slot ends up holding the pair's
+//                      sum and the reduction reads half as many partials
+//   bwd_dq_kernel      dQ_i = scale * sum over the slots, in slot order
+// No atomics: every output element is written by exactly one thread (a slot
+// value twice, by the same thread, in program order), and the dQ sum runs in a
+// fixed order, so the result is bit-reproducible.
 //
 // Within a wave the scores are computed as S = Q K^T (query rows x 32 keys),
 // so every lane owns one key column: P and dS in accumulator layout are then
@@ -38,8 +43,10 @@
 namespace fa2 {
 namespace {
 
-constexpr int kBK = 128;  // keys per workgroup
+constexpr int kBK = 128;  // keys per block (a workgroup takes two)
 constexpr int kBQ = 64;   // query rows per step
+// s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt fields at their maxima)
+constexpr int kWaitVm0 = 0x0F70;
 
 // ---------------------------------------------------------------------------
 // D_i = sum_c dO_ic O_ic and LSE_i * log2(e).  D/8 lanes per row.
@@ -123,22 +130,61 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
   const int hf = lane >> 5;
   const int col = lane & 31;
 
+  // one workgroup per pair of key blocks (kb_a = n_kb-1-slot, then kb_b = slot; one block
+  // when they coincide), so that both add into one dQ partial slot
   const int n_kb = (p.n_k + kBK - 1) / kBK;
+  const int n_slot = (n_kb + 1) / 2;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = L / n_kb;
-  const int kb = L % n_kb;
-  const int k0 = kb * kBK;
-  const int kw0 = k0 + 32 * wave;     // this wave's keys kw0 .. kw0 + 31
-  const int key = kw0 + col;          // this lane's key column
+  const int bh = L / n_slot;
+  const int slot = L % n_slot;
+  const int kb_a = n_kb - 1 - slot;
   const int n_qb = (p.n_q + kBQ - 1) / kBQ;
-  // causal: rows below k0 see none of this block's keys
-  const int qb0 = p.causal ? min(k0 / kBQ, n_qb) : 0;
+  // causal: rows below a block's first key see none of its keys
+  const int qb0_a = p.causal ? min(kb_a * kBK / kBQ, n_qb) : 0;
 
   const long long hq = (long long)bh * p.n_q, hk = (long long)bh * p.n_k;
   const i32x4 qrs = raw_rsrc(p.q + hq * D, (long long)p.n_q * D * 2);
   const i32x4 dors = raw_rsrc(p.dout + hq * D, (long long)p.n_q * D * 2);
   const i32x4 l2rs = raw_rsrc(p.l2vec + hq, (long long)p.n_q * 4);
   const i32x4 dvrs = raw_rsrc(p.dvec + hq, (long long)p.n_q * 4);
+
+  LdsAddr<D> la;  // over qdo: ka = A operand of S / dP (rows x d), va = A operand of dV^T / dK^T
+  make_lds_addr<D>(la, (unsigned)(uintptr_t)(const lds_void*)&qdo[0][0][0], lane);
+
+  // dQ product: wave w computes rows 32rb .. +31 (rb over RB), d columns 32cb .. +31
+  constexpr int RB = D == 128 ? 2 : 1;
+  const int cb = D == 128 ? wave : (wave & 1);
+  const int rb0 = D == 128 ? 0 : (wave >> 1);
+  unsigned da[RB][2], kba[2];
+  {
+    const unsigned dsb = (unsigned)(uintptr_t)(const lds_void*)dst_t;
+    const unsigned kbb = (unsigned)(uintptr_t)(const lds_void*)kblk;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int r = 0; r < RB; ++r) da[r][h] = tr_nat_addr<kBQ>(dsb, lane, 0, 32 * (rb0 + r), h);
+      kba[h] = tr_nat_addr<D>(kbb, lane, 0, 32 * cb, h);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      asm volatile("" : "+v"(kba[h]));
+#pragma unroll
+      for (int r = 0; r < RB; ++r) asm volatile("" : "+v"(da[r][h]));
+    }
+  }
+  // this lane's dS^T store address: key row (key - k0), query rows 8g + 4hf (+32qh) in chunk 4qh + g
+  const unsigned dsw = (unsigned)(uintptr_t)(const lds_void*)dst_t;
+
+  for (int pass = 0; pass < (kb_a == slot ? 1 : 2); ++pass) {
+  const int kb = pass == 0 ? kb_a : slot;
+  const int k0 = kb * kBK;
+  const int kw0 = k0 + 32 * wave;     // this wave's keys kw0 .. kw0 + 31
+  const int key = kw0 + col;          // this lane's key column
+  const int qb0 = p.causal ? min(k0 / kBQ, n_qb) : 0;
+  // query blocks from qb_add on already hold the first pass's contribution in the slot
+  const int qb_add = pass == 0 ? n_qb : qb0_a;
+  // every wave is done with the previous pass's LDS buffers
+  if (pass) __syncthreads();
 
   // this wave's keys and values as B operands (lane = key, k = d): zero past n_k
   bf16x8 kf[KT], vf[KT];
@@ -172,33 +218,6 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
     dkt[nb] = f32x16{};
   }
 
-  LdsAddr<D> la;  // over qdo: ka = A operand of S / dP (rows x d), va = A operand of dV^T / dK^T
-  make_lds_addr<D>(la, (unsigned)(uintptr_t)(const lds_void*)&qdo[0][0][0], lane);
-
-  // dQ product: wave w computes rows 32rb .. +31 (rb over RB), d columns 32cb .. +31
-  constexpr int RB = D == 128 ? 2 : 1;
-  const int cb = D == 128 ? wave : (wave & 1);
-  const int rb0 = D == 128 ? 0 : (wave >> 1);
-  unsigned da[RB][2], kba[2];
-  {
-    const unsigned dsb = (unsigned)(uintptr_t)(const lds_void*)dst_t;
-    const unsigned kbb = (unsigned)(uintptr_t)(const lds_void*)kblk;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int r = 0; r < RB; ++r) da[r][h] = tr_nat_addr<kBQ>(dsb, lane, 0, 32 * (rb0 + r), h);
-      kba[h] = tr_nat_addr<D>(kbb, lane, 0, 32 * cb, h);
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      asm volatile("" : "+v"(kba[h]));
-#pragma unroll
-      for (int r = 0; r < RB; ++r) asm volatile("" : "+v"(da[r][h]));
-    }
-  }
-  // this lane's dS^T store address: key row (key - k0), query rows 8g + 4hf (+32qh) in chunk 4qh + g
-  const unsigned dsw = (unsigned)(uintptr_t)(const lds_void*)dst_t;
-
   auto issue_q = [&](int stage, int qi) {
     const int r0 = qi * kBQ;
     issue_rows<D>(qrs, qdo[stage][0], r0, wave, lane);
@@ -219,6 +238,10 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
 #pragma unroll
   for (int ks = 0; ks < kBK / 16; ++ks) kTr[ks] = tr_pair(kba[0] + ks * 16 * ROW, kba[1] + ks * 16 * ROW);
 
+  // the key/value fragments have arrived (waited for here once, not inside the query loop)
+#pragma unroll
+  for (int t = 0; t < KT; ++t) asm volatile("" ::"v"(kf[t]), "v"(vf[t]));
+
   if (qb0 < n_qb) issue_q(0, qb0);
 
   // one query block; STG is the LDS stage (compile-time so that offsets are immediates)
@@ -228,6 +251,26 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
     const int i0 = qi * kBQ;
     // masking: causal diagonal, query rows past n_q, keys past n_k
     const bool need_mask = (p.causal && i0 < kw0 + 31) || (i0 + kBQ > p.n_q) || (kw0 + 32 > p.n_k);
+    // In the second pass the dQ accumulators of this query block start from what this same
+    // thread stored for it in the first pass (read now, so that the step's products hide the
+    // latency; rows past n_q read as zero through the range check); otherwise from zero.
+    const long long R = (long long)p.B * p.H * p.n_q;
+    f32x16 dq0[RB];
+    if (qi >= qb_add) {
+      const __amdgpu_buffer_rsrc_t srs = make_rsrc(p.ws_dq + ((long long)slot * R + hq) * D, (long long)p.n_q * D * 4);
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const unsigned off = ((unsigned)(i0 + 32 * (rb0 + r) + col) * D + 32 * cb + 8 * g + 4 * hf) * 4u;
+          const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(srs, off, 0, 0));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dq0[r][4 * g + e] = v[e];
+        }
+    } else {
+#pragma unroll
+      for (int r = 0; r < RB; ++r) dq0[r] = f32x16{};
+    }
 
     // S = Q K^T and dP = dO V^T for two 32-row halves
     f32x16 s[2], dp[2];
@@ -340,7 +383,7 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
       constexpr int PF = 3;
       f32x16 dqt[RB];
 #pragma unroll
-      for (int r = 0; r < RB; ++r) dqt[r] = f32x16{};
+      for (int r = 0; r < RB; ++r) dqt[r] = dq0[r];
       bf16x8 rds[PF];
       auto load = [&](int st) {
         const int ks = st / RB, r = st % RB;
@@ -359,12 +402,11 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
       }
-      const long long R = (long long)p.B * p.H * p.n_q;
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         const int row = i0 + 32 * (rb0 + r) + col;
         if (row < p.n_q) {
-          float* ws = p.ws_dq + ((long long)kb * R + hq + row) * D + 32 * cb + 4 * hf;
+          float* ws = p.ws_dq + ((long long)slot * R + hq + row) * D + 32 * cb + 4 * hf;
 #pragma unroll
           for (int g = 0; g < 4; ++g)
             __builtin_nontemporal_store(
@@ -382,12 +424,14 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
     // them out of and back into the AGPRs the products accumulate in
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(dvt[nb]), "+a"(dkt[nb]));
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // vmcnt(0) through the builtin, which the compiler's own wait tracking sees: it then
+    // knows that no earlier load is outstanding inside the step
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();  // stage 0 published; dS^T and stage 1 free
     if (qi + 1 < n_qb) issue_q(1, qi + 1);
     step(std::integral_constant<int, 0>{}, qi);
     if (qi + 1 < n_qb) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
       if (qi + 2 < n_qb) issue_q(0, qi + 2);
       step(std::integral_constant<int, 1>{}, qi + 1);
@@ -411,11 +455,14 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
         *reinterpret_cast<u32x2*>(dvr + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(v4, bf16x4));
       }
   }
+  // the first pass's partial stores have completed before the second pass reads them back
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }  // pass
 }
 
 // ---------------------------------------------------------------------------
-// dQ_i = scale * sum over key blocks kb of the partials, in kb order; under the
-// causal mask block kb wrote rows from kb*128 on only.  One thread per
+// dQ_i = scale * sum over slots s of the partials, in slot order; under the
+// causal mask slot s holds rows from s*128 on only.  One thread per
 // 4 elements.
 template <int D>
 __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
@@ -424,14 +471,15 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
   if (idx >= R * D) return;
   const long long rg = idx / D;
   const int i = (int)(rg % p.n_q);
-  const int n_kb = (p.n_k + kBK - 1) / kBK;
-  // query block qi was processed by key blocks kb with kb*128 <= qi*64 + 63 (causal)
-  const int kb_end = p.causal ? min(n_kb, (i / kBQ * kBQ + kBQ - 1) / kBK + 1) : n_kb;
+  const int n_slot = ((p.n_k + kBK - 1) / kBK + 1) / 2;
+  // slot s holds key blocks s and n_kb-1-s; under the causal mask query block qi was
+  // processed by block s (the earlier of the two) iff s*128 <= qi*64 + 63
+  const int s_end = p.causal ? min(n_slot, (i / kBQ * kBQ + kBQ - 1) / kBK + 1) : n_slot;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   // the partials are written once and read once: non-temporal on both sides
 #pragma unroll 4
-  for (int kb = 0; kb < kb_end; ++kb)
-    acc += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.ws_dq + (long long)kb * R * D + idx));
+  for (int s = 0; s < s_end; ++s)
+    acc += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.ws_dq + (long long)s * R * D + idx));
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   *reinterpret_cast<u32x2*>(p.dq + idx) = __builtin_bit_cast(u32x2, __builtin_convertvector(acc * p.scale, bf16x4));
 }
@@ -443,7 +491,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   const int n_kb = (p.n_k + kBK - 1) / kBK;
   const float sl2 = p.scale * kLog2e;
   const unsigned g0 = (unsigned)((R + (256 / (p.d / 8)) - 1) / (256 / (p.d / 8)));
-  const unsigned g1 = (unsigned)((long long)p.B * p.H * n_kb);
+  const unsigned g1 = (unsigned)((long long)p.B * p.H * ((n_kb + 1) / 2));
   const unsigned g2 = (unsigned)((R * p.d / 4 + 255) / 256);
   if (p.d == 128) {
     hipLaunchKernelGGL(bwd_prep_kernel<128>, dim3(g0), dim3(256), 0, stream, p);

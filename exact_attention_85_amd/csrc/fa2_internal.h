@@ -29,7 +29,8 @@ struct FwdParams {
 
 // Arguments of the backward launches.  dq, dk, dv are bf16 outputs; the
 // workspace holds l2vec [R] (LSE * log2 e), dvec [R] (rowsum dO * O) and the
-// per-key-block dQ partials ws_dq [n_kb][R][d], R = B*H*N_q.
+// dQ partials ws_dq [n_slot][R][d], R = B*H*N_q, one per pair of 128-key
+// blocks (n_slot = ceil(n_kb / 2)).
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;

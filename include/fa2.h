@@ -150,8 +150,9 @@ int fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float*
 
 /*
  * fa2_bwd_workspace_bytes — bytes of caller-owned device workspace fa2_bwd
- * needs: (2*R + ceil(N_k/128) * R * d) * 4 with R = B*H*N_q.  Returns 0 when
- * an argument is out of range.
+ * needs: (2*R + ceil(ceil(N_k/128)/2) * R * d) * 4 with R = B*H*N_q (one fp32
+ * dQ partial per pair of 128-key blocks).  Returns 0 when an argument is out
+ * of range.
  */
 size_t fa2_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d);
 
@@ -171,10 +172,11 @@ size_t fa2_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d);
  * P is rounded to bf16 for dV, dS to bf16 for dK and dQ; products accumulate
  * in fp32; dQ, dK, dV are written as bf16 (RNE).
  *
- * Passes: (1) D and LSE*log2(e) per row; (2) one workgroup per 128-key block
- * computes dK and dV for its keys and writes its contribution to dQ for every
- * query row into the workspace; (3) dQ = scale * the sum of the contributions
- * in key-block order.  No atomics: results are bit-reproducible.
+ * Passes: (1) D and LSE*log2(e) per row; (2) one workgroup per pair of
+ * 128-key blocks computes dK and dV for the keys of one block, then of the
+ * other, and writes the pair's summed contribution to dQ for every query row
+ * into the workspace; (3) dQ = scale * the sum of the pair contributions in
+ * pair order.  No atomics: results are bit-reproducible.
  *
  * Q, K, V, O, dO: bf16 [B][H][N][d] as in fa2_fwd; LSE: fp32 [B][H][N_q]
  * (natural log, as fa2_fwd writes it).  dQ [B][H][N_q][d], dK and dV

@@ -134,7 +134,9 @@ static void test_bwd() {
        *W = dev(5);
   float* L = devf(4);
   const long long R = 1 * 2 * 256;
-  CHECK(fa2_bwd_workspace_bytes(1, 2, 256, 200, 64) == (size_t)(2 * R + 2 * R * 64) * 4);
+  // 200 keys: two 128-key blocks, one pair, one dQ partial; 300 keys: two pairs
+  CHECK(fa2_bwd_workspace_bytes(1, 2, 256, 200, 64) == (size_t)(2 * R + 1 * R * 64) * 4);
+  CHECK(fa2_bwd_workspace_bytes(1, 2, 256, 300, 64) == (size_t)(2 * R + 2 * R * 64) * 4);
   CHECK(fa2_bwd_workspace_bytes(0, 2, 256, 200, 64) == 0);
   const size_t need = fa2_bwd_workspace_bytes(1, 2, 256, 200, 64);
   CHECK(fa2_bwd(Q, K, V, O, nullptr, L, dQ, dK, dV, 1, 2, 256, 200, 64, 0, 0.1f, W, need, nullptr) == FA2_ERR_NULLPTR);
@@ -147,9 +149,9 @@ static void test_bwd() {
   const fa2::BwdParams& p = stub::rec.bwd;
   float* ws = static_cast<float*>(W);
   CHECK(p.dout == dO && p.dq == dQ && p.dk == dK && p.dv == dV && p.lse == L && p.causal == 1);
-  // LSE*log2e [R], D [R], then the dQ partials [n_kb][R][d], ending at the workspace size
+  // LSE*log2e [R], D [R], then the dQ partials [n_slot][R][d], ending at the workspace size
   CHECK(p.l2vec == ws && p.dvec == ws + R && p.ws_dq == ws + 2 * R);
-  CHECK((size_t)((char*)(p.ws_dq + 2 * R * 64) - (char*)ws) == need);
+  CHECK((size_t)((char*)(p.ws_dq + 1 * R * 64) - (char*)ws) == need);
 }
 
 static void test_fp8() {

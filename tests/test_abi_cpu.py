@@ -187,7 +187,9 @@ def bwd(q=Q, k=K, v=V, o=O, do=DO, l=L, dq=DQ, dk=DK, dv=DV, B=1, H=2, nq=256, n
 def test_bwd_validation():
     lib = fa2.load_library()
     R = 1 * 2 * 256
-    assert lib.fa2_bwd_workspace_bytes(1, 2, 256, 200, 64) == (2 * R + 2 * R * 64) * 4
+    # 200 keys: two 128-key blocks, one pair, one dQ partial; 300 keys: three blocks, two pairs
+    assert lib.fa2_bwd_workspace_bytes(1, 2, 256, 200, 64) == (2 * R + 1 * R * 64) * 4
+    assert lib.fa2_bwd_workspace_bytes(1, 2, 256, 300, 64) == (2 * R + 2 * R * 64) * 4
     assert lib.fa2_bwd_workspace_bytes(0, 2, 256, 200, 64) == 0
     for name in ("q", "k", "v", "o", "do", "l", "dq", "dk", "dv"):
         assert bwd(**{name: None}) == NULLPTR, name
