@@ -171,7 +171,7 @@ int fa2_num_splits(int B, int H, int N_q, int N_k, int d, int num_cus) {
 size_t fa2_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d) {
   if (B < 1 || H < 1 || N_q < 1 || N_k < 1 || d < 1) return 0;
   const size_t R = (size_t)B * (size_t)H * (size_t)N_q;
-  const size_t n_slot = (((size_t)N_k + 127) / 128 + 1) / 2;  // one dQ partial per pair of 128-key blocks
+  const size_t n_slot = (size_t)fa2::bwd_num_slots(B, H, N_k);  // one dQ partial per group of key blocks
   return (2 * R + n_slot * R * (size_t)d) * 4u;
 }
 
@@ -182,8 +182,7 @@ int fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const vo
   // the forward's own checks on Q, K, V, O, LSE (LSE read-only here)
   int rc = check_common(Q, K, V, O, LSE, B, H, N_q, N_k, d, scale);
   if (rc != FA2_OK) return rc;
-  const long long n_slot = ((N_k + 127) / 128 + 1) / 2;  // workgroups per head
-  if (n_slot * B * H > kMaxGrid) return FA2_ERR_BAD_SHAPE;
+  if (fa2::bwd_num_slots(B, H, N_k) * B * H > kMaxGrid) return FA2_ERR_BAD_SHAPE;  // workgroups
   const size_t need = fa2_bwd_workspace_bytes(B, H, N_q, N_k, d);
   if (!workspace || workspace_bytes < need) return FA2_ERR_WORKSPACE;
   // outputs must not overlap any input, each other or the workspace

@@ -14,15 +14,16 @@
 //
 // Three launches:
 //   bwd_prep_kernel    D_i and LSE_i * log2(e) for every query row
-//   bwd_kv_kernel      one workgroup per pair of 128-key blocks, taken one
-//                      after the other (one wave per 32 keys): streams 64-row
-//                      query blocks through LDS and runs the five products on
-//                      the matrix cores; dK and dV stay in registers.  The
-//                      pair shares one workspace slot for its dQ contribution:
-//                      the first block stores it, and for the second block
-//                      each thread's dQ accumulators start from the values it
-//                      stored itself, so the slot ends up holding the pair's
-//                      sum and the reduction reads half as many partials
+//   bwd_kv_kernel      one workgroup per group of up to 8 128-key blocks,
+//                      taken one after the other (one wave per 32 keys):
+//                      streams 64-row query blocks through LDS and runs the
+//                      five products on the matrix cores; dK and dV stay in
+//                      registers.  The group shares one workspace slot for its
+//                      dQ contribution: the first block stores it, and for each
+//                      later block each thread's dQ accumulators start from the
+//                      values it stored itself, so the slot ends up holding the
+//                      group's sum and the reduction reads one partial per
+//                      group instead of one per block
 //   bwd_dq_kernel      dQ_i = scale * sum over the slots, in slot order
 // No atomics: every output element is written by exactly one thread (a slot
 // value twice, by the same thread, in program order), and the dQ sum runs in a
@@ -43,7 +44,7 @@
 namespace fa2 {
 namespace {
 
-constexpr int kBK = 128;  // keys per block (a workgroup takes two)
+constexpr int kBK = 128;  // keys per block (a workgroup takes a group of them)
 constexpr int kBQ = 64;   // query rows per step
 // s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt fields at their maxima)
 constexpr int kWaitVm0 = 0x0F70;
@@ -130,17 +131,18 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
   const int hf = lane >> 5;
   const int col = lane & 31;
 
-  // one workgroup per pair of key blocks (kb_a = n_kb-1-slot, then kb_b = slot; one block
-  // when they coincide), so that both add into one dQ partial slot
+  // One workgroup per group of G key blocks sharing a dQ slot s: with n = n_slot, the pairs
+  // (2jn + s, 2jn + 2n - 1 - s) for j < G / 2 (G = 1: block s alone), which gives every
+  // slot the same causal work.  They are taken in decreasing order (blocks past the last
+  // key are skipped), so that each block sees a superset of the query rows the blocks
+  // before it saw.
   const int n_kb = (p.n_k + kBK - 1) / kBK;
-  const int n_slot = (n_kb + 1) / 2;
+  const int G = bwd_blocks_per_group(p.B, p.H, p.n_k);
+  const int n_slot = (int)bwd_num_slots(p.B, p.H, p.n_k);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = L / n_slot;
   const int slot = L % n_slot;
-  const int kb_a = n_kb - 1 - slot;
   const int n_qb = (p.n_q + kBQ - 1) / kBQ;
-  // causal: rows below a block's first key see none of its keys
-  const int qb0_a = p.causal ? min(kb_a * kBK / kBQ, n_qb) : 0;
 
   const long long hq = (long long)bh * p.n_q, hk = (long long)bh * p.n_k;
   const i32x4 qrs = raw_rsrc(p.q + hq * D, (long long)p.n_q * D * 2);
@@ -175,16 +177,17 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
   // this lane's dS^T store address: key row (key - k0), query rows 8g + 4hf (+32qh) in chunk 4qh + g
   const unsigned dsw = (unsigned)(uintptr_t)(const lds_void*)dst_t;
 
-  for (int pass = 0; pass < (kb_a == slot ? 1 : 2); ++pass) {
-  const int kb = pass == 0 ? kb_a : slot;
+  int qb_add = n_qb;  // query blocks from here on already hold earlier blocks' contributions
+  for (int pass = 0; pass < G; ++pass) {
+  const int kb = G == 1 ? slot : (G / 2 - 1 - pass / 2) * 2 * n_slot + ((pass & 1) ? slot : 2 * n_slot - 1 - slot);
+  if (kb >= n_kb) continue;  // uniform over the workgroup
   const int k0 = kb * kBK;
   const int kw0 = k0 + 32 * wave;     // this wave's keys kw0 .. kw0 + 31
   const int key = kw0 + col;          // this lane's key column
+  // causal: rows below the block's first key see none of its keys
   const int qb0 = p.causal ? min(k0 / kBQ, n_qb) : 0;
-  // query blocks from qb_add on already hold the first pass's contribution in the slot
-  const int qb_add = pass == 0 ? n_qb : qb0_a;
-  // every wave is done with the previous pass's LDS buffers
-  if (pass) __syncthreads();
+  // every wave is done with the previous block's LDS buffers
+  if (pass > 0) __syncthreads();
 
   // this wave's keys and values as B operands (lane = key, k = d): zero past n_k
   bf16x8 kf[KT], vf[KT];
@@ -455,8 +458,9 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
         *reinterpret_cast<u32x2*>(dvr + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(v4, bf16x4));
       }
   }
-  // the first pass's partial stores have completed before the second pass reads them back
+  // this block's partial stores have completed before the next block reads them back
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  qb_add = qb0;
   }  // pass
 }
 
@@ -471,9 +475,9 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
   if (idx >= R * D) return;
   const long long rg = idx / D;
   const int i = (int)(rg % p.n_q);
-  const int n_slot = ((p.n_k + kBK - 1) / kBK + 1) / 2;
-  // slot s holds key blocks s and n_kb-1-s; under the causal mask query block qi was
-  // processed by block s (the earlier of the two) iff s*128 <= qi*64 + 63
+  const int n_slot = (int)bwd_num_slots(p.B, p.H, p.n_k);
+  // the lowest key block of slot s is block s; under the causal mask query block qi was
+  // processed by it (and so the slot written) iff s*128 <= qi*64 + 63
   const int s_end = p.causal ? min(n_slot, (i / kBQ * kBQ + kBQ - 1) / kBK + 1) : n_slot;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   // the partials are written once and read once: non-temporal on both sides
@@ -488,10 +492,9 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   const long long R = (long long)p.B * p.H * p.n_q;
-  const int n_kb = (p.n_k + kBK - 1) / kBK;
   const float sl2 = p.scale * kLog2e;
   const unsigned g0 = (unsigned)((R + (256 / (p.d / 8)) - 1) / (256 / (p.d / 8)));
-  const unsigned g1 = (unsigned)((long long)p.B * p.H * ((n_kb + 1) / 2));
+  const unsigned g1 = (unsigned)((long long)p.B * p.H * bwd_num_slots(p.B, p.H, p.n_k));
   const unsigned g2 = (unsigned)((R * p.d / 4 + 255) / 256);
   if (p.d == 128) {
     hipLaunchKernelGGL(bwd_prep_kernel<128>, dim3(g0), dim3(256), 0, stream, p);

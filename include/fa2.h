@@ -150,9 +150,10 @@ int fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float*
 
 /*
  * fa2_bwd_workspace_bytes — bytes of caller-owned device workspace fa2_bwd
- * needs: (2*R + ceil(ceil(N_k/128)/2) * R * d) * 4 with R = B*H*N_q (one fp32
- * dQ partial per pair of 128-key blocks).  Returns 0 when an argument is out
- * of range.
+ * needs: (2*R + S * R * d) * 4 with R = B*H*N_q, one fp32 dQ partial for each
+ * of the S = ceil(ceil(N_k/128)/G) groups of G 128-key blocks.  G is the
+ * largest of 8, 4 and 2 with B*H*S >= 256 (the number of workgroups), else 1.
+ * Returns 0 when an argument is out of range.
  */
 size_t fa2_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d);
 
@@ -172,11 +173,11 @@ size_t fa2_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d);
  * P is rounded to bf16 for dV, dS to bf16 for dK and dQ; products accumulate
  * in fp32; dQ, dK, dV are written as bf16 (RNE).
  *
- * Passes: (1) D and LSE*log2(e) per row; (2) one workgroup per pair of
- * 128-key blocks computes dK and dV for the keys of one block, then of the
- * other, and writes the pair's summed contribution to dQ for every query row
- * into the workspace; (3) dQ = scale * the sum of the pair contributions in
- * pair order.  No atomics: results are bit-reproducible.
+ * Passes: (1) D and LSE*log2(e) per row; (2) one workgroup per group of G
+ * 128-key blocks (G as in fa2_bwd_workspace_bytes) computes dK and dV for the
+ * keys of each block in turn, and writes the group's summed contribution to dQ
+ * for every query row into the workspace; (3) dQ = scale * the sum of the group
+ * contributions in group order.  No atomics: results are bit-reproducible.
  *
  * Q, K, V, O, dO: bf16 [B][H][N][d] as in fa2_fwd; LSE: fp32 [B][H][N_q]
  * (natural log, as fa2_fwd writes it).  dQ [B][H][N_q][d], dK and dV

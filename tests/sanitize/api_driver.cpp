@@ -134,9 +134,12 @@ static void test_bwd() {
        *W = dev(5);
   float* L = devf(4);
   const long long R = 1 * 2 * 256;
-  // 200 keys: two 128-key blocks, one pair, one dQ partial; 300 keys: two pairs
-  CHECK(fa2_bwd_workspace_bytes(1, 2, 256, 200, 64) == (size_t)(2 * R + 1 * R * 64) * 4);
-  CHECK(fa2_bwd_workspace_bytes(1, 2, 256, 300, 64) == (size_t)(2 * R + 2 * R * 64) * 4);
+  // two heads: too few workgroups to group key blocks, so one dQ partial per 128-key block
+  CHECK(fa2_bwd_workspace_bytes(1, 2, 256, 200, 64) == (size_t)(2 * R + 2 * R * 64) * 4);
+  CHECK(fa2_bwd_workspace_bytes(1, 2, 256, 300, 64) == (size_t)(2 * R + 3 * R * 64) * 4);
+  // 32 heads x 128 blocks: groups of 8 blocks, 16 partials (and no overflow at the limits)
+  CHECK(fa2_bwd_workspace_bytes(1, 32, 16384, 16384, 128) == (size_t)(2 + 16 * 128) * 32 * 16384 * 4);
+  CHECK(fa2_bwd_workspace_bytes(INT32_MAX, INT32_MAX, 1, INT32_MAX, 128) > 0);
   CHECK(fa2_bwd_workspace_bytes(0, 2, 256, 200, 64) == 0);
   const size_t need = fa2_bwd_workspace_bytes(1, 2, 256, 200, 64);
   CHECK(fa2_bwd(Q, K, V, O, nullptr, L, dQ, dK, dV, 1, 2, 256, 200, 64, 0, 0.1f, W, need, nullptr) == FA2_ERR_NULLPTR);
@@ -151,7 +154,7 @@ static void test_bwd() {
   CHECK(p.dout == dO && p.dq == dQ && p.dk == dK && p.dv == dV && p.lse == L && p.causal == 1);
   // LSE*log2e [R], D [R], then the dQ partials [n_slot][R][d], ending at the workspace size
   CHECK(p.l2vec == ws && p.dvec == ws + R && p.ws_dq == ws + 2 * R);
-  CHECK((size_t)((char*)(p.ws_dq + 1 * R * 64) - (char*)ws) == need);
+  CHECK((size_t)((char*)(p.ws_dq + 2 * R * 64) - (char*)ws) == need);
 }
 
 static void test_fp8() {

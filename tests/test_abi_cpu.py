@@ -187,9 +187,20 @@ def bwd(q=Q, k=K, v=V, o=O, do=DO, l=L, dq=DQ, dk=DK, dv=DV, B=1, H=2, nq=256, n
 def test_bwd_validation():
     lib = fa2.load_library()
     R = 1 * 2 * 256
-    # 200 keys: two 128-key blocks, one pair, one dQ partial; 300 keys: three blocks, two pairs
-    assert lib.fa2_bwd_workspace_bytes(1, 2, 256, 200, 64) == (2 * R + 1 * R * 64) * 4
-    assert lib.fa2_bwd_workspace_bytes(1, 2, 256, 300, 64) == (2 * R + 2 * R * 64) * 4
+    # one dQ partial per group of G 128-key blocks, G the largest of 8, 4, 2 that leaves at least
+    # 256 workgroups (B*H*ceil(n_kb/G)), else 1.  Two heads: too few workgroups to group any blocks
+    assert lib.fa2_bwd_workspace_bytes(1, 2, 256, 200, 64) == (2 * R + 2 * R * 64) * 4
+    assert lib.fa2_bwd_workspace_bytes(1, 2, 256, 300, 64) == (2 * R + 3 * R * 64) * 4
+    # 64 heads x 32 blocks (B4 H16 N4096): G = 8, 4 slots; 32 heads x 128 blocks: G = 8, 16 slots
+    R3, R4 = 4 * 16 * 4096, 32 * 16384
+    assert lib.fa2_bwd_workspace_bytes(4, 16, 4096, 4096, 128) == (2 * R3 + 4 * R3 * 128) * 4
+    assert lib.fa2_bwd_workspace_bytes(1, 32, 16384, 16384, 128) == (2 * R4 + 16 * R4 * 128) * 4
+    # 8 heads x 32 blocks: 8 * 16 = 128 < 256 even with G = 2, so G = 1 (32 slots)
+    R5 = 8 * 4096
+    assert lib.fa2_bwd_workspace_bytes(1, 8, 4096, 4096, 64) == (2 * R5 + 32 * R5 * 64) * 4
+    # 128 heads x 16 blocks: G = 8 gives 256 workgroups, 2 slots
+    R6 = 128 * 2048
+    assert lib.fa2_bwd_workspace_bytes(8, 16, 2048, 2048, 64) == (2 * R6 + 2 * R6 * 64) * 4
     assert lib.fa2_bwd_workspace_bytes(0, 2, 256, 200, 64) == 0
     for name in ("q", "k", "v", "o", "do", "l", "dq", "dk", "dv"):
         assert bwd(**{name: None}) == NULLPTR, name
