@@ -9,7 +9,8 @@ normal build's.  A missing wait or barrier shows up as NaN or as a changed
 bit.  Each case runs both builds on the same inputs through the C ABI and
 compares every output bit for bit, over the paths that stream through LDS:
 the 4-wave and 8-wave forward kernels (plain, causal, windowed, ragged), the
-split-KV partials, the backward pass and the FP8 forward.
+split-KV partials, the backward pass (one key block or a group of them per
+workgroup) and the FP8 forward.
 """
 import pytest
 import torch
@@ -71,11 +72,14 @@ def test_splitkv_partials():
     same(a, b, "split-KV")
 
 
-@pytest.mark.parametrize("nq,d,causal", [(700, 128, 0), (700, 128, 1), (450, 64, 0)])
-def test_backward(nq, d, causal):
-    print(f"race check fa2_bwd N{nq} d{d} causal={causal}", flush=True)
-    q, k, v = workloads.make_qkv_shape(1, 2, nq, nq, d, 74, DEV)
-    do = workloads.make_qkv_shape(1, 2, nq, nq, d, 75, DEV)[0]
+# B*H = 2: one key block per workgroup; B*H = 256: groups of key blocks per workgroup, which
+# refill the same LDS buffers block after block
+@pytest.mark.parametrize("B,H,nq,d,causal", [(1, 2, 700, 128, 0), (1, 2, 700, 128, 1), (1, 2, 450, 64, 0),
+                                             (16, 16, 600, 128, 1), (16, 16, 1000, 64, 0)])
+def test_backward(B, H, nq, d, causal):
+    print(f"race check fa2_bwd B{B} H{H} N{nq} d{d} causal={causal}", flush=True)
+    q, k, v = workloads.make_qkv_shape(B, H, nq, nq, d, 74, DEV)
+    do = workloads.make_qkv_shape(B, H, nq, nq, d, 75, DEV)[0]
     o, lse = fa2.forward(q, k, v, causal=bool(causal))
     a, b = both(lambda: fa2.backward(q, k, v, o, lse, do, causal=bool(causal)))
     same(a, b, "backward")
