@@ -35,6 +35,7 @@ METRIC = "attention fwd TFLOP/s (bf16, causal/non-causal) and % of MI355X MFMA p
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "exact_attention_85_amd", "csrc", "fa2_fwd.hip")
 FP8_SRC = os.path.join(ROOT, "exact_attention_85_amd", "csrc", "fa2_fp8.hip")
+BWD_SRC = os.path.join(ROOT, "exact_attention_85_amd", "csrc", "fa2_bwd.hip")
 METRIC_FP8 = "attention fwd TFLOP/s (fp8 e4m3 inputs, per-head scaling) and % of MI355X fp8 MFMA peak"
 
 
@@ -45,6 +46,15 @@ def log(*a):
 def kernel_source_sha(path: str = KERNEL_SRC) -> str:
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def env_info() -> dict:
+    """Where the line was measured: the device, the runtime versions, and the kernel
+    sources it ran (sha256[:16], the key the committed counter summaries carry)."""
+    props = torch.cuda.get_device_properties(0)
+    return {"gpu": props.name, "arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
+            "hip": torch.version.hip, "torch": torch.__version__,
+            "kernel_sources": {os.path.basename(p): kernel_source_sha(p) for p in (KERNEL_SRC, BWD_SRC, FP8_SRC)}}
 
 
 def measured_traffic(key: str, src: str = KERNEL_SRC):
@@ -327,6 +337,7 @@ def main():
     if not args.no_cpu and not args.fp8:  # the oracle baseline is the bf16 definition
         result["cpu_baseline"] = cpu_baseline(w, causal, q, k, v)
         log(f"oracle: {result['cpu_baseline']}")
+    result["env"] = env_info()
     print(json.dumps(result), flush=True)
 
 
