@@ -49,7 +49,9 @@ def load_library():
 @contextlib.contextmanager
 def library_at(path: str):
     """Routes this module's calls to the build at `path` (such as the race-check
-    build) inside the block; the default library is used again afterwards."""
+    build) inside the block; the default library is used again afterwards.  It
+    swaps one module-wide handle, so it is for single-threaded use (tests and
+    measurements), not for code that calls the library from several threads."""
     global _lib
     saved = load_library()
     _lib = open_library(path)

@@ -179,288 +179,289 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
 
   int qb_add = n_qb;  // query blocks from here on already hold earlier blocks' contributions
   for (int pass = 0; pass < G; ++pass) {
-  const int kb = G == 1 ? slot : (G / 2 - 1 - pass / 2) * 2 * n_slot + ((pass & 1) ? slot : 2 * n_slot - 1 - slot);
-  if (kb >= n_kb) continue;  // uniform over the workgroup
-  const int k0 = kb * kBK;
-  const int kw0 = k0 + 32 * wave;     // this wave's keys kw0 .. kw0 + 31
-  const int key = kw0 + col;          // this lane's key column
-  // causal: rows below the block's first key see none of its keys
-  const int qb0 = p.causal ? min(k0 / kBQ, n_qb) : 0;
-  // every wave is done with the previous block's LDS buffers
-  if (pass > 0) __syncthreads();
+    const int kb = G == 1 ? slot : (G / 2 - 1 - pass / 2) * 2 * n_slot + ((pass & 1) ? slot : 2 * n_slot - 1 - slot);
+    if (kb >= n_kb) continue;  // uniform over the workgroup
+    const int k0 = kb * kBK;
+    const int kw0 = k0 + 32 * wave;     // this wave's keys kw0 .. kw0 + 31
+    const int key = kw0 + col;          // this lane's key column
+    // causal: rows below the block's first key see none of its keys
+    const int qb0 = p.causal ? min(k0 / kBQ, n_qb) : 0;
+    // every wave is done with the previous block's LDS buffers
+    if (pass > 0) __syncthreads();
 
-  // this wave's keys and values as B operands (lane = key, k = d): zero past n_k
-  bf16x8 kf[KT], vf[KT];
-  {
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + hk * D, (long long)p.n_k * D * 2);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + hk * D, (long long)p.n_k * D * 2);
+    // this wave's keys and values as B operands (lane = key, k = d): zero past n_k
+    bf16x8 kf[KT], vf[KT];
+    {
+      const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + hk * D, (long long)p.n_k * D * 2);
+      const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + hk * D, (long long)p.n_k * D * 2);
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      const unsigned off = ((unsigned)key * D + 16 * t + 8 * hf) * 2u;
-      kf[t] = as_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0)));
-      vf[t] = as_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0)));
+      for (int t = 0; t < KT; ++t) {
+        const unsigned off = ((unsigned)key * D + 16 * t + 8 * hf) * 2u;
+        kf[t] = as_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0)));
+        vf[t] = as_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0)));
+      }
     }
-  }
-  // the whole key block, row-major swizzled, for the dQ product
-  {
-    constexpr int CPR = D / 8;
-    const i32x4 krs = raw_rsrc(p.k + hk * D, (long long)p.n_k * D * 2);
+    // the whole key block, row-major swizzled, for the dQ product
+    {
+      constexpr int CPR = D / 8;
+      const i32x4 krs = raw_rsrc(p.k + hk * D, (long long)p.n_k * D * 2);
 #pragma unroll
-    for (int i = 0; i < kBK * CPR / 256; ++i) {
-      const int s = (i * 4 + wave) * 64 + lane;
-      const int r = s / CPR;
-      const int c = (s % CPR) ^ (swz<D>(r, 0) - r * CPR);
-      lds_dma16(krs, kblk + (i * 4 + wave) * 64 * 16, ((unsigned)(k0 + r) * D + c * 8) * 2u);
+      for (int i = 0; i < kBK * CPR / 256; ++i) {
+        const int s = (i * 4 + wave) * 64 + lane;
+        const int r = s / CPR;
+        const int c = (s % CPR) ^ (swz<D>(r, 0) - r * CPR);
+        lds_dma16(krs, kblk + (i * 4 + wave) * 64 * 16, ((unsigned)(k0 + r) * D + c * 8) * 2u);
+      }
     }
-  }
 
-  f32x16 dvt[NB], dkt[NB];  // dV^T, dK^T: rows d, columns this wave's keys
+    f32x16 dvt[NB], dkt[NB];  // dV^T, dK^T: rows d, columns this wave's keys
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    dvt[nb] = f32x16{};
-    dkt[nb] = f32x16{};
-  }
+    for (int nb = 0; nb < NB; ++nb) {
+      dvt[nb] = f32x16{};
+      dkt[nb] = f32x16{};
+    }
 
-  auto issue_q = [&](int stage, int qi) {
-    const int r0 = qi * kBQ;
-    issue_rows<D>(qrs, qdo[stage][0], r0, wave, lane);
-    issue_rows<D>(dors, qdo[stage][1], r0, wave, lane);
-    // lanes 0-15 of wave 0 bring the 64 L2 values, lanes 16-31 the 64 D values
-    // (lane l writes 16 bytes at the LDS base + 16 l)
-    if (wave == 0 && lane < 16)
-      lds_dma16(l2rs, reinterpret_cast<const char*>(&rowv[stage][0][0]), (unsigned)(r0 * 4 + lane * 16));
-    else if (wave == 0 && lane < 32)
-      lds_dma16(dvrs, reinterpret_cast<const char*>(&rowv[stage][1][0]) - 256, (unsigned)(r0 * 4 + (lane - 16) * 16));
-  };
+    auto issue_q = [&](int stage, int qi) {
+      const int r0 = qi * kBQ;
+      issue_rows<D>(qrs, qdo[stage][0], r0, wave, lane);
+      issue_rows<D>(dors, qdo[stage][1], r0, wave, lane);
+      // lanes 0-15 of wave 0 bring the 64 L2 values, lanes 16-31 the 64 D values
+      // (lane l writes 16 bytes at the LDS base + 16 l)
+      if (wave == 0 && lane < 16)
+        lds_dma16(l2rs, reinterpret_cast<const char*>(&rowv[stage][0][0]), (unsigned)(r0 * 4 + lane * 16));
+      else if (wave == 0 && lane < 32)
+        lds_dma16(dvrs, reinterpret_cast<const char*>(&rowv[stage][1][0]) - 256, (unsigned)(r0 * 4 + (lane - 16) * 16));
+    };
 
-  // K^T fragments of this wave's d columns for the dQ product: the key block is the
-  // same for every query block, so they are read from LDS once and kept in registers
-  bf16x8 kTr[kBK / 16];
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();  // the key block is in LDS
+    // K^T fragments of this wave's d columns for the dQ product: the key block is the
+    // same for every query block, so they are read from LDS once and kept in registers
+    bf16x8 kTr[kBK / 16];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // the key block is in LDS
 #pragma unroll
-  for (int ks = 0; ks < kBK / 16; ++ks) kTr[ks] = tr_pair(kba[0] + ks * 16 * ROW, kba[1] + ks * 16 * ROW);
+    for (int ks = 0; ks < kBK / 16; ++ks) kTr[ks] = tr_pair(kba[0] + ks * 16 * ROW, kba[1] + ks * 16 * ROW);
 
-  // the key/value fragments have arrived (waited for here once, not inside the query loop)
+    // the key/value fragments have arrived (waited for here once, not inside the query loop)
 #pragma unroll
-  for (int t = 0; t < KT; ++t) asm volatile("" ::"v"(kf[t]), "v"(vf[t]));
+    for (int t = 0; t < KT; ++t) asm volatile("" ::"v"(kf[t]), "v"(vf[t]));
 
-  if (qb0 < n_qb) issue_q(0, qb0);
+    if (qb0 < n_qb) issue_q(0, qb0);
 
-  // one query block; STG is the LDS stage (compile-time so that offsets are immediates)
-  auto step = [&](auto stg_c, int qi) {
-    constexpr int STG = decltype(stg_c)::value;
-    constexpr unsigned QOFF = STG * 2 * TILE, DOFF = QOFF + TILE;
-    const int i0 = qi * kBQ;
-    // masking: causal diagonal, query rows past n_q, keys past n_k
-    const bool need_mask = (p.causal && i0 < kw0 + 31) || (i0 + kBQ > p.n_q) || (kw0 + 32 > p.n_k);
-    // In the second pass the dQ accumulators of this query block start from what this same
-    // thread stored for it in the first pass (read now, so that the step's products hide the
-    // latency; rows past n_q read as zero through the range check); otherwise from zero.
-    const long long R = (long long)p.B * p.H * p.n_q;
-    f32x16 dq0[RB];
-    if (qi >= qb_add) {
-      const __amdgpu_buffer_rsrc_t srs = make_rsrc(p.ws_dq + ((long long)slot * R + hq) * D, (long long)p.n_q * D * 4);
+    // one query block; STG is the LDS stage (compile-time so that offsets are immediates)
+    auto step = [&](auto stg_c, int qi) {
+      constexpr int STG = decltype(stg_c)::value;
+      constexpr unsigned QOFF = STG * 2 * TILE, DOFF = QOFF + TILE;
+      const int i0 = qi * kBQ;
+      // masking: causal diagonal, query rows past n_q, keys past n_k
+      const bool need_mask = (p.causal && i0 < kw0 + 31) || (i0 + kBQ > p.n_q) || (kw0 + 32 > p.n_k);
+      // In the second pass the dQ accumulators of this query block start from what this same
+      // thread stored for it in the first pass (read now, so that the step's products hide the
+      // latency; rows past n_q read as zero through the range check); otherwise from zero.
+      const long long R = (long long)p.B * p.H * p.n_q;
+      f32x16 dq0[RB];
+      if (qi >= qb_add) {
+        const __amdgpu_buffer_rsrc_t srs =
+            make_rsrc(p.ws_dq + ((long long)slot * R + hq) * D, (long long)p.n_q * D * 4);
 #pragma unroll
-      for (int r = 0; r < RB; ++r)
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const unsigned off = ((unsigned)(i0 + 32 * (rb0 + r) + col) * D + 32 * cb + 8 * g + 4 * hf) * 4u;
+            const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(srs, off, 0, 0));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dq0[r][4 * g + e] = v[e];
+          }
+      } else {
+#pragma unroll
+        for (int r = 0; r < RB; ++r) dq0[r] = f32x16{};
+      }
+
+      // S = Q K^T and dP = dO V^T for two 32-row halves
+      f32x16 s[2], dp[2];
+      {
+        // operands read PF steps ahead of their products (LDS latency exceeds two products)
+        constexpr int PF = 2;
+        constexpr int NST = 2 * KT;  // steps (qh, t)
+        bf16x8 ra[PF][2];
+#pragma unroll
+        for (int st = 0; st < PF; ++st) {
+          ra[st][0] = lds_load<bf16x8>(la.ka[st % KT] + QOFF + (st / KT) * 32 * ROW);
+          ra[st][1] = lds_load<bf16x8>(la.ka[st % KT] + DOFF + (st / KT) * 32 * ROW);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+          const int qh = st / KT, t = st % KT;
+          if (t == 0) {
+            s[qh] = f32x16{};
+            dp[qh] = f32x16{};
+          }
+          s[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[st % PF][0], kf[t], s[qh], 0, 0, 0);
+          dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[st % PF][1], vf[t], dp[qh], 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          if (st + PF < NST) {
+            const int s2 = st + PF;
+            ra[st % PF][0] = lds_load<bf16x8>(la.ka[s2 % KT] + QOFF + (s2 / KT) * 32 * ROW);
+            ra[st % PF][1] = lds_load<bf16x8>(la.ka[s2 % KT] + DOFF + (s2 / KT) * 32 * ROW);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+        }
+      }
+      // P = exp2(s * scale*log2e - LSE*log2e), dS = P (dP - D); row of register r:
+      // 32qh + 8(r/4) + 4hf + r%4
+      bf16x8 pb[2][2], db[2][2];
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        f32x16 pv, dsv;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const unsigned off = ((unsigned)(i0 + 32 * (rb0 + r) + col) * D + 32 * cb + 8 * g + 4 * hf) * 4u;
-          const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(srs, off, 0, 0));
+          const int rl = 32 * qh + 8 * g + 4 * hf;  // first of this lane's 4 rows in the tile
+          const f32x4 l2 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+              (uintptr_t)(const lds_void*)&rowv[STG][0][rl]);
+          const f32x4 dd = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+              (uintptr_t)(const lds_void*)&rowv[STG][1][rl]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dq0[r][4 * g + e] = v[e];
-        }
-    } else {
-#pragma unroll
-      for (int r = 0; r < RB; ++r) dq0[r] = f32x16{};
-    }
-
-    // S = Q K^T and dP = dO V^T for two 32-row halves
-    f32x16 s[2], dp[2];
-    {
-      // operands read PF steps ahead of their products (LDS latency exceeds two products)
-      constexpr int PF = 2;
-      constexpr int NST = 2 * KT;  // steps (qh, t)
-      bf16x8 ra[PF][2];
-#pragma unroll
-      for (int st = 0; st < PF; ++st) {
-        ra[st][0] = lds_load<bf16x8>(la.ka[st % KT] + QOFF + (st / KT) * 32 * ROW);
-        ra[st][1] = lds_load<bf16x8>(la.ka[st % KT] + DOFF + (st / KT) * 32 * ROW);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
-#pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const int qh = st / KT, t = st % KT;
-        if (t == 0) {
-          s[qh] = f32x16{};
-          dp[qh] = f32x16{};
-        }
-        s[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[st % PF][0], kf[t], s[qh], 0, 0, 0);
-        dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[st % PF][1], vf[t], dp[qh], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        if (st + PF < NST) {
-          const int s2 = st + PF;
-          ra[st % PF][0] = lds_load<bf16x8>(la.ka[s2 % KT] + QOFF + (s2 / KT) * 32 * ROW);
-          ra[st % PF][1] = lds_load<bf16x8>(la.ka[s2 % KT] + DOFF + (s2 / KT) * 32 * ROW);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-      }
-    }
-    // P = exp2(s * scale*log2e - LSE*log2e), dS = P (dP - D); row of register r:
-    // 32qh + 8(r/4) + 4hf + r%4
-    bf16x8 pb[2][2], db[2][2];
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-      f32x16 pv, dsv;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int rl = 32 * qh + 8 * g + 4 * hf;  // first of this lane's 4 rows in the tile
-        const f32x4 l2 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-            (uintptr_t)(const lds_void*)&rowv[STG][0][rl]);
-        const f32x4 dd = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-            (uintptr_t)(const lds_void*)&rowv[STG][1][rl]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qh][r], sl2, -l2[e]));
-          if (need_mask) {
-            const int row = i0 + rl + e;
-            const bool ok = row < p.n_q && key < p.n_k && (!p.causal || key <= row);
-            pr = ok ? pr : 0.f;
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qh][r], sl2, -l2[e]));
+            if (need_mask) {
+              const int row = i0 + rl + e;
+              const bool ok = row < p.n_q && key < p.n_k && (!p.causal || key <= row);
+              pr = ok ? pr : 0.f;
+            }
+            pv[r] = pr;
+            dsv[r] = pr * (dp[qh][r] - dd[e]);
           }
-          pv[r] = pr;
-          dsv[r] = pr * (dp[qh][r] - dd[e]);
+        }
+        pb[qh][0] = cvt_bf16x8(slice8(pv, 0));
+        pb[qh][1] = cvt_bf16x8(slice8(pv, 1));
+        db[qh][0] = cvt_bf16x8(slice8(dsv, 0));
+        db[qh][1] = cvt_bf16x8(slice8(dsv, 1));
+        // dS^T to LDS: 4 consecutive rows (8 bytes) per g
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = 4 * qh + g;  // chunk of 8 rows
+          const unsigned addr = dsw + swz<kBQ>(key - k0, c) * 16 + hf * 8;
+          const u32x4 w4 = __builtin_bit_cast(u32x4, g < 2 ? db[qh][0] : db[qh][1]);
+          const u32x2 w2 = (g & 1) ? u32x2{w4.z, w4.w} : u32x2{w4.x, w4.y};
+          *reinterpret_cast<__attribute__((address_space(3))) u32x2*>((uintptr_t)addr) = w2;
         }
       }
-      pb[qh][0] = cvt_bf16x8(slice8(pv, 0));
-      pb[qh][1] = cvt_bf16x8(slice8(pv, 1));
-      db[qh][0] = cvt_bf16x8(slice8(dsv, 0));
-      db[qh][1] = cvt_bf16x8(slice8(dsv, 1));
-      // dS^T to LDS: 4 consecutive rows (8 bytes) per g
+      // dV^T += dO^T P and dK^T += Q^T dS over the 64 rows (4 k-steps of 16), steps
+      // (qh, t, nb) in that order; the transposed operands are read PF steps ahead of
+      // their products (one LDS read outlasts the two products it feeds)
+      {
+        constexpr int NST = 4 * NB;
+        constexpr int PF = 3;
+        bf16x8 rdo[PF], rq[PF];
+        auto load = [&](int st) {
+          const int qh = st / (2 * NB), t = (st / NB) % 2, nb = st % NB;
+          const unsigned roff = (32 * qh + 16 * t) * ROW;
+          rdo[st % PF] = tr_pair(la.va[2 * nb] + DOFF + roff, la.va[2 * nb + 1] + DOFF + roff);
+          rq[st % PF] = tr_pair(la.va[2 * nb] + QOFF + roff, la.va[2 * nb + 1] + QOFF + roff);
+        };
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = 4 * qh + g;  // chunk of 8 rows
-        const unsigned addr = dsw + swz<kBQ>(key - k0, c) * 16 + hf * 8;
-        const u32x4 w4 = __builtin_bit_cast(u32x4, g < 2 ? db[qh][0] : db[qh][1]);
-        const u32x2 w2 = (g & 1) ? u32x2{w4.z, w4.w} : u32x2{w4.x, w4.y};
-        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>((uintptr_t)addr) = w2;
-      }
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS over the 64 rows (4 k-steps of 16), steps
-    // (qh, t, nb) in that order; the transposed operands are read PF steps ahead of
-    // their products (one LDS read outlasts the two products it feeds)
-    {
-      constexpr int NST = 4 * NB;
-      constexpr int PF = 3;
-      bf16x8 rdo[PF], rq[PF];
-      auto load = [&](int st) {
-        const int qh = st / (2 * NB), t = (st / NB) % 2, nb = st % NB;
-        const unsigned roff = (32 * qh + 16 * t) * ROW;
-        rdo[st % PF] = tr_pair(la.va[2 * nb] + DOFF + roff, la.va[2 * nb + 1] + DOFF + roff);
-        rq[st % PF] = tr_pair(la.va[2 * nb] + QOFF + roff, la.va[2 * nb + 1] + QOFF + roff);
-      };
+        for (int st = 0; st < PF; ++st) load(st);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * PF, 0);
 #pragma unroll
-      for (int st = 0; st < PF; ++st) load(st);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4 * PF, 0);
-#pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const int qh = st / (2 * NB), t = (st / NB) % 2, nb = st % NB;
-        dvt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rdo[st % PF], pb[qh][t], dvt[nb], 0, 0, 0);
-        dkt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq[st % PF], db[qh][t], dkt[nb], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        if (st + PF < NST) {
-          load(st + PF);
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        for (int st = 0; st < NST; ++st) {
+          const int qh = st / (2 * NB), t = (st / NB) % 2, nb = st % NB;
+          dvt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rdo[st % PF], pb[qh][t], dvt[nb], 0, 0, 0);
+          dkt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq[st % PF], db[qh][t], dkt[nb], 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          if (st + PF < NST) {
+            load(st + PF);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          }
         }
       }
-    }
-    // every wave's dS^T is in LDS
-    __syncthreads();
-    // dQ contribution of this key block, computed transposed (dQ^T = K^T dS^T)
-    // so that each lane holds one query row and 4 consecutive d per register
-    // group: rows 32(rb0 + r) + lane%32, d columns 32cb + 8g + 4hf + 0..3
-    // Steps (ks, r): consecutive products accumulate into different row groups, and
-    // the dS^T operands are read PF steps ahead.
-    {
-      constexpr int NST = (kBK / 16) * RB;
-      constexpr int PF = 3;
-      f32x16 dqt[RB];
-#pragma unroll
-      for (int r = 0; r < RB; ++r) dqt[r] = dq0[r];
-      bf16x8 rds[PF];
-      auto load = [&](int st) {
-        const int ks = st / RB, r = st % RB;
-        rds[st % PF] = tr_pair(da[r][0] + ks * 16 * kBQ * 2, da[r][1] + ks * 16 * kBQ * 2);
-      };
-#pragma unroll
-      for (int st = 0; st < PF; ++st) load(st);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
-#pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const int ks = st / RB, r = st % RB;
-        dqt[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kTr[ks], rds[st % PF], dqt[r], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (st + PF < NST) {
-          load(st + PF);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        const int row = i0 + 32 * (rb0 + r) + col;
-        if (row < p.n_q) {
-          float* ws = p.ws_dq + ((long long)slot * R + hq + row) * D + 32 * cb + 4 * hf;
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            __builtin_nontemporal_store(
-                f32x4{dqt[r][4 * g], dqt[r][4 * g + 1], dqt[r][4 * g + 2], dqt[r][4 * g + 3]},
-                reinterpret_cast<f32x4*>(ws + 8 * g));
-        }
-      }
-    }
-  };
-
-  // two LDS stages, unrolled by two so that every offset is an immediate
-  for (int qi = qb0; qi < n_qb; qi += 2) {
-    // keep the dV^T / dK^T accumulators in AGPRs across iterations: otherwise the
-    // loop-carried values are assigned VGPRs and each iteration copies all 128 of
-    // them out of and back into the AGPRs the products accumulate in
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(dvt[nb]), "+a"(dkt[nb]));
-    // vmcnt(0) through the builtin, which the compiler's own wait tracking sees: it then
-    // knows that no earlier load is outstanding inside the step
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();  // stage 0 published; dS^T and stage 1 free
-    if (qi + 1 < n_qb) issue_q(1, qi + 1);
-    step(std::integral_constant<int, 0>{}, qi);
-    if (qi + 1 < n_qb) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      // every wave's dS^T is in LDS
       __syncthreads();
-      if (qi + 2 < n_qb) issue_q(0, qi + 2);
-      step(std::integral_constant<int, 1>{}, qi + 1);
-    }
-  }
-
-  // dK = scale * dK, dV, rows d 32nb + 8g + 4hf + 0..3 of this lane's key
-  if (key < p.n_k) {
-    uint16_t* dkr = p.dk + (hk + key) * D;
-    uint16_t* dvr = p.dv + (hk + key) * D;
+      // dQ contribution of this key block, computed transposed (dQ^T = K^T dS^T)
+      // so that each lane holds one query row and 4 consecutive d per register
+      // group: rows 32(rb0 + r) + lane%32, d columns 32cb + 8g + 4hf + 0..3
+      // Steps (ks, r): consecutive products accumulate into different row groups, and
+      // the dS^T operands are read PF steps ahead.
+      {
+        constexpr int NST = (kBK / 16) * RB;
+        constexpr int PF = 3;
+        f32x16 dqt[RB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+        for (int r = 0; r < RB; ++r) dqt[r] = dq0[r];
+        bf16x8 rds[PF];
+        auto load = [&](int st) {
+          const int ks = st / RB, r = st % RB;
+          rds[st % PF] = tr_pair(da[r][0] + ks * 16 * kBQ * 2, da[r][1] + ks * 16 * kBQ * 2);
+        };
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        const f32x4 k4 = {dkt[nb][4 * g] * p.scale, dkt[nb][4 * g + 1] * p.scale, dkt[nb][4 * g + 2] * p.scale,
-                          dkt[nb][4 * g + 3] * p.scale};
-        const f32x4 v4 = {dvt[nb][4 * g], dvt[nb][4 * g + 1], dvt[nb][4 * g + 2], dvt[nb][4 * g + 3]};
-        const int d0 = 32 * nb + 8 * g + 4 * hf;
-        *reinterpret_cast<u32x2*>(dkr + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(k4, bf16x4));
-        *reinterpret_cast<u32x2*>(dvr + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(v4, bf16x4));
+        for (int st = 0; st < PF; ++st) load(st);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+          const int ks = st / RB, r = st % RB;
+          dqt[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kTr[ks], rds[st % PF], dqt[r], 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (st + PF < NST) {
+            load(st + PF);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          const int row = i0 + 32 * (rb0 + r) + col;
+          if (row < p.n_q) {
+            float* ws = p.ws_dq + ((long long)slot * R + hq + row) * D + 32 * cb + 4 * hf;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              __builtin_nontemporal_store(
+                  f32x4{dqt[r][4 * g], dqt[r][4 * g + 1], dqt[r][4 * g + 2], dqt[r][4 * g + 3]},
+                  reinterpret_cast<f32x4*>(ws + 8 * g));
+          }
+        }
       }
-  }
-  // this block's partial stores have completed before the next block reads them back
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  qb_add = qb0;
+    };
+
+    // two LDS stages, unrolled by two so that every offset is an immediate
+    for (int qi = qb0; qi < n_qb; qi += 2) {
+      // keep the dV^T / dK^T accumulators in AGPRs across iterations: otherwise the
+      // loop-carried values are assigned VGPRs and each iteration copies all 128 of
+      // them out of and back into the AGPRs the products accumulate in
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(dvt[nb]), "+a"(dkt[nb]));
+      // vmcnt(0) through the builtin, which the compiler's own wait tracking sees: it then
+      // knows that no earlier load is outstanding inside the step
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();  // stage 0 published; dS^T and stage 1 free
+      if (qi + 1 < n_qb) issue_q(1, qi + 1);
+      step(std::integral_constant<int, 0>{}, qi);
+      if (qi + 1 < n_qb) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __syncthreads();
+        if (qi + 2 < n_qb) issue_q(0, qi + 2);
+        step(std::integral_constant<int, 1>{}, qi + 1);
+      }
+    }
+
+    // dK = scale * dK, dV, rows d 32nb + 8g + 4hf + 0..3 of this lane's key
+    if (key < p.n_k) {
+      uint16_t* dkr = p.dk + (hk + key) * D;
+      uint16_t* dvr = p.dv + (hk + key) * D;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          const f32x4 k4 = {dkt[nb][4 * g] * p.scale, dkt[nb][4 * g + 1] * p.scale, dkt[nb][4 * g + 2] * p.scale,
+                            dkt[nb][4 * g + 3] * p.scale};
+          const f32x4 v4 = {dvt[nb][4 * g], dvt[nb][4 * g + 1], dvt[nb][4 * g + 2], dvt[nb][4 * g + 3]};
+          const int d0 = 32 * nb + 8 * g + 4 * hf;
+          *reinterpret_cast<u32x2*>(dkr + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(k4, bf16x4));
+          *reinterpret_cast<u32x2*>(dvr + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(v4, bf16x4));
+        }
+    }
+    // this block's partial stores have completed before the next block reads them back
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    qb_add = qb0;
   }  // pass
 }
 
