@@ -347,34 +347,6 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
           *reinterpret_cast<__attribute__((address_space(3))) u32x2*>((uintptr_t)addr) = w2;
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over the 64 rows (4 k-steps of 16), steps
-      // (qh, t, nb) in that order; the transposed operands are read PF steps ahead of
-      // their products (one LDS read outlasts the two products it feeds)
-      {
-        constexpr int NST = 4 * NB;
-        constexpr int PF = 3;
-        bf16x8 rdo[PF], rq[PF];
-        auto load = [&](int st) {
-          const int qh = st / (2 * NB), t = (st / NB) % 2, nb = st % NB;
-          const unsigned roff = (32 * qh + 16 * t) * ROW;
-          rdo[st % PF] = tr_pair(la.va[2 * nb] + DOFF + roff, la.va[2 * nb + 1] + DOFF + roff);
-          rq[st % PF] = tr_pair(la.va[2 * nb] + QOFF + roff, la.va[2 * nb + 1] + QOFF + roff);
-        };
-#pragma unroll
-        for (int st = 0; st < PF; ++st) load(st);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 * PF, 0);
-#pragma unroll
-        for (int st = 0; st < NST; ++st) {
-          const int qh = st / (2 * NB), t = (st / NB) % 2, nb = st % NB;
-          dvt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rdo[st % PF], pb[qh][t], dvt[nb], 0, 0, 0);
-          dkt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq[st % PF], db[qh][t], dkt[nb], 0, 0, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          if (st + PF < NST) {
-            load(st + PF);
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-          }
-        }
-      }
       // every wave's dS^T is in LDS
       __syncthreads();
       // dQ contribution of this key block, computed transposed (dQ^T = K^T dS^T)
@@ -416,6 +388,37 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
               __builtin_nontemporal_store(
                   f32x4{dqt[r][4 * g], dqt[r][4 * g + 1], dqt[r][4 * g + 2], dqt[r][4 * g + 3]},
                   reinterpret_cast<f32x4*>(ws + 8 * g));
+          }
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the 64 rows (4 k-steps of 16), steps
+      // (qh, t, nb) in that order; the transposed operands are read PF steps ahead of
+      // their products (one LDS read outlasts the two products it feeds).  These come
+      // after the dQ products: the dQ stores then complete while they run, instead of
+      // holding up the wait at the top of the next step (one counter covers loads and
+      // stores).
+      {
+        constexpr int NST = 4 * NB;
+        constexpr int PF = 3;
+        bf16x8 rdo[PF], rq[PF];
+        auto load = [&](int st) {
+          const int qh = st / (2 * NB), t = (st / NB) % 2, nb = st % NB;
+          const unsigned roff = (32 * qh + 16 * t) * ROW;
+          rdo[st % PF] = tr_pair(la.va[2 * nb] + DOFF + roff, la.va[2 * nb + 1] + DOFF + roff);
+          rq[st % PF] = tr_pair(la.va[2 * nb] + QOFF + roff, la.va[2 * nb + 1] + QOFF + roff);
+        };
+#pragma unroll
+        for (int st = 0; st < PF; ++st) load(st);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * PF, 0);
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+          const int qh = st / (2 * NB), t = (st / NB) % 2, nb = st % NB;
+          dvt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rdo[st % PF], pb[qh][t], dvt[nb], 0, 0, 0);
+          dkt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq[st % PF], db[qh][t], dkt[nb], 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          if (st + PF < NST) {
+            load(st + PF);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
           }
         }
       }
