@@ -86,10 +86,11 @@ def time_launches(fn, steps: int, warmup: int):
     return start.elapsed_time(stop) / steps
 
 
-def cpu_baseline(w, causal: bool, q, k, v):
+def cpu_baseline(w, causal: bool, q, k, v, o, lse):
     """The fp64 oracle on a bounded sample of query rows of the workload, spread
     over all heads (about 15 s of host work), in TFLOP/s with the same FLOP count
-    per row as the GPU figure."""
+    per row as the GPU figure.  The same oracle rows are compared with the timed
+    run's O and LSE: returns (baseline, parity)."""
     import oracle
 
     bits = [workloads.bf16_bits(t) for t in (q, k, v)]  # whole tensors on the host
@@ -100,20 +101,30 @@ def cpu_baseline(w, causal: bool, q, k, v):
     def run(n_rows):
         rows = np.sort(rng.choice(total_rows, size=n_rows, replace=False)).astype(np.int64)
         t0 = time.perf_counter()
-        oracle.attention_rows_bf16(*bits, rows, causal, w.scale)
-        return time.perf_counter() - t0
+        o_ref, l_ref = oracle.attention_rows_bf16(*bits, rows, causal, w.scale)
+        return time.perf_counter() - t0, rows, o_ref, l_ref
 
     # grow the sample until one run takes about 10-30 s (a small sample over-states the cost
     # per row: each thread converts the K/V heads its rows touch)
     n_rows = min(total_rows, 2048)
-    dt = run(n_rows)
+    dt, rows, o_ref, l_ref = run(n_rows)
     while dt < 10.0 and n_rows < total_rows:
         n_rows = int(min(total_rows, n_rows * min(8.0, 15.0 / max(dt, 1e-3))))
-        dt = run(n_rows)
-    return {"value": n_rows * flop_row / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{n_rows} random query rows (all heads) of {w.name}, "
-                      f"{'causal' if causal else 'non-causal'}, fp64 two-pass softmax, {dt:.1f} s"}
+        dt, rows, o_ref, l_ref = run(n_rows)
+    baseline = {"value": n_rows * flop_row / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+                "kind": "oracle",
+                "sample": f"{n_rows} random query rows (all heads) of {w.name}, "
+                          f"{'causal' if causal else 'non-causal'}, fp64 two-pass softmax, {dt:.1f} s"}
+    # the timed run's outputs at those rows (flat row = (b*H + h)*N_q + i)
+    idx = torch.from_numpy(rows).to(o.device)
+    o_g = o.reshape(-1, w.d)[idx].float().cpu().double().numpy()
+    l_g = lse.reshape(-1)[idx].cpu().double().numpy()
+    d_o, d_l = np.abs(o_g - o_ref), np.abs(l_g - l_ref)
+    ok = bool(np.all(np.isfinite(o_g)) and np.all(np.isfinite(l_g)) and d_o.max() <= 1e-2 and d_l.max() <= 1e-3)
+    parity = {"rows": int(n_rows), "of_rows": int(total_rows), "max_abs_O": float(d_o.max()),
+              "max_abs_LSE": float(d_l.max()), "tol_O": 1e-2, "tol_LSE": 1e-3, "pass": ok,
+              "checked": "the timed run's O and LSE at the oracle rows of cpu_baseline"}
+    return baseline, parity
 
 
 def main():
@@ -335,8 +346,9 @@ def main():
         result["workloads"] = extra
 
     if not args.no_cpu and not args.fp8:  # the oracle baseline is the bf16 definition
-        result["cpu_baseline"] = cpu_baseline(w, causal, q, k, v)
+        result["cpu_baseline"], result["parity"] = cpu_baseline(w, causal, q, k, v, o, lse)
         log(f"oracle: {result['cpu_baseline']}")
+        log(f"parity of the timed run: {result['parity']}")
     result["env"] = env_info()
     print(json.dumps(result), flush=True)
 

@@ -120,6 +120,32 @@ def _check_inputs(q, k, v):
     return B, H, n_q, n_k, d
 
 
+def _check_out(t, name, shape, dtype, device):
+    """A caller-supplied output: exactly `shape` and `dtype`, contiguous, on `device`.  The
+    library sizes every write from the shape arguments, so anything else would be written out
+    of bounds or read back wrongly."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+    return t
+
+
+def _outputs(out, lse, B, H, n_q, d, device):
+    """O and LSE buffers: the caller's (validated) or new ones."""
+    if out is None:
+        out = torch.empty((B, H, n_q, d), dtype=torch.bfloat16, device=device)
+    else:
+        _check_out(out, "out", (B, H, n_q, d), torch.bfloat16, device)
+    if lse is None:
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=device)
+    else:
+        _check_out(lse, "lse", (B, H, n_q), torch.float32, device)
+    return out, lse
+
+
 def _scale(scale, d):
     return float(1.0 / math.sqrt(d)) if scale is None else float(scale)
 
@@ -136,10 +162,7 @@ def forward(q, k, v, causal: bool = False, scale=None, out=None, lse=None):
     enqueued on torch's current stream of q's device."""
     lib = load_library()
     B, H, n_q, n_k, d = _check_inputs(q, k, v)
-    if out is None:
-        out = torch.empty((B, H, n_q, d), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    out, lse = _outputs(out, lse, B, H, n_q, d, q.device)
     rc = lib.fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                      B, H, n_q, n_k, d, int(bool(causal)), _scale(scale, d), _stream_handle(q.device))
     _check(rc)
@@ -152,10 +175,7 @@ def forward_window(q, k, v, window_left: int, window_right: int, scale=None, out
     Returns (o, lse); rows that see no key get O = 0 and LSE = -inf."""
     lib = load_library()
     B, H, n_q, n_k, d = _check_inputs(q, k, v)
-    if out is None:
-        out = torch.empty((B, H, n_q, d), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    out, lse = _outputs(out, lse, B, H, n_q, d, q.device)
     rc = lib.fa2_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                             B, H, n_q, n_k, d, int(window_left), int(window_right), _scale(scale, d),
                             _stream_handle(q.device))
@@ -172,23 +192,25 @@ def forward_splitkv(q, k, v, num_splits: int = 16, causal: bool = False, scale=N
     """Same result as forward(), with the key sequence split into num_splits chunks
     (fp32 partials in a workspace, then a merge pass), via fa2_fwd_splitkv.
 
-    Returns (o, lse, workspace); the workspace holds the per-chunk partials
-    acc [S][R][d], then m, l and l_lse, each [S][R] (R = B*H*N_q), as fp32."""
+    Returns (o, lse).  A caller-supplied workspace (fp32, contiguous, on q's device, at least
+    splitkv_workspace_bytes() bytes) holds the per-chunk partials afterwards: acc [S][R][d],
+    then m and l, each [S][R] (R = B*H*N_q), with acc / l the chunk's output and m + log(l)
+    its log-sum-exp."""
     lib = load_library()
     B, H, n_q, n_k, d = _check_inputs(q, k, v)
     need = lib.fa2_splitkv_workspace_bytes(B, H, n_q, d, int(num_splits))
     if workspace is None:
         workspace = torch.empty((max(need, 4) + 3) // 4, dtype=torch.float32, device=q.device)
-    if out is None:
-        out = torch.empty((B, H, n_q, d), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    elif (not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.float32
+          or not workspace.is_contiguous() or workspace.device != q.device):
+        raise ValueError("workspace must be a contiguous fp32 tensor on q's device")
+    out, lse = _outputs(out, lse, B, H, n_q, d, q.device)
     rc = lib.fa2_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                              B, H, n_q, n_k, d, int(bool(causal)), _scale(scale, d), int(num_splits),
                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                              _stream_handle(q.device))
     _check(rc)
-    return out, lse, workspace
+    return out, lse
 
 
 def num_splits(B, H, n_q, n_k, d, num_cus: int = 0) -> int:
@@ -209,8 +231,7 @@ def attention(q, k, v, causal: bool = False, scale=None):
         s = num_splits(B, H, n_q, n_k, d, 0)
     if s == 1:
         return forward(q, k, v, causal=causal, scale=scale)
-    o, lse, _ = forward_splitkv(q, k, v, num_splits=s, causal=causal, scale=scale)
-    return o, lse
+    return forward_splitkv(q, k, v, num_splits=s, causal=causal, scale=scale)
 
 
 def bwd_workspace_bytes(B, H, n_q, n_k, d) -> int:
@@ -227,12 +248,17 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale=None, workspace=No
             raise ValueError(f"{name} must be a contiguous bf16 {shape} tensor on q's device")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, n_q) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous fp32 [B, H, N_q] tensor")
+    if lse.device != q.device:
+        raise ValueError("lse must be on q's device")
     need = lib.fa2_bwd_workspace_bytes(B, H, n_q, n_k, d)
     if workspace is None:
         workspace = torch.empty((max(need, 4) + 3) // 4, dtype=torch.float32, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    elif (not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.float32
+          or not workspace.is_contiguous() or workspace.device != q.device):
+        raise ValueError("workspace must be a contiguous fp32 tensor on q's device")
+    dq = torch.empty_like(q) if dq is None else _check_out(dq, "dq", q.shape, torch.bfloat16, q.device)
+    dk = torch.empty_like(k) if dk is None else _check_out(dk, "dk", k.shape, torch.bfloat16, q.device)
+    dv = torch.empty_like(v) if dv is None else _check_out(dv, "dv", v.shape, torch.bfloat16, q.device)
     rc = lib.fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, n_q, n_k, d, int(bool(causal)),
                      _scale(scale, d), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -290,10 +316,7 @@ def forward_fp8(qc, kc, vt, descale_q, descale_k, descale_v, causal: bool = Fals
     for name, t in (("descale_q", descale_q), ("descale_k", descale_k), ("descale_v", descale_v)):
         if t.dtype != torch.float32 or tuple(t.shape) != (B, H) or not t.is_contiguous() or t.device != qc.device:
             raise ValueError(f"{name} must be a contiguous fp32 [B, H] tensor on qc's device")
-    if out is None:
-        out = torch.empty((B, H, n_q, d), dtype=torch.bfloat16, device=qc.device)
-    if lse is None:
-        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=qc.device)
+    out, lse = _outputs(out, lse, B, H, n_q, d, qc.device)
     rc = lib.fa2_fwd_fp8(qc.data_ptr(), kc.data_ptr(), vt.data_ptr(), descale_q.data_ptr(), descale_k.data_ptr(),
                          descale_v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, n_q, n_k, d,
                          int(bool(causal)), _scale(scale, d), _stream_handle(qc.device))
@@ -319,10 +342,7 @@ def decode_fp8(qc, kc, vc, descale_q, descale_k, descale_v, scale=None, out=None
     for name, t in (("descale_q", descale_q), ("descale_k", descale_k), ("descale_v", descale_v)):
         if t.dtype != torch.float32 or tuple(t.shape) != (B, H) or not t.is_contiguous() or t.device != qc.device:
             raise ValueError(f"{name} must be a contiguous fp32 [B, H] tensor on qc's device")
-    if out is None:
-        out = torch.empty((B, H, 1, d), dtype=torch.bfloat16, device=qc.device)
-    if lse is None:
-        lse = torch.empty((B, H, 1), dtype=torch.float32, device=qc.device)
+    out, lse = _outputs(out, lse, B, H, 1, d, qc.device)
     rc = lib.fa2_decode_fp8(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), descale_q.data_ptr(),
                             descale_k.data_ptr(), descale_v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                             B, H, n_k, d, _scale(scale, d), _stream_handle(qc.device))

@@ -10,6 +10,7 @@
 namespace {
 
 constexpr long long kMaxGrid = (1LL << 31) - 1;
+constexpr long long kMaxItems = (1LL << 32) - 1;  // work-items per grid dimension of one dispatch
 constexpr long long kMaxHeadElems = (1LL << 30) - 1;  // one head's Q or K/V below 2^31 bytes
 constexpr int kMaxWindow = 1 << 30;                   // keeps row +- window inside int
 
@@ -54,6 +55,20 @@ int check_alias(const void* Q, const void* K, const void* V, const void* O, cons
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A 1-D launch of `blocks` workgroups of `threads` work-items fits one dispatch:
+// below 2^31 workgroups and below 2^32 work-items (the dispatch packet's grid
+// size is a 32-bit count of work-items).  blocks is checked first, so the
+// product cannot overflow.
+bool launch_fits(long long blocks, long long threads) { return blocks <= kMaxGrid && blocks * threads <= kMaxItems; }
+
+// The launches of one forward (fa2_fwd, fa2_fwd_window, the FP8 forward): the
+// 4-wave tile kernel takes ceil(N_q/128)*B*H workgroups of 256 work-items; the
+// 8-wave kernel (256 rows, 512 work-items) and the single-row decode kernel
+// (B*H workgroups of 256) never launch more work-items than that.
+bool fwd_fits(int B, int H, int N_q) {
+  return launch_fits((long long)((N_q + 127) / 128) * B * H, 256);
+}
+
 fa2::FwdParams make_params(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q,
                            int N_k, int d, int causal, float scale) {
   fa2::FwdParams p{};
@@ -77,14 +92,45 @@ fa2::FwdParams make_params(const void* Q, const void* K, const void* V, void* O,
 
 }  // namespace
 
+namespace fa2 {
+
+int splitkv_check_args(const void* Q, const void* K, const void* V, const void* O, const float* LSE, int B, int H,
+                       int N_q, int N_k, int d, float scale, int num_splits) {
+  int rc = check_common(Q, K, V, O, LSE, B, H, N_q, N_k, d, scale);
+  if (rc != FA2_OK) return rc;
+  if (num_splits < 1 || num_splits > FA2_MAX_SPLITS || num_splits > N_k) return FA2_ERR_SPLITS;
+  // partial pass: ceil(N_q/128)*B*H*S workgroups of 256 (tile kernel) or B*H*S of 256 (decode);
+  // merge pass: one wave per query row, four rows per workgroup of 256
+  if (!launch_fits((long long)((N_q + 127) / 128) * B * H * num_splits, 256) ||
+      !launch_fits(((long long)B * H * N_q + 3) / 4, 256))
+    return FA2_ERR_BAD_SHAPE;
+  return check_alias(Q, K, V, O, LSE, B, H, N_q, N_k, d, nullptr, 0);
+}
+
+int splitkv_run(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q, int N_k,
+                int d, int causal, float scale, int num_splits, float* ws, void* stream) {
+  FwdParams p = make_params(Q, K, V, O, LSE, B, H, N_q, N_k, d, causal, scale);
+  p.num_splits = num_splits;
+  p.split_len = (N_k + num_splits - 1) / num_splits;
+  const long long R = (long long)B * H * N_q;
+  p.ws_acc = ws;
+  p.ws_m = ws + (long long)num_splits * R * d;
+  p.ws_l = p.ws_m + (long long)num_splits * R;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_splitkv_partial(p, s) != hipSuccess) return FA2_ERR_HIP;
+  if (launch_splitkv_merge(p, s) != hipSuccess) return FA2_ERR_HIP;
+  return FA2_OK;
+}
+
+}  // namespace fa2
+
 extern "C" {
 
 int fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q, int N_k, int d,
             int causal, float scale, void* stream) {
   int rc = check_common(Q, K, V, O, LSE, B, H, N_q, N_k, d, scale);
   if (rc != FA2_OK) return rc;
-  const int br = 128;  // query rows per workgroup of the forward kernel
-  if ((long long)((N_q + br - 1) / br) * B * H > kMaxGrid) return FA2_ERR_BAD_SHAPE;
+  if (!fwd_fits(B, H, N_q)) return FA2_ERR_BAD_SHAPE;
   rc = check_alias(Q, K, V, O, LSE, B, H, N_q, N_k, d, nullptr, 0);
   if (rc != FA2_OK) return rc;
   const fa2::FwdParams p = make_params(Q, K, V, O, LSE, B, H, N_q, N_k, d, causal, scale);
@@ -98,8 +144,7 @@ int fa2_fwd_window(const void* Q, const void* K, const void* V, void* O, float* 
   if (rc != FA2_OK) return rc;
   if (window_left < -1 || window_right < -1 || window_left > kMaxWindow || window_right > kMaxWindow)
     return FA2_ERR_WINDOW;
-  const int br = 128;
-  if ((long long)((N_q + br - 1) / br) * B * H > kMaxGrid) return FA2_ERR_BAD_SHAPE;
+  if (!fwd_fits(B, H, N_q)) return FA2_ERR_BAD_SHAPE;
   rc = check_alias(Q, K, V, O, LSE, B, H, N_q, N_k, d, nullptr, 0);
   if (rc != FA2_OK) return rc;
   fa2::FwdParams p = make_params(Q, K, V, O, LSE, B, H, N_q, N_k, d, 0, scale);
@@ -111,35 +156,20 @@ int fa2_fwd_window(const void* Q, const void* K, const void* V, void* O, float* 
 
 size_t fa2_splitkv_workspace_bytes(int B, int H, int N_q, int d, int num_splits) {
   if (B < 1 || H < 1 || N_q < 1 || d < 1 || num_splits < 1 || num_splits > FA2_MAX_SPLITS) return 0;
-  return (size_t)num_splits * (size_t)B * (size_t)H * (size_t)N_q * (size_t)(d + 3) * 4u;
+  return (size_t)num_splits * (size_t)B * (size_t)H * (size_t)N_q * (size_t)(d + 2) * 4u;
 }
 
 int fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q, int N_k,
                     int d, int causal, float scale, int num_splits, void* workspace, size_t workspace_bytes,
                     void* stream) {
-  int rc = check_common(Q, K, V, O, LSE, B, H, N_q, N_k, d, scale);
+  int rc = fa2::splitkv_check_args(Q, K, V, O, LSE, B, H, N_q, N_k, d, scale, num_splits);
   if (rc != FA2_OK) return rc;
-  if (num_splits < 1 || num_splits > FA2_MAX_SPLITS || num_splits > N_k) return FA2_ERR_SPLITS;
-  const int br = 128;
-  if ((long long)((N_q + br - 1) / br) * B * H * num_splits > kMaxGrid) return FA2_ERR_BAD_SHAPE;
   const size_t need = fa2_splitkv_workspace_bytes(B, H, N_q, d, num_splits);
   if (!workspace || workspace_bytes < need) return FA2_ERR_WORKSPACE;
   rc = check_alias(Q, K, V, O, LSE, B, H, N_q, N_k, d, workspace, need);
   if (rc != FA2_OK) return rc;
-
-  fa2::FwdParams p = make_params(Q, K, V, O, LSE, B, H, N_q, N_k, d, causal, scale);
-  p.num_splits = num_splits;
-  p.split_len = (N_k + num_splits - 1) / num_splits;
-  const long long R = (long long)B * H * N_q;
-  float* ws = static_cast<float*>(workspace);
-  p.ws_acc = ws;
-  p.ws_m = ws + (long long)num_splits * R * d;
-  p.ws_l = p.ws_m + (long long)num_splits * R;
-  p.ws_ll = p.ws_l + (long long)num_splits * R;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (fa2::launch_splitkv_partial(p, s) != hipSuccess) return FA2_ERR_HIP;
-  if (fa2::launch_splitkv_merge(p, s) != hipSuccess) return FA2_ERR_HIP;
-  return FA2_OK;
+  return fa2::splitkv_run(Q, K, V, O, LSE, B, H, N_q, N_k, d, causal, scale, num_splits,
+                          static_cast<float*>(workspace), stream);
 }
 
 int fa2_num_splits(int B, int H, int N_q, int N_k, int d, int num_cus) {
@@ -182,7 +212,12 @@ int fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const vo
   // the forward's own checks on Q, K, V, O, LSE (LSE read-only here)
   int rc = check_common(Q, K, V, O, LSE, B, H, N_q, N_k, d, scale);
   if (rc != FA2_OK) return rc;
-  if (fa2::bwd_num_slots(B, H, N_k) * B * H > kMaxGrid) return FA2_ERR_BAD_SHAPE;  // workgroups
+  // the three launches: D and LSE*log2e (256 work-items per 256/(d/8) rows), the key-block
+  // groups (one workgroup of 256 per group), the dQ reduction (one work-item per 4 elements)
+  const long long R_all = (long long)B * H * N_q;
+  if (!launch_fits((R_all + 256 / (d / 8) - 1) / (256 / (d / 8)), 256) ||
+      !launch_fits(fa2::bwd_num_slots(B, H, N_k) * B * H, 256) || !launch_fits((R_all * (d / 4) + 255) / 256, 256))
+    return FA2_ERR_BAD_SHAPE;
   const size_t need = fa2_bwd_workspace_bytes(B, H, N_q, N_k, d);
   if (!workspace || workspace_bytes < need) return FA2_ERR_WORKSPACE;
   // outputs must not overlap any input, each other or the workspace
@@ -233,6 +268,8 @@ int fa2_quantize_fp8(const void* X, void* codes, float* descale, int B, int H, i
   if (!X || !codes || !descale) return FA2_ERR_NULLPTR;
   if (B < 1 || H < 1 || N < 1) return FA2_ERR_BAD_SHAPE;
   if (d != 64 && d != 128) return FA2_ERR_HEAD_DIM;
+  // two-dimensional launches (blocks per head, B*H): B*H is the y dimension, and with one head
+  // below 2^30 elements no x dimension reaches 2^32 work-items
   if ((long long)N * d > kMaxHeadElems || (long long)B * H > 65535) return FA2_ERR_BAD_SHAPE;
   if (!aligned16(X) || !aligned16(codes) || !aligned16(descale)) return FA2_ERR_ALIGN;
   const long long bh = (long long)B * H;
@@ -260,8 +297,7 @@ int fa2_fwd_fp8(const void* Qc, const void* Kc, const void* Vt, const float* des
   if (!descale_q || !descale_k || !descale_v) return FA2_ERR_NULLPTR;
   int rc = check_common(Qc, Kc, Vt, O, LSE, B, H, N_q, N_k, d, scale);
   if (rc != FA2_OK) return rc;
-  const int br = 128;
-  if ((long long)((N_q + br - 1) / br) * B * H > kMaxGrid) return FA2_ERR_BAD_SHAPE;
+  if (!fwd_fits(B, H, N_q)) return FA2_ERR_BAD_SHAPE;
   const void* ptrs[8] = {Qc, Kc, Vt, descale_q, descale_k, descale_v, O, LSE};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return FA2_ERR_ALIGN;
@@ -301,6 +337,7 @@ int fa2_decode_fp8(const void* Qc, const void* Kc, const void* Vc, const float* 
   if (!descale_q || !descale_k || !descale_v) return FA2_ERR_NULLPTR;
   int rc = check_common(Qc, Kc, Vc, O, LSE, B, H, 1, N_k, d, scale);
   if (rc != FA2_OK) return rc;
+  if (!launch_fits((long long)B * H, 256)) return FA2_ERR_BAD_SHAPE;
   const void* ptrs[8] = {Qc, Kc, Vc, descale_q, descale_k, descale_v, O, LSE};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return FA2_ERR_ALIGN;

@@ -392,20 +392,23 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
       }
     if (hf == 0) p.lse[(long long)bh * p.n_q + row] = l_tot > 0.f ? (w.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
+    // partial (acc, m, l) with l the fp32 sum: acc is rescaled by l / l16 so that acc / l is
+    // the chunk's output exactly as normalised by its bf16 probabilities (0 for an empty chunk)
     const long long R = (long long)p.B * p.H * p.n_q;
     const long long rg = (long long)bh * p.n_q + row;
+    const float rescale = l16_tot > 0.f ? l_tot / l16_tot : 0.f;
     float* wa = p.ws_acc + ((long long)split * R + rg) * D;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 o4 = {w.acc[nb][4 * g], w.acc[nb][4 * g + 1], w.acc[nb][4 * g + 2], w.acc[nb][4 * g + 3]};
+        const f32x4 o4 = {w.acc[nb][4 * g] * rescale, w.acc[nb][4 * g + 1] * rescale,
+                          w.acc[nb][4 * g + 2] * rescale, w.acc[nb][4 * g + 3] * rescale};
         *reinterpret_cast<f32x4*>(wa + 32 * nb + 8 * g + 4 * hf) = o4;
       }
     if (hf == 0) {
       p.ws_m[split * R + rg] = w.m_run == -INFINITY ? -INFINITY : w.m_run * kLn2;
-      p.ws_l[split * R + rg] = l16_tot;
-      p.ws_ll[split * R + rg] = l_tot;
+      p.ws_l[split * R + rg] = l_tot;
     }
   }
 }
@@ -562,13 +565,13 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(FwdParams p
   }
   if (tid == 0) {
     p.ws_m[split * R + bh] = M == -INFINITY ? -INFINITY : M * kLn2;
-    p.ws_l[split * R + bh] = lsum;   // P is used in fp32 here: one sum serves both
-    p.ws_ll[split * R + bh] = lsum;
+    p.ws_l[split * R + bh] = lsum;   // P is used in fp32 here, so acc / lsum is the chunk's output
   }
 }
 
 // ---------------------------------------------------------------------------
-// Split-KV merge: one wave per query row, chunks combined in order 0..S-1.
+// Split-KV merge: one wave per query row, chunks combined in order 0..S-1:
+// O = sum_c w_c acc_c / sum_c w_c l_c, LSE = M + ln sum_c w_c l_c, w_c = exp(m_c - M).
 template <int D>
 __global__ void __launch_bounds__(256) splitkv_merge_kernel(FwdParams p) {
   constexpr int PER = D / 64;  // head-dim elements per lane
@@ -584,13 +587,12 @@ __global__ void __launch_bounds__(256) splitkv_merge_kernel(FwdParams p) {
   float o[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.f;
-  float lsum = 0.f, llsum = 0.f;
+  float lsum = 0.f;
   for (int c = 0; c < S; ++c) {
     const float mc = p.ws_m[c * R + rg];
     if (mc == -INFINITY) continue;  // empty chunk
     const float w = __builtin_amdgcn_exp2f((mc - M) * kLog2e);
     lsum += w * p.ws_l[c * R + rg];
-    llsum += w * p.ws_ll[c * R + rg];
     const float* a = p.ws_acc + (c * R + rg) * D;
 #pragma unroll
     for (int i = 0; i < PER; ++i) o[i] += w * a[lane + 64 * i];
@@ -602,7 +604,7 @@ __global__ void __launch_bounds__(256) splitkv_merge_kernel(FwdParams p) {
     const __bf16 b = (__bf16)(o[i] * inv);
     orow[lane + 64 * i] = __builtin_bit_cast(uint16_t, b);
   }
-  if (lane == 0) p.lse[rg] = llsum > 0.f ? M + __logf(llsum) : -INFINITY;
+  if (lane == 0) p.lse[rg] = lsum > 0.f ? M + __logf(lsum) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------

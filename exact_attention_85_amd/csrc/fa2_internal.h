@@ -15,10 +15,9 @@ struct FwdParams {
   const uint16_t* v;
   uint16_t* o;       // bf16 output (forward mode)
   float* lse;        // fp32 natural-log LSE (forward mode)
-  float* ws_acc;     // split mode: [S][R][d] unnormalised accumulators
-  float* ws_m;       // split mode: [S][R] chunk reference maxima (natural-log units)
-  float* ws_l;       // split mode: [S][R] sums of the probabilities as accumulated in acc
-  float* ws_ll;      // split mode: [S][R] fp32 sums of the probabilities (for LSE)
+  float* ws_acc;     // split mode: [S][R][d] l * (the chunk's normalised output)
+  float* ws_m;       // split mode: [S][R] chunk reference levels (natural-log units)
+  float* ws_l;       // split mode: [S][R] fp32 sums of exp(s - m)
   int B, H, n_q, n_k, d;
   int wl, wr;        // key band [i - wl, i + wr] of query i (top-left aligned); -1: unbounded.
                      // Plain attention is (-1, -1), the causal mask (-1, 0).
@@ -95,6 +94,14 @@ struct QuantParams {
   int transposed;
   int vt_stride;
 };
+
+// Split-KV forward, host side (fa2_api.cpp): every check of fa2_fwd_splitkv except those of the
+// workspace, with no HIP call (returns FA2_OK or a negative fa2_status); then the two passes
+// over an fp32 workspace of fa2_splitkv_workspace_bytes() bytes (FA2_OK or FA2_ERR_HIP).
+int splitkv_check_args(const void* Q, const void* K, const void* V, const void* O, const float* LSE, int B, int H,
+                       int N_q, int N_k, int d, float scale, int num_splits);
+int splitkv_run(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q, int N_k,
+                int d, int causal, float scale, int num_splits, float* ws, void* stream);
 
 // Forward: O, LSE.  Returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);

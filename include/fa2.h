@@ -50,14 +50,16 @@ typedef enum fa2_status {
   FA2_ERR_BAD_SCALE = -4, /* scale is not finite */
   FA2_ERR_WORKSPACE = -5, /* split-KV workspace NULL or smaller than fa2_splitkv_workspace_bytes() */
   FA2_ERR_ALIAS = -6,     /* an output overlaps an input, another output or the workspace */
-  FA2_ERR_SPLITS = -7,    /* num_splits outside [1, min(N_k, FA2_MAX_SPLITS)] */
-  FA2_ERR_HIP = -8,       /* the HIP runtime rejected a kernel launch */
+  FA2_ERR_HIP = -7,       /* the HIP runtime rejected a kernel launch */
+  FA2_ERR_SPLITS = -8,    /* num_splits outside [1, min(N_k, FA2_MAX_SPLITS)] */
   FA2_ERR_WINDOW = -9,    /* a window size below -1 or above 2^30 */
   FA2_ERR_ALIGN = -10     /* an FP8 entry point's tensor pointer is not 16-byte aligned */
 } fa2_status;
 
 /* Size limits (validated): N_k * d and N_q * d below 2^30 per head (one
- * head's Q, K or V under 2 GiB), and the launch grid below 2^31 workgroups. */
+ * head's Q, K or V under 2 GiB); every launch below 2^31 workgroups and
+ * below 2^32 work-items in all (workgroups x threads per workgroup).
+ * Shapes beyond them return FA2_ERR_BAD_SHAPE with nothing enqueued. */
 #define FA2_MAX_SPLITS 256
 
 /*
@@ -107,7 +109,7 @@ int fa2_fwd_window(const void* Q, const void* K, const void* V, void* O, float* 
 
 /*
  * fa2_splitkv_workspace_bytes — bytes of caller-owned device workspace that
- * fa2_fwd_splitkv needs: num_splits * B * H * N_q * (d + 3) * 4.
+ * fa2_fwd_splitkv needs: num_splits * B * H * N_q * (d + 2) * 4.
  * Returns 0 when an argument is out of range.
  */
 size_t fa2_splitkv_workspace_bytes(int B, int H, int N_q, int d, int num_splits);
@@ -120,22 +122,22 @@ size_t fa2_splitkv_workspace_bytes(int B, int H, int N_q, int d, int num_splits)
  *
  * Chunk c covers keys [c*L, min((c+1)*L, N_k)), L = ceil(N_k / num_splits);
  * a chunk may be empty.  Pass 1 writes, per chunk and query row, the fp32
- * partial (acc, m, l, l_lse) into the workspace:
- *   m     = a reference level in natural-log units: the running maximum of
- *           the chunk's visible scaled scores s_ij at its last refresh (at most
- *           the true maximum; -inf exactly when the chunk holds no visible key);
- *   acc   = sum over the chunk of p_ij * V[j], p_ij = exp(s_ij - m) as used in
- *           the P.V product (0 when empty);
- *   l     = sum of the same p_ij                          (0 when empty);
- *   l_lse = sum of exp(s_ij - m) in fp32                  (0 when empty).
- * Pass 2 merges them in chunk order: M = max_c m_c, w_c = exp(m_c - M)
- * (0 for an empty chunk), O = (sum_c w_c acc_c) / (sum_c w_c l_c),
- * LSE = M + log(sum_c w_c l_lse_c) — the same rescaling as the online
- * softmax (walkthrough page, main-loop pseudocode).  acc / l and
- * m + log(l_lse) do not depend on the reference m.
+ * partial (acc, m, l) into the workspace:
+ *   m   = a reference level in natural-log units: the running maximum of the
+ *         chunk's visible scaled scores s_ij at its last refresh (at most the
+ *         true maximum; -inf exactly when the chunk holds no visible key);
+ *   l   = sum over the chunk of exp(s_ij - m), in fp32           (0 when empty);
+ *   acc = l * (the chunk's normalised output): acc / l is the chunk's
+ *         attention output exactly as the P.V product formed it, a convex
+ *         combination of the chunk's V rows                        (0 when empty).
+ * So acc / l and m + log(l) (the chunk's log-sum-exp) do not depend on the
+ * reference m.  Pass 2 merges them in chunk order: M = max_c m_c,
+ * w_c = exp(m_c - M) (0 for an empty chunk), O = (sum_c w_c acc_c) /
+ * (sum_c w_c l_c), LSE = M + log(sum_c w_c l_c) — the same rescaling as the
+ * online softmax (walkthrough page, main-loop pseudocode).
  *
  * Workspace layout (fp32, R = B*H*N_q rows, row = (b*H + h)*N_q + i):
- *   acc [num_splits][R][d], then m, l and l_lse, each [num_splits][R].
+ *   acc [num_splits][R][d], then m and l, each [num_splits][R].
  * Its contents after the call are the partials above; it must not overlap
  * any input or output.  Both passes run in order on `stream`.
  *

@@ -78,6 +78,62 @@ def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, tol_o=TOL_O, tol_lse=TOL_LSE, w
     return float(do.max()), float(dl[il])
 
 
+def balanced_order(n):
+    """0, n-1, 1, n-2, ...: under the causal mask row i costs i+1 keys, so consecutive pairs cost
+    the same and the oracle's static split of the row list over its threads stays even."""
+    i = np.arange(n, dtype=np.int64)
+    out = np.empty(n, dtype=np.int64)
+    out[0::2] = i[: (n + 1) // 2]
+    out[1::2] = (n - 1 - i)[: n // 2]
+    return out
+
+
+def assert_all_rows(q, k, v, o, lse, causal, scale, what, heads_per_call=4, tol_o=TOL_O, tol_lse=TOL_LSE):
+    """Every row of a GPU result (o [B,H,N_q,d] bf16, lse [B,H,N_q] fp32) against the oracle.
+
+    The oracle runs on the bf16 bits of q, k, v, a few heads per call, so host memory stays
+    bounded; each call takes all rows of its heads.  Reports max|dO| and max|dLSE| with their
+    (b, h, i, c) locations, the reference value there, the mean error and the count over the
+    tolerance, and asserts max|dO| <= tol_o, max|dLSE| <= tol_lse and no NaN."""
+    B, H, n_q, d = q.shape
+    worst_o = (-1.0, None, 0.0)
+    worst_l = (-1.0, None, 0.0)
+    sum_o, n_el, over_o, over_l = 0.0, 0, 0, 0
+    order = balanced_order(n_q)
+    for b in range(B):
+        kb = workloads.bf16_bits(k[b][None])
+        vb = workloads.bf16_bits(v[b][None])
+        qb = workloads.bf16_bits(q[b][None])
+        og = o[b].float().cpu().double().numpy()
+        lg = lse[b].cpu().double().numpy()
+        for h0 in range(0, H, heads_per_call):
+            h1 = min(H, h0 + heads_per_call)
+            rows = (np.arange(h0, h1, dtype=np.int64)[:, None] * n_q + order[None, :]).reshape(-1)
+            o_ref, l_ref = oracle.attention_rows_bf16(qb, kb, vb, rows, causal, scale)
+            hh, ii = rows // n_q, rows % n_q
+            o_g, l_g = og[hh, ii], lg[hh, ii]
+            if not (np.all(np.isfinite(o_g)) and np.all(np.isfinite(l_g))):
+                raise AssertionError(f"{what}: non-finite output in batch {b}, heads {h0}..{h1 - 1}")
+            do = np.abs(o_g - o_ref)
+            dl = np.abs(l_g - l_ref)
+            sum_o += float(do.sum())
+            n_el += do.size
+            over_o += int((do > tol_o).sum())
+            over_l += int((dl > tol_lse).sum())
+            r, c = np.unravel_index(np.argmax(do), do.shape)
+            if do[r, c] > worst_o[0]:
+                worst_o = (float(do[r, c]), (b, int(hh[r]), int(ii[r]), int(c)), float(o_ref[r, c]))
+            r = int(np.argmax(dl))
+            if dl[r] > worst_l[0]:
+                worst_l = (float(dl[r]), (b, int(hh[r]), int(ii[r])), float(l_ref[r]))
+    msg = (f"{what}: all {B * H * n_q} rows: max|dO|={worst_o[0]:.3e} at (b,h,i,c)={worst_o[1]} "
+           f"(ref {worst_o[2]:.4f}), mean|dO|={sum_o / n_el:.2e}, over {tol_o}: {over_o}; "
+           f"max|dLSE|={worst_l[0]:.3e} at (b,h,i)={worst_l[1]} (ref {worst_l[2]:.4f}), over {tol_lse}: {over_l}")
+    print(msg, flush=True)
+    assert worst_o[0] <= tol_o and worst_l[0] <= tol_lse, msg
+    return worst_o[0], worst_l[0]
+
+
 def sample_rows(B, H, n_q, n, seed, block=128):
     """Rows (b, h, i): every head's first and last row, rows at query-block
     boundaries, and n random rows."""

@@ -268,13 +268,34 @@ def pin_p9_invariants(orc):
         assert np.array_equal(lse_r, lse_full.reshape(-1)[rows])
 
 
-def recurrence_model(q, k, v, causal, scale, block_r, block_c):
-    """The pages' tiled online recurrence (FlashAttention-2 walkthrough page,
-    main-loop pseudocode), in float64, one (b, h) at a time:
-    per query block, m = -inf, l = 0, acc = 0; per key block S = scale*Q K^T,
-    mask, m_new = max(m, rowmax S), P = exp(S - m_new),
-    acc = acc*exp(m - m_new) + P V, l = l*exp(m - m_new) + rowsum P; finally
-    O = acc / l and LSE = m + ln l."""
+def _block_state(s, vb):
+    """Softmax state (m, l, a) of one block of scores s [rows, keys] (-inf where not visible)
+    and its values vb [keys, d]: m = row maximum, l = sum exp(s - m), a = sum exp(s - m) v.
+    A row with no visible key is the empty state (-inf, 0, 0)."""
+    m = s.max(axis=1)
+    shift = np.where(np.isneginf(m), 0.0, m)
+    e = np.exp(s - shift[:, None])
+    return m, e.sum(axis=1), e @ vb
+
+
+def _combine(x, y):
+    """The associative combination of two softmax states over disjoint key sets: both are
+    brought to the larger maximum.  The empty state is its identity."""
+    (m1, l1, a1), (m2, l2, a2) = x, y
+    m = np.maximum(m1, m2)
+    shift = np.where(np.isneginf(m), 0.0, m)
+    w1, w2 = np.exp(m1 - shift), np.exp(m2 - shift)
+    return m, w1 * l1 + w2 * l2, w1[:, None] * a1 + w2[:, None] * a2
+
+
+def blockwise_model(q, k, v, visible, scale, block_r, block_c):
+    """Attention assembled from tiles, the decomposition the kernels rely on (FlashAttention-2
+    walkthrough page, kernel main loop section: per query block, key/value blocks are folded into a
+    running maximum, sum and accumulator, and O and the log-sum-exp come out at the end).  Here
+    every (query block, key block) tile yields its own state, and the states of a query block are
+    combined pairwise as a balanced tree rather than left to right, so the check rests on the
+    associativity of the combination rather than on one order of it.  visible(rows, cols) is the
+    boolean mask of a tile.  Rows that see no key get O = 0 and LSE = -inf."""
     B, H, n_q, d = q.shape
     n_k = k.shape[2]
     o = np.zeros((B, H, n_q, d))
@@ -283,25 +304,27 @@ def recurrence_model(q, k, v, causal, scale, block_r, block_c):
         for h in range(H):
             for r0 in range(0, n_q, block_r):
                 r1 = min(r0 + block_r, n_q)
-                m = np.full(r1 - r0, -np.inf)
-                l_ = np.zeros(r1 - r0)
-                acc = np.zeros((r1 - r0, d))
+                rows = np.arange(r0, r1)[:, None]
+                states = []
                 for c0 in range(0, n_k, block_c):
                     c1 = min(c0 + block_c, n_k)
                     s = scale * (q[b, h, r0:r1] @ k[b, h, c0:c1].T)
-                    if causal:
-                        rows = np.arange(r0, r1)[:, None]
-                        cols = np.arange(c0, c1)[None, :]
-                        s = np.where(cols <= rows, s, -np.inf)
-                    m_new = np.maximum(m, s.max(axis=1))
-                    p = np.exp(s - m_new[:, None])
-                    alpha = np.exp(m - m_new)
-                    acc = acc * alpha[:, None] + p @ v[b, h, c0:c1]
-                    l_ = l_ * alpha + p.sum(axis=1)
-                    m = m_new
-                o[b, h, r0:r1] = acc / l_[:, None]
-                lse[b, h, r0:r1] = m + np.log(l_)
+                    s = np.where(visible(rows, np.arange(c0, c1)[None, :]), s, -np.inf)
+                    states.append(_block_state(s, v[b, h, c0:c1]))
+                while len(states) > 1:
+                    states = [_combine(states[i], states[i + 1]) if i + 1 < len(states) else states[i]
+                              for i in range(0, len(states), 2)]
+                m, l_, a = states[0]
+                seen = l_ > 0
+                o[b, h, r0:r1] = np.where(seen[:, None], a / np.where(seen, l_, 1.0)[:, None], 0.0)
+                lse[b, h, r0:r1] = np.where(seen, m + np.log(np.where(seen, l_, 1.0)), -np.inf)
     return o, lse
+
+
+def recurrence_model(q, k, v, causal, scale, block_r, block_c):
+    """blockwise_model under the causal (top-left) mask, or none."""
+    return blockwise_model(q, k, v, (lambda r, c: c <= r) if causal else (lambda r, c: np.ones(
+        np.broadcast_shapes(r.shape, c.shape), dtype=bool)), scale, block_r, block_c)
 
 
 def pin_p10_recurrence(orc):
@@ -408,41 +431,16 @@ def pin_p13_window_torch(orc):
 
 
 def window_recurrence_model(q, k, v, wl, wr, scale, block_r, block_c):
-    """The tiled online recurrence of recurrence_model with the band mask applied
-    per tile; rows that never see a key end with O = 0 and LSE = -inf."""
-    B, H, n_q, d = q.shape
-    n_k = k.shape[2]
-    o = np.zeros((B, H, n_q, d))
-    lse = np.zeros((B, H, n_q))
-    for b in range(B):
-        for h in range(H):
-            for r0 in range(0, n_q, block_r):
-                r1 = min(r0 + block_r, n_q)
-                m = np.full(r1 - r0, -np.inf)
-                l_ = np.zeros(r1 - r0)
-                acc = np.zeros((r1 - r0, d))
-                for c0 in range(0, n_k, block_c):
-                    c1 = min(c0 + block_c, n_k)
-                    s = scale * (q[b, h, r0:r1] @ k[b, h, c0:c1].T)
-                    rows = np.arange(r0, r1)[:, None]
-                    cols = np.arange(c0, c1)[None, :]
-                    vis = np.ones_like(s, dtype=bool)
-                    if wl >= 0:
-                        vis &= cols >= rows - wl
-                    if wr >= 0:
-                        vis &= cols <= rows + wr
-                    s = np.where(vis, s, -np.inf)
-                    m_new = np.maximum(m, s.max(axis=1))
-                    m_use = np.where(np.isneginf(m_new), 0.0, m_new)
-                    p = np.exp(s - m_use[:, None])
-                    alpha = np.exp(m - m_use)
-                    acc = acc * alpha[:, None] + p @ v[b, h, c0:c1]
-                    l_ = l_ * alpha + p.sum(axis=1)
-                    m = m_new
-                seen = l_ > 0
-                o[b, h, r0:r1] = np.where(seen[:, None], acc / np.where(seen, l_, 1.0)[:, None], 0.0)
-                lse[b, h, r0:r1] = np.where(seen, m + np.log(np.where(seen, l_, 1.0)), -np.inf)
-    return o, lse
+    """blockwise_model under the band mask: key j visible to query i iff (wl < 0 or j >= i - wl)
+    and (wr < 0 or j <= i + wr)."""
+    def visible(r, c):
+        vis = np.ones(np.broadcast_shapes(r.shape, c.shape), dtype=bool)
+        if wl >= 0:
+            vis &= c >= r - wl
+        if wr >= 0:
+            vis &= c <= r + wr
+        return vis
+    return blockwise_model(q, k, v, visible, scale, block_r, block_c)
 
 
 def pin_p14_window_recurrence(orc):

@@ -92,7 +92,7 @@ static void test_window() {
 static void test_splitkv() {
   void *Q = dev(0), *K = dev(1), *V = dev(2), *O = dev(3), *W = dev(5);
   float* L = devf(4);
-  CHECK(fa2_splitkv_workspace_bytes(64, 32, 1, 128, 16) == (size_t)16 * 64 * 32 * 131 * 4);
+  CHECK(fa2_splitkv_workspace_bytes(64, 32, 1, 128, 16) == (size_t)16 * 64 * 32 * 130 * 4);
   CHECK(fa2_splitkv_workspace_bytes(1, 1, 1, 64, 0) == 0);
   CHECK(fa2_splitkv_workspace_bytes(1, 1, 1, 64, FA2_MAX_SPLITS + 1) == 0);
   CHECK(fa2_splitkv_workspace_bytes(INT32_MAX, INT32_MAX, INT32_MAX, 128, FA2_MAX_SPLITS) > 0);
@@ -109,9 +109,17 @@ static void test_splitkv() {
   const long long R = 2 * 4 * 3;
   float* ws = static_cast<float*>(W);
   CHECK(p.num_splits == 5 && p.split_len == 20 && p.wr == 0);
-  // acc [S][R][d], then m, l and the fp32 sums [S][R] each, ending exactly at the workspace size
-  CHECK(p.ws_acc == ws && p.ws_m == ws + 5 * R * 64 && p.ws_l == p.ws_m + 5 * R && p.ws_ll == p.ws_l + 5 * R);
-  CHECK((size_t)((char*)(p.ws_ll + 5 * R) - (char*)ws) == need);
+  // acc [S][R][d], then m and l [S][R] each, ending exactly at the workspace size
+  CHECK(p.ws_acc == ws && p.ws_m == ws + 5 * R * 64 && p.ws_l == p.ws_m + 5 * R);
+  CHECK((size_t)((char*)(p.ws_l + 5 * R) - (char*)ws) == need);
+  // 2^20 heads of one query row in 16 chunks: 2^24 decode workgroups of 256 work-items, one past
+  // the 2^32 work-items of a dispatch; 2^20 - 1 heads fit
+  const int c1 = stub::rec.calls;
+  CHECK(fa2_fwd_splitkv(Q, K, V, O, L, 1 << 10, 1 << 10, 1, 16, 128, 0, 0.1f, 16, W,
+                        fa2_splitkv_workspace_bytes(1 << 10, 1 << 10, 1, 128, 16), nullptr) == FA2_ERR_BAD_SHAPE);
+  CHECK(stub::rec.calls == c1);
+  CHECK(fa2_fwd_splitkv(Q, K, V, O, L, (1 << 20) - 1, 1, 1, 16, 128, 0, 0.1f, 16, W,
+                        fa2_splitkv_workspace_bytes((1 << 20) - 1, 1, 1, 128, 16), nullptr) == FA2_OK);
 }
 
 static void test_num_splits() {

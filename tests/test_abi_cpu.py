@@ -12,7 +12,7 @@ import exact_attention_85_amd as fa2
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa2.h")
 
-OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, SPLITS, HIP, WINDOW, ALIGN = (
+OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, HIP, SPLITS, WINDOW, ALIGN = (
     0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10)
 
 
@@ -24,8 +24,22 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_decode_fp8", "fa2_fp8_vt_stride", "fa2_fwd",
-                                    "fa2_fwd_fp8", "fa2_fwd_splitkv", "fa2_fwd_window", "fa2_num_splits",
-                                    "fa2_quantize_fp8", "fa2_splitkv_workspace_bytes", "fa2_status_string"]
+                                    "fa2_fwd_fp8", "fa2_fwd_splitkv", "fa2_fwd_window",
+                                    "fa2_num_splits", "fa2_quantize_fp8", "fa2_splitkv_workspace_bytes",
+                                    "fa2_status_string"]
+
+
+def test_status_codes_pinned():
+    # the seven codes of the boundary's contract keep their values (FA2_ERR_HIP is -7);
+    # the codes added for later entry points follow them
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef enum fa2_status \{(.*?)\} fa2_status;", text, flags=re.S).group(1)
+    codes = {name: int(val) for name, val in re.findall(r"(FA2_[A-Z_]+)\s*=\s*(-?\d+)", body)}
+    assert codes == {"FA2_OK": 0, "FA2_ERR_NULLPTR": -1, "FA2_ERR_BAD_SHAPE": -2, "FA2_ERR_HEAD_DIM": -3,
+                     "FA2_ERR_BAD_SCALE": -4, "FA2_ERR_WORKSPACE": -5, "FA2_ERR_ALIAS": -6, "FA2_ERR_HIP": -7,
+                     "FA2_ERR_SPLITS": -8, "FA2_ERR_WINDOW": -9, "FA2_ERR_ALIGN": -10}
+    for name, val in codes.items():
+        assert fa2.status_string(val).startswith(name + ":"), name
 
 
 def test_library_exports_every_declared_symbol():
@@ -94,7 +108,10 @@ def test_alias():
 
 def test_splits_and_workspace():
     lib = fa2.load_library()
-    assert lib.fa2_splitkv_workspace_bytes(64, 32, 1, 128, 16) == 16 * 64 * 32 * 1 * 131 * 4
+    # S * B * H * N_q * (d + 2) * 4: per chunk and row, d accumulators, the reference m and the sum l
+    for B, H, nq, d, S in ((64, 32, 1, 128, 16), (2, 3, 5, 64, 7), (1, 1, 1, 64, 1), (3, 1, 1000, 128, 256)):
+        assert lib.fa2_splitkv_workspace_bytes(B, H, nq, d, S) == S * B * H * nq * (d + 2) * 4
+    assert split(ws_bytes=lib.fa2_splitkv_workspace_bytes(1, 2, 1, 64, 4) - 1) == WORKSPACE
     assert lib.fa2_splitkv_workspace_bytes(1, 1, 1, 64, 0) == 0
     assert lib.fa2_splitkv_workspace_bytes(1, 1, 1, 64, 257) == 0
     assert split(s=0) == SPLITS
@@ -286,3 +303,21 @@ def test_decode_fp8_validation():
     assert dec8(v=V + 4) == ALIGN
     assert dec8(o=K + 64) == ALIAS
     assert dec8(l=SV) == ALIAS
+
+
+def test_work_item_limits():
+    # a dispatch counts at most 2^32 - 1 work-items: 2^20 heads of one query row in 16 chunks
+    # need 2^24 decode workgroups of 256 work-items, one past it; nothing is enqueued
+    lib = fa2.load_library()
+    need = lib.fa2_splitkv_workspace_bytes(1 << 10, 1 << 10, 1, 128, 16)
+    assert split(B=1 << 10, H=1 << 10, nq=1, nk=16, d=128, s=16, ws_bytes=need) == BAD_SHAPE
+    # the tile kernel: ceil(N_q / 128) * B * H workgroups of 256 work-items
+    assert fwd(B=1 << 12, H=1 << 12, nq=128, nk=16, d=64) == BAD_SHAPE
+    assert window(B=1 << 12, H=1 << 12, nq=128, nk=16, d=64) == BAD_SHAPE
+    assert fwd8(B=1 << 12, H=1 << 12, nq=128, nk=16, d=64) == BAD_SHAPE
+    assert dec8(B=1 << 12, H=1 << 12, nk=16, d=64) == BAD_SHAPE
+    # the backward: its per-row pass takes 16 work-items per row at d = 128, its dQ reduction one
+    # per 4 elements (32 per row); R = 2^18 * 513 rows fit the first but not the second
+    assert bwd(B=1 << 9, H=1 << 9, nq=513, nk=16, d=128) == BAD_SHAPE
+    assert bwd(B=1 << 11, H=1 << 11, nq=256, nk=16, d=128) == BAD_SHAPE
+

@@ -38,6 +38,10 @@ def _check_line(d, dtype, with_cpu):
         for key in ("value", "unit", "cores", "kind", "sample"):
             assert key in c, key
         assert c["kind"] == "oracle" and c["cores"] >= 1 and c["value"] > 0
+        # the timed run's outputs at the oracle's rows, within the parity tolerances
+        p = d["parity"]
+        assert p["rows"] >= 1 and p["pass"] is True
+        assert p["max_abs_O"] <= 1e-2 and p["max_abs_LSE"] <= 1e-3
 
 
 @pytest.mark.gpu

@@ -68,7 +68,13 @@ def test_window(nq, wl, wr):
 def test_splitkv_partials():
     print("race check fa2_fwd_splitkv B2 H2 N_q300 N_k1000 d128 S3", flush=True)
     q, k, v = workloads.make_qkv_shape(2, 2, 300, 1000, 128, 73, DEV)
-    a, b = both(lambda: fa2.forward_splitkv(q, k, v, num_splits=3, causal=False))
+
+    def run():
+        ws = torch.empty(fa2.splitkv_workspace_bytes(2, 2, 300, 128, 3) // 4, dtype=torch.float32, device=DEV)
+        o, lse = fa2.forward_splitkv(q, k, v, num_splits=3, causal=False, workspace=ws)
+        return o, lse, ws
+
+    a, b = both(run)
     same(a, b, "split-KV")
 
 

@@ -70,7 +70,7 @@ def test_largest_head(d):
     # row 0 alone: the streaming decode kernel, directly and split in 16 chunks
     q0 = q[:, :, :1].contiguous()
     o1, l1 = fa2.forward(q0, k, v, causal=False, scale=scale)
-    o2, l2, _ = fa2.forward_splitkv(q0, k, v, num_splits=16, causal=False, scale=scale)
+    o2, l2 = fa2.forward_splitkv(q0, k, v, num_splits=16, causal=False, scale=scale)
     torch.cuda.synchronize()
     for oo, ll, what in ((o1, l1, "decode"), (o2, l2, "split 16")):
         gu.assert_close(oo[0, 0].float().cpu().double().numpy(), ll[0, 0].cpu().double().numpy(),
