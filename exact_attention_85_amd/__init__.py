@@ -15,6 +15,8 @@ from ._binding import (  # noqa: F401
     forward,
     forward_fp8,
     forward_splitkv,
+    forward_splitkv_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     forward_window,
     fp8_vt_stride,
     lib_path,

@@ -69,6 +69,8 @@ def open_library(path: str):
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     lib.fa2_fwd.restype = i
+    lib.fa2_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.fa2_fwd_splitkv_noalloc.restype = i
     lib.fa2_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa2_splitkv_workspace_bytes.restype = ctypes.c_size_t
     lib.fa2_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, ctypes.c_size_t, vp]
@@ -209,6 +211,25 @@ def forward_splitkv(q, k, v, num_splits: int = 16, causal: bool = False, scale=N
                              B, H, n_q, n_k, d, int(bool(causal)), _scale(scale, d), int(num_splits),
                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                              _stream_handle(q.device))
+    _check(rc)
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # FA2_NOALLOC_SCRATCH_BYTES
+
+
+def forward_splitkv_noalloc(q, k, v, num_splits: int = 16, causal: bool = False, scale=None, out=None, lse=None):
+    """forward_splitkv() with the partials in the library's own fixed device array
+    (fa2_fwd_splitkv_noalloc): no workspace, nothing allocated by the library.  Pass out and
+    lse to allocate nothing at all.  Calls that overlap on one GPU share that array and race.
+    Returns (o, lse); raises Fa2Error (FA2_ERR_SCRATCH) when the partials would exceed
+    NOALLOC_SCRATCH_BYTES."""
+    lib = load_library()
+    B, H, n_q, n_k, d = _check_inputs(q, k, v)
+    out, lse = _outputs(out, lse, B, H, n_q, d, q.device)
+    rc = lib.fa2_fwd_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                     B, H, n_q, n_k, d, int(bool(causal)), _scale(scale, d), int(num_splits),
+                                     _stream_handle(q.device))
     _check(rc)
     return out, lse
 

@@ -382,6 +382,8 @@ const char* fa2_status_string(int status) {
     case FA2_ERR_HIP: return "FA2_ERR_HIP: the HIP runtime rejected a kernel launch";
     case FA2_ERR_WINDOW: return "FA2_ERR_WINDOW: window sizes must be -1 (unbounded) or in [0, 2^30]";
     case FA2_ERR_ALIGN: return "FA2_ERR_ALIGN: FP8 entry points need 16-byte aligned tensor pointers";
+    case FA2_ERR_SCRATCH:
+      return "FA2_ERR_SCRATCH: the split-KV partials exceed the library's fixed scratch (FA2_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown fa2 status";
   }
 }

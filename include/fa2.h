@@ -53,7 +53,8 @@ typedef enum fa2_status {
   FA2_ERR_HIP = -7,       /* the HIP runtime rejected a kernel launch */
   FA2_ERR_SPLITS = -8,    /* num_splits outside [1, min(N_k, FA2_MAX_SPLITS)] */
   FA2_ERR_WINDOW = -9,    /* a window size below -1 or above 2^30 */
-  FA2_ERR_ALIGN = -10     /* an FP8 entry point's tensor pointer is not 16-byte aligned */
+  FA2_ERR_ALIGN = -10,    /* an FP8 entry point's tensor pointer is not 16-byte aligned */
+  FA2_ERR_SCRATCH = -11   /* fa2_fwd_splitkv_noalloc: the partials exceed FA2_NOALLOC_SCRATCH_BYTES */
 } fa2_status;
 
 /* Size limits (validated): N_k * d and N_q * d below 2^30 per head (one
@@ -192,6 +193,30 @@ int fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const vo
             const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N_q, int N_k,
             int d, int causal, float scale, void* workspace, size_t workspace_bytes,
             void* stream);
+
+/*
+ * fa2_fwd_splitkv_noalloc — fa2_fwd_splitkv without a caller workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  It allocates nothing
+ * and calls no allocating routine.
+ *
+ * The partials go to a fixed array of FA2_NOALLOC_SCRATCH_BYTES bytes of device
+ * memory that the library owns (one per GPU, held until the process ends), in
+ * the workspace layout of fa2_fwd_splitkv; the same two kernels run, so O and
+ * LSE equal fa2_fwd_splitkv's bit for bit.  Problems whose partials
+ * (fa2_splitkv_workspace_bytes()) exceed that size return FA2_ERR_SCRATCH
+ * with nothing enqueued.  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's partials: calls that overlap on one GPU (different
+ * streams, or host threads) race, and the caller must order them.  The
+ * array's device address is looked up on the first call for each device; the
+ * kernels run on `stream`'s device (the current device for NULL).
+ *
+ * Arguments and the remaining errors as fa2_fwd_splitkv, without the workspace.
+ */
+#define FA2_NOALLOC_SCRATCH_BYTES (32u << 20)
+int fa2_fwd_splitkv_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            int B, int H, int N_q, int N_k, int d, int causal, float scale,
+                            int num_splits, void* stream);
 
 /*
  * fa2_num_splits — a key-chunk count for fa2_fwd_splitkv that fills the chip

@@ -27,9 +27,9 @@ static void* dev(int i) { return reinterpret_cast<void*>((uintptr_t)(0x100000000
 static float* devf(int i) { return static_cast<float*>(dev(i)); }
 
 static void test_status_strings() {
-  for (int s = 0; s >= -10; --s) CHECK(strncmp(fa2_status_string(s), "FA2_", 4) == 0);
+  for (int s = 0; s >= -11; --s) CHECK(strncmp(fa2_status_string(s), "FA2_", 4) == 0);
   CHECK(strcmp(fa2_status_string(1), "unknown fa2 status") == 0);
-  CHECK(strcmp(fa2_status_string(-11), "unknown fa2 status") == 0);
+  CHECK(strcmp(fa2_status_string(-12), "unknown fa2 status") == 0);
 }
 
 static void test_fwd() {

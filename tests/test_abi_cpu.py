@@ -12,8 +12,8 @@ import exact_attention_85_amd as fa2
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa2.h")
 
-OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, HIP, SPLITS, WINDOW, ALIGN = (
-    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10)
+OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, HIP, SPLITS, WINDOW, ALIGN, SCRATCH = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11)
 
 
 def declared_functions():
@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_decode_fp8", "fa2_fp8_vt_stride", "fa2_fwd",
-                                    "fa2_fwd_fp8", "fa2_fwd_splitkv", "fa2_fwd_window",
+                                    "fa2_fwd_fp8", "fa2_fwd_splitkv", "fa2_fwd_splitkv_noalloc", "fa2_fwd_window",
                                     "fa2_num_splits", "fa2_quantize_fp8", "fa2_splitkv_workspace_bytes",
                                     "fa2_status_string"]
 
@@ -37,7 +37,7 @@ def test_status_codes_pinned():
     codes = {name: int(val) for name, val in re.findall(r"(FA2_[A-Z_]+)\s*=\s*(-?\d+)", body)}
     assert codes == {"FA2_OK": 0, "FA2_ERR_NULLPTR": -1, "FA2_ERR_BAD_SHAPE": -2, "FA2_ERR_HEAD_DIM": -3,
                      "FA2_ERR_BAD_SCALE": -4, "FA2_ERR_WORKSPACE": -5, "FA2_ERR_ALIAS": -6, "FA2_ERR_HIP": -7,
-                     "FA2_ERR_SPLITS": -8, "FA2_ERR_WINDOW": -9, "FA2_ERR_ALIGN": -10}
+                     "FA2_ERR_SPLITS": -8, "FA2_ERR_WINDOW": -9, "FA2_ERR_ALIGN": -10, "FA2_ERR_SCRATCH": -11}
     for name, val in codes.items():
         assert fa2.status_string(val).startswith(name + ":"), name
 
@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in (OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, SPLITS, HIP, WINDOW, ALIGN):
+    for code in (OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, SPLITS, HIP, WINDOW, ALIGN, SCRATCH):
         s = fa2.status_string(code)
         assert s and "unknown" not in s
     assert "unknown" in fa2.status_string(12345)
@@ -321,3 +321,23 @@ def test_work_item_limits():
     assert bwd(B=1 << 9, H=1 << 9, nq=513, nk=16, d=128) == BAD_SHAPE
     assert bwd(B=1 << 11, H=1 << 11, nq=256, nk=16, d=128) == BAD_SHAPE
 
+
+def noalloc(q=Q, k=K, v=V, o=O, l=L, B=1, H=2, nq=1, nk=256, d=64, causal=0, scale=0.125, s=4):
+    return fa2.load_library().fa2_fwd_splitkv_noalloc(q, k, v, o, l, B, H, nq, nk, d, causal, scale, s, None)
+
+
+def test_noalloc_validation():
+    # the checks of fa2_fwd_splitkv, then the fixed array's size, all before any HIP call
+    text = open(HEADER).read()
+    assert "#define FA2_NOALLOC_SCRATCH_BYTES (32u << 20)" in text
+    assert fa2.NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert noalloc(q=None) == NULLPTR
+    assert noalloc(d=96) == HEAD_DIM
+    assert noalloc(s=0) == SPLITS and noalloc(s=300, nk=256) == SPLITS
+    assert noalloc(o=Q) == ALIAS
+    assert noalloc(scale=float("nan")) == BAD_SCALE
+    # partials of S * B * H * N_q * (d + 2) * 4 bytes: one chunk-row more than fits is refused
+    S, d = 16, 128
+    rows_fit = (32 << 20) // (S * (d + 2) * 4)
+    assert noalloc(B=1, H=rows_fit + 1, nq=1, nk=64, d=d, s=S) == SCRATCH
+    assert noalloc(B=4, H=64, nq=1024, nk=8192, d=d, s=S) == SCRATCH
