@@ -11,8 +11,11 @@ from ._binding import (  # noqa: F401
     attention,
     backward,
     bwd_workspace_bytes,
+    config_name,
+    default_config,
     decode_fp8,
     forward,
+    forward_config,
     forward_fp8,
     forward_splitkv,
     forward_splitkv_noalloc,
@@ -24,7 +27,9 @@ from ._binding import (  # noqa: F401
     load_library,
     open_library,
     poison_lib_path,
+    num_configs,
     num_splits,
+    probe_xcc,
     quantize_fp8,
     splitkv_workspace_bytes,
     status_string,

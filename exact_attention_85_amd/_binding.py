@@ -91,6 +91,16 @@ def open_library(path: str):
     lib.fa2_fwd_fp8.restype = i
     lib.fa2_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, vp]
     lib.fa2_decode_fp8.restype = i
+    lib.fa2_fwd_config.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa2_fwd_config.restype = i
+    lib.fa2_fwd_num_configs.argtypes = []
+    lib.fa2_fwd_num_configs.restype = i
+    lib.fa2_fwd_config_name.argtypes = [i]
+    lib.fa2_fwd_config_name.restype = ctypes.c_char_p
+    lib.fa2_fwd_default_config.argtypes = [i, i, i, i, i]
+    lib.fa2_fwd_default_config.restype = i
+    lib.fa2_probe_xcc.argtypes = [vp, i, vp]
+    lib.fa2_probe_xcc.restype = i
     lib.fa2_status_string.argtypes = [i]
     lib.fa2_status_string.restype = ctypes.c_char_p
     return lib
@@ -183,6 +193,51 @@ def forward_window(q, k, v, window_left: int, window_right: int, scale=None, out
                             _stream_handle(q.device))
     _check(rc)
     return out, lse
+
+
+def num_configs() -> int:
+    """Number of forward configurations (kernel x workgroup order) fa2_fwd_config accepts."""
+    return int(load_library().fa2_fwd_num_configs())
+
+
+def config_name(config: int) -> str:
+    name = load_library().fa2_fwd_config_name(int(config))
+    if name is None:
+        raise ValueError(f"no forward configuration {config}")
+    return name.decode()
+
+
+def default_config(d: int, banded: bool, n_q: int, B: int = 1, H: int = 1) -> int:
+    """The configuration fa2_fwd / fa2_fwd_window take for the shape (the tuned table)."""
+    rc = int(load_library().fa2_fwd_default_config(int(d), int(bool(banded)), int(n_q), int(B), int(H)))
+    if rc < 0:
+        _check(rc)
+    return rc
+
+
+def forward_config(q, k, v, config: int, window_left: int = -1, window_right: int = -1, scale=None, out=None,
+                   lse=None):
+    """fa2_fwd_window with an explicit forward configuration (see config_name); causal is the
+    window (-1, 0).  Returns (o, lse)."""
+    lib = load_library()
+    B, H, n_q, n_k, d = _check_inputs(q, k, v)
+    out, lse = _outputs(out, lse, B, H, n_q, d, q.device)
+    rc = lib.fa2_fwd_config(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            B, H, n_q, n_k, d, int(window_left), int(window_right), _scale(scale, d), int(config),
+                            _stream_handle(q.device))
+    _check(rc)
+    return out, lse
+
+
+def probe_xcc(n_workgroups: int, device="cuda"):
+    """fa2_probe_xcc: (xcd [n], hw_id [n]) int32 tensors on the host, for workgroups 0 .. n-1
+    of one launch."""
+    lib = load_library()
+    dev = torch.device(device)
+    out = torch.full((n_workgroups, 2), -1, dtype=torch.int32, device=dev)
+    _check(lib.fa2_probe_xcc(out.data_ptr(), int(n_workgroups), _stream_handle(dev)))
+    out = out.cpu()
+    return out[:, 0], out[:, 1]
 
 
 def splitkv_workspace_bytes(B, H, n_q, d, num_splits) -> int:

@@ -9,7 +9,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa2.so")
 # race-check build: every LDS slot is filled with NaN before its asynchronous load
 POISON_LIB = os.path.join(PKG, "libfa2_poison.so")
-SOURCES = [os.path.join(CSRC, n) for n in ("fa2_fwd.hip", "fa2_bwd.hip", "fa2_fp8.hip", "fa2_noalloc.hip", "fa2_api.cpp")]
+SOURCES = [os.path.join(CSRC, n) for n in ("fa2_fwd.hip", "fa2_bwd.hip", "fa2_fp8.hip", "fa2_noalloc.hip", "fa2_probe.hip", "fa2_api.cpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "fa2_internal.h"
+#include "fa2_tune_table.h"
 
 namespace {
 
@@ -87,12 +88,34 @@ fa2::FwdParams make_params(const void* Q, const void* K, const void* V, void* O,
   p.scale = scale;
   p.num_splits = 1;
   p.split_len = N_k;
+  p.sched = fa2::kSchedRemap;
   return p;
 }
 
 }  // namespace
 
 namespace fa2 {
+
+const FwdConfig kFwdConfigs[kNumFwdConfigs] = {
+    {0, kSchedRemap, "tile128_remap_headmajor"},
+    {0, kSchedRemap | kSchedQbMajor, "tile128_remap_qbmajor"},
+    {0, 0, "tile128_noremap_headmajor"},
+    {0, kSchedQbMajor, "tile128_noremap_qbmajor"},
+    {1, kSchedRemap, "pingpong256_remap_headmajor"},
+    {1, kSchedRemap | kSchedQbMajor, "pingpong256_remap_qbmajor"},
+    {1, 0, "pingpong256_noremap_headmajor"},
+    {1, kSchedQbMajor, "pingpong256_noremap_qbmajor"},
+};
+
+int fwd_default_config(int d, bool banded, int n_q, long long /*n_bh*/) {
+  int best = 0, best_min = -1;
+  for (const TuneRow& r : kTuneTable)
+    if (r.d == d && r.banded == (banded ? 1 : 0) && r.nq_min <= n_q && r.nq_min > best_min) {
+      best = r.config;
+      best_min = r.nq_min;
+    }
+  return best;
+}
 
 int splitkv_check_args(const void* Q, const void* K, const void* V, const void* O, const float* LSE, int B, int H,
                        int N_q, int N_k, int d, float scale, int num_splits) {
@@ -134,7 +157,8 @@ int fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   rc = check_alias(Q, K, V, O, LSE, B, H, N_q, N_k, d, nullptr, 0);
   if (rc != FA2_OK) return rc;
   const fa2::FwdParams p = make_params(Q, K, V, O, LSE, B, H, N_q, N_k, d, causal, scale);
-  if (fa2::launch_fwd(p, static_cast<hipStream_t>(stream)) != hipSuccess) return FA2_ERR_HIP;
+  const int config = fa2::fwd_default_config(d, causal != 0, N_q, (long long)B * H);
+  if (fa2::launch_fwd(p, config, static_cast<hipStream_t>(stream)) != hipSuccess) return FA2_ERR_HIP;
   return FA2_OK;
 }
 
@@ -150,8 +174,40 @@ int fa2_fwd_window(const void* Q, const void* K, const void* V, void* O, float* 
   fa2::FwdParams p = make_params(Q, K, V, O, LSE, B, H, N_q, N_k, d, 0, scale);
   p.wl = window_left;
   p.wr = window_right;
-  if (fa2::launch_fwd(p, static_cast<hipStream_t>(stream)) != hipSuccess) return FA2_ERR_HIP;
+  const bool banded = window_left >= 0 || window_right >= 0;
+  const int config = fa2::fwd_default_config(d, banded, N_q, (long long)B * H);
+  if (fa2::launch_fwd(p, config, static_cast<hipStream_t>(stream)) != hipSuccess) return FA2_ERR_HIP;
   return FA2_OK;
+}
+
+int fa2_fwd_config(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q,
+                   int N_k, int d, int window_left, int window_right, float scale, int config, void* stream) {
+  int rc = check_common(Q, K, V, O, LSE, B, H, N_q, N_k, d, scale);
+  if (rc != FA2_OK) return rc;
+  if (window_left < -1 || window_right < -1 || window_left > kMaxWindow || window_right > kMaxWindow)
+    return FA2_ERR_WINDOW;
+  if (config < 0 || config >= fa2::kNumFwdConfigs) return FA2_ERR_CONFIG;
+  if (!fwd_fits(B, H, N_q)) return FA2_ERR_BAD_SHAPE;
+  rc = check_alias(Q, K, V, O, LSE, B, H, N_q, N_k, d, nullptr, 0);
+  if (rc != FA2_OK) return rc;
+  fa2::FwdParams p = make_params(Q, K, V, O, LSE, B, H, N_q, N_k, d, 0, scale);
+  p.wl = window_left;
+  p.wr = window_right;
+  if (fa2::launch_fwd(p, config, static_cast<hipStream_t>(stream)) != hipSuccess) return FA2_ERR_HIP;
+  return FA2_OK;
+}
+
+int fa2_fwd_num_configs(void) { return fa2::kNumFwdConfigs; }
+
+const char* fa2_fwd_config_name(int config) {
+  if (config < 0 || config >= fa2::kNumFwdConfigs) return nullptr;
+  return fa2::kFwdConfigs[config].name;
+}
+
+int fa2_fwd_default_config(int d, int banded, int N_q, int B, int H) {
+  if (B < 1 || H < 1 || N_q < 1) return FA2_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return FA2_ERR_HEAD_DIM;
+  return fa2::fwd_default_config(d, banded != 0, N_q, (long long)B * H);
 }
 
 size_t fa2_splitkv_workspace_bytes(int B, int H, int N_q, int d, int num_splits) {
@@ -369,6 +425,13 @@ int fa2_decode_fp8(const void* Qc, const void* Kc, const void* Vc, const float* 
   return FA2_OK;
 }
 
+int fa2_probe_xcc(int* out, int n_workgroups, void* stream) {
+  if (!out) return FA2_ERR_NULLPTR;
+  if (n_workgroups < 1 || !launch_fits(n_workgroups, 64)) return FA2_ERR_BAD_SHAPE;
+  if (fa2::launch_xcc_probe(out, n_workgroups, static_cast<hipStream_t>(stream)) != hipSuccess) return FA2_ERR_HIP;
+  return FA2_OK;
+}
+
 const char* fa2_status_string(int status) {
   switch (status) {
     case FA2_OK: return "FA2_OK: success";
@@ -382,6 +445,7 @@ const char* fa2_status_string(int status) {
     case FA2_ERR_HIP: return "FA2_ERR_HIP: the HIP runtime rejected a kernel launch";
     case FA2_ERR_WINDOW: return "FA2_ERR_WINDOW: window sizes must be -1 (unbounded) or in [0, 2^30]";
     case FA2_ERR_ALIGN: return "FA2_ERR_ALIGN: FP8 entry points need 16-byte aligned tensor pointers";
+    case FA2_ERR_CONFIG: return "FA2_ERR_CONFIG: config must be in [0, fa2_fwd_num_configs())";
     case FA2_ERR_SCRATCH:
       return "FA2_ERR_SCRATCH: the split-KV partials exceed the library's fixed scratch (FA2_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown fa2 status";

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa2_internal.h"
+
 namespace fa2 {
 namespace {
 
@@ -48,6 +50,25 @@ __device__ __forceinline__ int xcd_remap(int w, int G) {
   const int tall = G - (per - 1) * X;  // XCDs that receive `per` ids
   const int x = w % X, i = w / X;
   return x < tall ? x * per + i : tall * per + (x - tall) * (per - 1) + i;
+}
+
+// (batch*head, query block) of logical workgroup L among n_qb query blocks per head
+// and n_bh heads; heavy_first reverses the block order (the heaviest block of a
+// causal-like band is the last one).
+__device__ __forceinline__ void wg_coords(int L, int n_qb, int n_bh, int sched, bool heavy_first, int& bh,
+                                          int& qb) {
+  if (sched & kSchedQbMajor) {
+    qb = L / n_bh;
+    bh = L % n_bh;
+  } else {
+    bh = L / n_qb;
+    qb = L % n_qb;
+  }
+  if (heavy_first) qb = n_qb - 1 - qb;
+}
+
+__device__ __forceinline__ int wg_logical(int sched) {
+  return (sched & kSchedRemap) ? xcd_remap(blockIdx.x, gridDim.x) : (int)blockIdx.x;
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

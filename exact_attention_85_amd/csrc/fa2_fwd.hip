@@ -32,8 +32,6 @@ namespace fa2 {
 namespace {
 
 constexpr int kBC = 64;  // keys per K/V tile
-constexpr int kPingPongMinRows = 2048;        // unbanded attention: ping-pong kernel from here
-constexpr int kPingPongMinRowsBanded = 8192;  // causal or windowed
 
 // Per-wave state of one 32-row query block: the Q fragment (B operand of
 // S^T = K Q^T; lane holds Q[row][16t + 8hf .. +7]), the O^T accumulator
@@ -282,16 +280,16 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
 
   // ---- workgroup -> (batch*head, query block, key chunk) ----
   const int n_qb = (p.n_q + BR - 1) / BR;
-  int L = xcd_remap(blockIdx.x, gridDim.x);
+  int L = wg_logical(p.sched);
   int split = 0;
   if (SPLIT) {
     split = L % p.num_splits;
     L /= p.num_splits;
   }
-  const int bh = L / n_qb;
-  int qb = L % n_qb;
   const int wl = p.wl, wr = p.wr;  // key band [i - wl, i + wr] of query i; -1: unbounded
-  if (wl < 0 && wr >= 0) qb = n_qb - 1 - qb;  // causal-like band: heaviest query blocks first
+  int bh, qb;
+  // causal-like band: heaviest query blocks first
+  wg_coords(L, n_qb, p.B * p.H, p.sched, wl < 0 && wr >= 0, bh, qb);
   const int q0 = qb * BR;
   const int q0w = q0 + wave * 32;
   const int row = q0w + col;
@@ -728,11 +726,9 @@ __global__ void __launch_bounds__(512, 1) fwd_pp_kernel(FwdParams p, float sl2, 
   const int col = lane & 31;
 
   const int n_qb = (p.n_q + BR - 1) / BR;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = L / n_qb;
-  int qb = L % n_qb;
   const int wl = p.wl, wr = p.wr;
-  if (wl < 0 && wr >= 0) qb = n_qb - 1 - qb;
+  int bh, qb;
+  wg_coords(wg_logical(p.sched), n_qb, p.B * p.H, p.sched, wl < 0 && wr >= 0, bh, qb);
   const int q0 = qb * BR;
   const int q0w = q0 + wave * 32;
   const int row = q0w + col;
@@ -889,23 +885,26 @@ hipError_t launch_decode(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_pp(const FwdParams& p, hipStream_t stream) {
+  float sl2;
+  unsigned qsign;
+  fold_scale(p.scale, &sl2, &qsign);
+  const unsigned grid = (unsigned)((long long)((p.n_q + 255) / 256) * p.B * p.H);
+  hipLaunchKernelGGL(fwd_pp_kernel<D>, dim3(grid), dim3(512), 0, stream, p, sl2, qsign);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
+hipError_t launch_fwd(const FwdParams& p_in, int config, hipStream_t stream) {
   // one query row per head: the streaming decode kernel over the whole key range
-  if (p.n_q == 1) return launch_decode<true>(p, stream);
-  // long sequences at d = 128: the ping-pong kernel (256-row blocks); it loses on shorter
-  // banded or causal sequences, where a 256-row block wastes more work at the band edges
-  if (p.d == 128 && p.n_q >= (p.wl < 0 && p.wr < 0 ? kPingPongMinRows : kPingPongMinRowsBanded)) {
-    float sl2;
-    unsigned qsign;
-    fold_scale(p.scale, &sl2, &qsign);
-    const unsigned grid = (unsigned)((long long)((p.n_q + 255) / 256) * p.B * p.H);
-    hipLaunchKernelGGL(fwd_pp_kernel<128>, dim3(grid), dim3(512), 0, stream, p, sl2, qsign);
-    return hipGetLastError();
-  }
-  if (p.d == 128) return launch_tile<128, 4, false>(p, stream);
-  return launch_tile<64, 4, false>(p, stream);
+  if (p_in.n_q == 1) return launch_decode<true>(p_in, stream);
+  const FwdConfig& c = kFwdConfigs[config];
+  FwdParams p = p_in;
+  p.sched = c.sched;
+  if (c.kernel == 1) return p.d == 128 ? launch_pp<128>(p, stream) : launch_pp<64>(p, stream);
+  return p.d == 128 ? launch_tile<128, 4, false>(p, stream) : launch_tile<64, 4, false>(p, stream);
 }
 
 hipError_t launch_splitkv_partial(const FwdParams& p, hipStream_t stream) {

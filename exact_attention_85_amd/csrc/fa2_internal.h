@@ -7,6 +7,17 @@
 
 namespace fa2 {
 
+// Workgroup order of the forward kernels (FwdParams::sched bits).
+//   kSchedRemap   renumber workgroup ids with xcd_remap (each XCD a contiguous range);
+//                 without it, id i runs on XCD i % 8 as dispatched.
+//   kSchedQbMajor logical ids run over (query block, batch*head) with the query block
+//                 slowest: under a causal-like band the heaviest block of every head
+//                 is dispatched before any lighter one.  Without a remap and with
+//                 B*H a multiple of 8, XCD x then serves the heads h = x (mod 8).
+//                 Otherwise ids run head by head (all blocks of one head together).
+constexpr int kSchedRemap = 1;
+constexpr int kSchedQbMajor = 2;
+
 // Arguments of one forward (or split-KV partial) launch.  Pointers are device
 // pointers; sizes were validated by the host API.
 struct FwdParams {
@@ -24,7 +35,22 @@ struct FwdParams {
   float scale;
   int num_splits;    // 1 in forward mode
   int split_len;     // keys per chunk (N_k in forward mode)
+  int sched;         // workgroup order bits (fa2_device.h: kSchedRemap, kSchedQbMajor)
 };
+
+// Forward kernel configurations (fa2_fwd_config): the kernel and the workgroup order.
+//   kernel 0: 4 waves, 128 query rows per workgroup, two workgroups per compute unit
+//   kernel 1: 8 waves, 256 query rows, ping-pong of matrix and vector phases
+struct FwdConfig {
+  int kernel;
+  int sched;
+  const char* name;
+};
+constexpr int kNumFwdConfigs = 8;
+extern const FwdConfig kFwdConfigs[kNumFwdConfigs];
+
+// The configuration fa2_fwd takes for a shape (the measured table in fa2_tune_table.h).
+int fwd_default_config(int d, bool banded, int n_q, long long n_bh);
 
 // Backward: 128-key blocks that one workgroup takes one after the other,
 // sharing one dQ partial slot.  The largest of 8, 4 and 2 that still leaves at
@@ -103,8 +129,9 @@ int splitkv_check_args(const void* Q, const void* K, const void* V, const void* 
 int splitkv_run(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q, int N_k,
                 int d, int causal, float scale, int num_splits, float* ws, void* stream);
 
-// Forward: O, LSE.  Returns hipSuccess or the launch error.
-hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
+// Forward: O, LSE, with configuration `config` (0 .. kNumFwdConfigs - 1; N_q == 1 always
+// takes the decode kernel).  Returns hipSuccess or the launch error.
+hipError_t launch_fwd(const FwdParams& p, int config, hipStream_t stream);
 
 // Split-KV pass 1 (partials into the workspace) and pass 2 (merge into O, LSE).
 hipError_t launch_splitkv_partial(const FwdParams& p, hipStream_t stream);
@@ -112,6 +139,9 @@ hipError_t launch_splitkv_merge(const FwdParams& p, hipStream_t stream);
 
 // Backward: D and LSE*log2e, then dK, dV and the dQ partials, then the dQ reduction.
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+
+// Dispatch-order probe: out[2i] = XCD id, out[2i + 1] = hardware id word of workgroup i.
+hipError_t launch_xcc_probe(int* out, int n, hipStream_t stream);
 
 // FP8 forward and the quantiser that prepares its inputs.
 hipError_t launch_fwd_fp8(const Fp8Params& p, hipStream_t stream);

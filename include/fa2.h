@@ -54,7 +54,8 @@ typedef enum fa2_status {
   FA2_ERR_SPLITS = -8,    /* num_splits outside [1, min(N_k, FA2_MAX_SPLITS)] */
   FA2_ERR_WINDOW = -9,    /* a window size below -1 or above 2^30 */
   FA2_ERR_ALIGN = -10,    /* an FP8 entry point's tensor pointer is not 16-byte aligned */
-  FA2_ERR_SCRATCH = -11   /* fa2_fwd_splitkv_noalloc: the partials exceed FA2_NOALLOC_SCRATCH_BYTES */
+  FA2_ERR_SCRATCH = -11,  /* fa2_fwd_splitkv_noalloc: the partials exceed FA2_NOALLOC_SCRATCH_BYTES */
+  FA2_ERR_CONFIG = -12    /* fa2_fwd_config: config outside [0, fa2_fwd_num_configs()) */
 } fa2_status;
 
 /* Size limits (validated): N_k * d and N_q * d below 2^30 per head (one
@@ -107,6 +108,46 @@ int fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
 int fa2_fwd_window(const void* Q, const void* K, const void* V, void* O, float* LSE,
                    int B, int H, int N_q, int N_k, int d, int window_left, int window_right,
                    float scale, void* stream);
+
+/*
+ * Forward configurations (the synthesis page, section 3 item 3: FA2 picks its
+ * block sizes by hand from a few candidates; section 5 item 1: search block
+ * sizes, warp counts and stages per shape instead).  A configuration is a
+ * kernel plus a workgroup order; every configuration computes the same result
+ * (the kernels share their arithmetic, so outputs agree bit for bit between
+ * configurations of one kernel, and to rounding between kernels):
+ *   kernel   "tile128":     4 waves, 128 query rows per workgroup, two
+ *                           workgroups per compute unit;
+ *            "pingpong256": 8 waves, 256 query rows, waves sharing a SIMD
+ *                           alternate matrix and vector phases;
+ *   order    "remap":       workgroup ids renumbered so that each of the 8
+ *                           XCDs (chiplets) runs a contiguous range of blocks
+ *                           (the synthesis page, section 2, Chiplet FA
+ *                           paragraph: K/V reuse in one chiplet's L2);
+ *            "noremap":     ids as dispatched (id i on XCD i mod 8);
+ *            "headmajor":   all query blocks of one (batch, head) together;
+ *            "qbmajor":     query block slowest, (batch, head) fastest, so that
+ *                           under a causal or banded mask the heaviest block of
+ *                           every head is dispatched before any lighter one.
+ * fa2_fwd and fa2_fwd_window take the configuration a measured table picks
+ * for (d, banded, N_q) (fa2_fwd_default_config); fa2_fwd_config runs a chosen
+ * one (for measuring, and for parity tests of every configuration).
+ *
+ * fa2_fwd_num_configs: the number of configurations.
+ * fa2_fwd_config_name: a static name for config, or NULL when out of range.
+ * fa2_fwd_default_config: the configuration fa2_fwd (banded = causal) or
+ *   fa2_fwd_window (banded = a window side >= 0) takes for the shape, or
+ *   FA2_ERR_BAD_SHAPE / FA2_ERR_HEAD_DIM.  No HIP call.
+ * fa2_fwd_config: fa2_fwd_window with the given configuration; arguments and
+ *   errors as fa2_fwd_window, plus FA2_ERR_CONFIG.  N_q == 1 always runs the
+ *   single-row decode kernel, whatever the configuration.
+ */
+int fa2_fwd_num_configs(void);
+const char* fa2_fwd_config_name(int config);
+int fa2_fwd_default_config(int d, int banded, int N_q, int B, int H);
+int fa2_fwd_config(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                   int B, int H, int N_q, int N_k, int d, int window_left, int window_right,
+                   float scale, int config, void* stream);
 
 /*
  * fa2_splitkv_workspace_bytes — bytes of caller-owned device workspace that
@@ -319,6 +360,18 @@ int fa2_fwd_fp8(const void* Qc, const void* Kc, const void* Vt, const float* des
 int fa2_decode_fp8(const void* Qc, const void* Kc, const void* Vc, const float* descale_q,
                    const float* descale_k, const float* descale_v, void* O, float* LSE, int B, int H,
                    int N_k, int d, float scale, void* stream);
+
+/*
+ * fa2_probe_xcc — where the workgroups of a launch run (a diagnostic behind
+ * the forward's XCD-aware workgroup order; the synthesis page, section 2,
+ * Chiplet FA paragraph).  Launches n_workgroups workgroups of one wave; for
+ * workgroup i it writes out[2i] = the XCD (chiplet) id and out[2i + 1] = the
+ * wave's hardware id word (HW_ID register: wave slot, SIMD, compute unit,
+ * shader array and engine fields).  out: device int[2 * n_workgroups].
+ * Returns FA2_OK, FA2_ERR_NULLPTR, FA2_ERR_BAD_SHAPE (n_workgroups < 1 or
+ * beyond a launch's limits) or FA2_ERR_HIP.
+ */
+int fa2_probe_xcc(int* out, int n_workgroups, void* stream);
 
 /* fa2_status_string — static, human-readable text for a status code. */
 const char* fa2_status_string(int status);

@@ -27,9 +27,9 @@ static void* dev(int i) { return reinterpret_cast<void*>((uintptr_t)(0x100000000
 static float* devf(int i) { return static_cast<float*>(dev(i)); }
 
 static void test_status_strings() {
-  for (int s = 0; s >= -11; --s) CHECK(strncmp(fa2_status_string(s), "FA2_", 4) == 0);
+  for (int s = 0; s >= -12; --s) CHECK(strncmp(fa2_status_string(s), "FA2_", 4) == 0);
   CHECK(strcmp(fa2_status_string(1), "unknown fa2 status") == 0);
-  CHECK(strcmp(fa2_status_string(-12), "unknown fa2 status") == 0);
+  CHECK(strcmp(fa2_status_string(-13), "unknown fa2 status") == 0);
 }
 
 static void test_fwd() {
@@ -87,6 +87,37 @@ static void test_window() {
   CHECK(stub::rec.fwd.wl == (1 << 30) && stub::rec.fwd.wr == (1 << 30));
   CHECK(fa2_fwd_window(Q, K, V, O, L, 2, 3, 300, 500, 128, 17, 0, 0.1f, nullptr) == FA2_OK);
   CHECK(stub::rec.fwd.wl == 17 && stub::rec.fwd.wr == 0 && stub::rec.fwd.n_k == 500);
+}
+
+static void test_configs() {
+  void *Q = dev(0), *K = dev(1), *V = dev(2), *O = dev(3);
+  float* L = devf(4);
+  const int n = fa2_fwd_num_configs();
+  CHECK(n == 8);
+  for (int c = 0; c < n; ++c) {
+    CHECK(fa2_fwd_config_name(c) != nullptr);
+    CHECK(fa2_fwd_config(Q, K, V, O, L, 2, 3, 300, 400, 128, -1, 0, 0.1f, c, nullptr) == FA2_OK);
+    CHECK(stub::rec.config == c && stub::rec.fwd.wl == -1 && stub::rec.fwd.wr == 0);
+  }
+  CHECK(fa2_fwd_config_name(-1) == nullptr && fa2_fwd_config_name(n) == nullptr);
+  CHECK(fa2_fwd_config(Q, K, V, O, L, 2, 3, 300, 400, 128, -1, 0, 0.1f, n, nullptr) == FA2_ERR_CONFIG);
+  CHECK(fa2_fwd_config(Q, K, V, O, L, 2, 3, 300, 400, 128, -1, 0, 0.1f, -1, nullptr) == FA2_ERR_CONFIG);
+  CHECK(fa2_fwd_config(Q, K, V, O, L, 2, 3, 300, 400, 128, -3, 0, 0.1f, 0, nullptr) == FA2_ERR_WINDOW);
+  // fa2_fwd and fa2_fwd_window take the table's configuration for the shape
+  CHECK(fa2_fwd(Q, K, V, O, L, 1, 32, 16384, 16384, 128, 0, 0.1f, nullptr) == FA2_OK);
+  CHECK(stub::rec.config == fa2_fwd_default_config(128, 0, 16384, 1, 32));
+  CHECK(fa2_fwd(Q, K, V, O, L, 8, 16, 2048, 2048, 64, 1, 0.1f, nullptr) == FA2_OK);
+  CHECK(stub::rec.config == fa2_fwd_default_config(64, 1, 2048, 8, 16));
+  CHECK(fa2_fwd_window(Q, K, V, O, L, 1, 2, 9000, 9000, 128, 100, 0, 0.1f, nullptr) == FA2_OK);
+  CHECK(stub::rec.config == fa2_fwd_default_config(128, 1, 9000, 1, 2));
+  CHECK(fa2_fwd_default_config(96, 0, 100, 1, 1) == FA2_ERR_HEAD_DIM);
+  CHECK(fa2_fwd_default_config(64, 0, 0, 1, 1) == FA2_ERR_BAD_SHAPE);
+  for (int nq = 1; nq < (1 << 24); nq *= 3)
+    for (int d = 64; d <= 128; d += 64)
+      for (int b = 0; b < 2; ++b) {
+        const int c = fa2_fwd_default_config(d, b, nq, 1, 1);
+        CHECK(c >= 0 && c < n);
+      }
 }
 
 static void test_splitkv() {
@@ -193,6 +224,7 @@ int main() {
   test_status_strings();
   test_fwd();
   test_window();
+  test_configs();
   test_splitkv();
   test_num_splits();
   test_bwd();

@@ -10,9 +10,10 @@ Record rec;
 
 namespace fa2 {
 
-hipError_t launch_fwd(const FwdParams& p, hipStream_t) {
+hipError_t launch_fwd(const FwdParams& p, int config, hipStream_t) {
   stub::rec.kind = "fwd";
   stub::rec.fwd = p;
+  stub::rec.config = config;
   ++stub::rec.calls;
   return stub::rec.result;
 }
@@ -55,6 +56,12 @@ hipError_t launch_quantize_fp8(const QuantParams& p, hipStream_t) {
 hipError_t launch_decode_fp8(const Fp8Params& p, hipStream_t) {
   stub::rec.kind = "decode_fp8";
   stub::rec.fp8 = p;
+  ++stub::rec.calls;
+  return stub::rec.result;
+}
+
+hipError_t launch_xcc_probe(int*, int, hipStream_t) {
+  stub::rec.kind = "xcc_probe";
   ++stub::rec.calls;
   return stub::rec.result;
 }

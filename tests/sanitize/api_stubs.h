@@ -10,6 +10,7 @@ struct Record {
   int calls = 0;            // launcher calls so far
   const char* kind = "";    // which launcher ran last
   fa2::FwdParams fwd{};     // launch_fwd, launch_splitkv_partial / _merge
+  int config = -1;          // launch_fwd's configuration
   fa2::BwdParams bwd{};     // launch_bwd
   fa2::Fp8Params fp8{};     // launch_fwd_fp8, launch_decode_fp8
   fa2::QuantParams quant{}; // launch_quantize_fp8

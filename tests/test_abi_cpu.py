@@ -12,8 +12,8 @@ import exact_attention_85_amd as fa2
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa2.h")
 
-OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, HIP, SPLITS, WINDOW, ALIGN, SCRATCH = (
-    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11)
+OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, HIP, SPLITS, WINDOW, ALIGN, SCRATCH, CONFIG = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11, -12)
 
 
 def declared_functions():
@@ -24,8 +24,10 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_decode_fp8", "fa2_fp8_vt_stride", "fa2_fwd",
-                                    "fa2_fwd_fp8", "fa2_fwd_splitkv", "fa2_fwd_splitkv_noalloc", "fa2_fwd_window",
-                                    "fa2_num_splits", "fa2_quantize_fp8", "fa2_splitkv_workspace_bytes",
+                                    "fa2_fwd_config", "fa2_fwd_config_name", "fa2_fwd_default_config",
+                                    "fa2_fwd_fp8", "fa2_fwd_num_configs", "fa2_fwd_splitkv",
+                                    "fa2_fwd_splitkv_noalloc", "fa2_fwd_window", "fa2_num_splits",
+                                    "fa2_probe_xcc", "fa2_quantize_fp8", "fa2_splitkv_workspace_bytes",
                                     "fa2_status_string"]
 
 
@@ -37,7 +39,8 @@ def test_status_codes_pinned():
     codes = {name: int(val) for name, val in re.findall(r"(FA2_[A-Z_]+)\s*=\s*(-?\d+)", body)}
     assert codes == {"FA2_OK": 0, "FA2_ERR_NULLPTR": -1, "FA2_ERR_BAD_SHAPE": -2, "FA2_ERR_HEAD_DIM": -3,
                      "FA2_ERR_BAD_SCALE": -4, "FA2_ERR_WORKSPACE": -5, "FA2_ERR_ALIAS": -6, "FA2_ERR_HIP": -7,
-                     "FA2_ERR_SPLITS": -8, "FA2_ERR_WINDOW": -9, "FA2_ERR_ALIGN": -10, "FA2_ERR_SCRATCH": -11}
+                     "FA2_ERR_SPLITS": -8, "FA2_ERR_WINDOW": -9, "FA2_ERR_ALIGN": -10, "FA2_ERR_SCRATCH": -11,
+                     "FA2_ERR_CONFIG": -12}
     for name, val in codes.items():
         assert fa2.status_string(val).startswith(name + ":"), name
 
@@ -49,7 +52,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in (OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, SPLITS, HIP, WINDOW, ALIGN, SCRATCH):
+    for code in (OK, NULLPTR, BAD_SHAPE, HEAD_DIM, BAD_SCALE, WORKSPACE, ALIAS, SPLITS, HIP, WINDOW, ALIGN, SCRATCH, CONFIG):
         s = fa2.status_string(code)
         assert s and "unknown" not in s
     assert "unknown" in fa2.status_string(12345)
@@ -341,3 +344,21 @@ def test_noalloc_validation():
     rows_fit = (32 << 20) // (S * (d + 2) * 4)
     assert noalloc(B=1, H=rows_fit + 1, nq=1, nk=64, d=d, s=S) == SCRATCH
     assert noalloc(B=4, H=64, nq=1024, nk=8192, d=d, s=S) == SCRATCH
+
+
+def cfg(q=Q, k=K, v=V, o=O, l=L, B=1, H=2, nq=256, nk=256, d=64, wl=-1, wr=0, scale=0.125, c=0):
+    return fa2.load_library().fa2_fwd_config(q, k, v, o, l, B, H, nq, nk, d, wl, wr, scale, c, None)
+
+
+def test_config_validation():
+    n = fa2.num_configs()
+    assert n == 8 and len({fa2.config_name(c) for c in range(n)}) == n
+    assert cfg(c=-1) == CONFIG and cfg(c=n) == CONFIG
+    assert cfg(q=None) == NULLPTR and cfg(d=96) == HEAD_DIM and cfg(wl=-5) == WINDOW and cfg(o=Q) == ALIAS
+    assert fa2.load_library().fa2_fwd_config_name(n) is None
+    with pytest.raises(ValueError):
+        fa2.config_name(n)
+    with pytest.raises(fa2.Fa2Error):
+        fa2.default_config(96, False, 100)
+    assert fa2.load_library().fa2_probe_xcc(None, 10, None) == NULLPTR
+    assert fa2.load_library().fa2_probe_xcc(Q, 0, None) == BAD_SHAPE
