@@ -105,6 +105,8 @@ const FwdConfig kFwdConfigs[kNumFwdConfigs] = {
     {1, kSchedRemap | kSchedQbMajor, "pingpong256_remap_qbmajor"},
     {1, 0, "pingpong256_noremap_headmajor"},
     {1, kSchedQbMajor, "pingpong256_noremap_qbmajor"},
+    {2, kSchedRemap, "tile256_remap_headmajor"},
+    {2, kSchedQbMajor, "tile256_noremap_qbmajor"},
 };
 
 int fwd_default_config(int d, bool banded, int n_q, long long /*n_bh*/) {

@@ -904,6 +904,7 @@ hipError_t launch_fwd(const FwdParams& p_in, int config, hipStream_t stream) {
   FwdParams p = p_in;
   p.sched = c.sched;
   if (c.kernel == 1) return p.d == 128 ? launch_pp<128>(p, stream) : launch_pp<64>(p, stream);
+  if (c.kernel == 2) return p.d == 128 ? launch_tile<128, 8, false>(p, stream) : launch_tile<64, 8, false>(p, stream);
   return p.d == 128 ? launch_tile<128, 4, false>(p, stream) : launch_tile<64, 4, false>(p, stream);
 }
 

@@ -41,12 +41,13 @@ struct FwdParams {
 // Forward kernel configurations (fa2_fwd_config): the kernel and the workgroup order.
 //   kernel 0: 4 waves, 128 query rows per workgroup, two workgroups per compute unit
 //   kernel 1: 8 waves, 256 query rows, ping-pong of matrix and vector phases
+//   kernel 2: 8 waves, 256 query rows, the tile loop of kernel 0 (every wave in step)
 struct FwdConfig {
   int kernel;
   int sched;
   const char* name;
 };
-constexpr int kNumFwdConfigs = 8;
+constexpr int kNumFwdConfigs = 10;
 extern const FwdConfig kFwdConfigs[kNumFwdConfigs];
 
 // The configuration fa2_fwd takes for a shape (the measured table in fa2_tune_table.h).

@@ -120,6 +120,8 @@ int fa2_fwd_window(const void* Q, const void* K, const void* V, void* O, float* 
  *                           workgroups per compute unit;
  *            "pingpong256": 8 waves, 256 query rows, waves sharing a SIMD
  *                           alternate matrix and vector phases;
+ *            "tile256":     8 waves, 256 query rows, the tile128 loop with every
+ *                           wave in step (K/V tiles shared by twice the rows);
  *   order    "remap":       workgroup ids renumbered so that each of the 8
  *                           XCDs (chiplets) runs a contiguous range of blocks
  *                           (the synthesis page, section 2, Chiplet FA

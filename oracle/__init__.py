@@ -30,6 +30,7 @@ _lib = None
 _dp = ctypes.POINTER(ctypes.c_double)
 _u16p = ctypes.POINTER(ctypes.c_uint16)
 _i64p = ctypes.POINTER(ctypes.c_int64)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
 _i = ctypes.c_int
 
 
@@ -62,10 +63,16 @@ def _load():
                                         _i, _i, _i, _i]
     lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
     lib.oracle_e4m3_encode.restype = ctypes.c_uint8
-    _u8p = ctypes.POINTER(ctypes.c_uint8)
     _fp = ctypes.POINTER(ctypes.c_float)
     lib.oracle_attention_fp8_rows.argtypes = [_u8p, _u8p, _u8p, _fp, _fp, _fp, _i64p, ctypes.c_int64, _dp, _dp,
                                               _i, _i, _i, _i, _i, _i, ctypes.c_double]
+    lib.oracle_attention_blockmask_f64.argtypes = [_dp, _dp, _dp, _dp, _dp, _i, _i, _i, _i, _i, _u8p, _i, _i, _i,
+                                                   _i, _i, _i, ctypes.c_double]
+    lib.oracle_attention_blockmask_rows_bf16.argtypes = [_u16p, _u16p, _u16p, _i64p, ctypes.c_int64, _dp, _dp, _i,
+                                                         _i, _i, _i, _i, _u8p, _i, _i, _i, _i, _i, _i,
+                                                         ctypes.c_double]
+    lib.oracle_blockmask_pairs.argtypes = [_i, _i, _u8p, _i, _i, _i, _i, _i, _i, _i, _i]
+    lib.oracle_blockmask_pairs.restype = ctypes.c_int64
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -285,3 +292,71 @@ def attention_fp8_rows(qc, kc, vc, dq, dk, dv, rows, causal: bool, scale: float)
                                            B, H, n_q, n_k, d, int(causal), float(scale))
     _check(rc, "attention_fp8_rows")
     return O, L
+
+
+def _mask4(mask, B, H):
+    """A block mask as a contiguous uint8 [Mb, Mh, n_qb, n_kb] array with Mb in {1, B}, Mh in {1, H}."""
+    m = np.ascontiguousarray(mask, dtype=np.uint8)
+    if m.ndim == 2:
+        m = m[None, None]
+    elif m.ndim == 3:
+        m = m[None]
+    assert m.ndim == 4 and m.shape[0] in (1, B) and m.shape[1] in (1, H), m.shape
+    return np.ascontiguousarray(m)
+
+
+def attention_blockmask(q, k, v, mask, block_q: int, block_k: int, scale: float, window_left: int = -1,
+                        window_right: int = -1):
+    """Block-sparse attention in fp64 (the synthesis page, section 5 item 4).
+
+    mask: uint8 [n_qb, n_kb], [Mh, n_qb, n_kb] or [Mb, Mh, n_qb, n_kb] (Mb in {1, B}, Mh in {1, H};
+    n_qb = ceil(N_q / block_q), n_kb = ceil(N_k / block_k)).  Key j is visible to query i of
+    (b, h) iff mask[b][h][i // block_q][j // block_k] != 0 and the band (window_left,
+    window_right) admits it (as attention_window).  Rows that see no key get O = 0, LSE = -inf."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, n_q, d = q.shape
+    n_k = k.shape[2]
+    m = _mask4(mask, B, H)
+    assert m.shape[2:] == (-(-n_q // block_q), -(-n_k // block_k)), m.shape
+    o = np.empty((B, H, n_q, d), dtype=np.float64)
+    lse = np.empty((B, H, n_q), dtype=np.float64)
+    rc = _load().oracle_attention_blockmask_f64(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(o, _dp),
+                                                _ptr(lse, _dp), B, H, n_q, n_k, d, _ptr(m, _u8p), m.shape[0],
+                                                m.shape[1], int(block_q), int(block_k), int(window_left),
+                                                int(window_right), float(scale))
+    _check(rc, "attention_blockmask")
+    return o, lse
+
+
+def attention_blockmask_rows_bf16(q_bits, k_bits, v_bits, rows, mask, block_q: int, block_k: int, scale: float,
+                                  window_left: int = -1, window_right: int = -1):
+    """attention_blockmask for selected flat rows ((b*H + h)*N_q + i) of bf16 inputs given as uint16 bits."""
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    k_bits = np.ascontiguousarray(k_bits, dtype=np.uint16)
+    v_bits = np.ascontiguousarray(v_bits, dtype=np.uint16)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    B, H, n_q, d = q_bits.shape
+    n_k = k_bits.shape[2]
+    m = _mask4(mask, B, H)
+    assert m.shape[2:] == (-(-n_q // block_q), -(-n_k // block_k)), m.shape
+    o = np.empty((rows.size, d), dtype=np.float64)
+    lse = np.empty((rows.size,), dtype=np.float64)
+    rc = _load().oracle_attention_blockmask_rows_bf16(_ptr(q_bits, _u16p), _ptr(k_bits, _u16p), _ptr(v_bits, _u16p),
+                                                      _ptr(rows, _i64p), rows.size, _ptr(o, _dp), _ptr(lse, _dp),
+                                                      B, H, n_q, n_k, d, _ptr(m, _u8p), m.shape[0], m.shape[1],
+                                                      int(block_q), int(block_k), int(window_left),
+                                                      int(window_right), float(scale))
+    _check(rc, "attention_blockmask_rows_bf16")
+    return o, lse
+
+
+def blockmask_pairs(n_q: int, n_k: int, mask, b: int, h: int, block_q: int, block_k: int, window_left: int = -1,
+                    window_right: int = -1) -> int:
+    """Visible (query, key) pairs of one (b, h) under the block mask and band."""
+    m = np.ascontiguousarray(mask, dtype=np.uint8)
+    while m.ndim < 4:
+        m = m[None]
+    m = np.ascontiguousarray(m)
+    return int(_load().oracle_blockmask_pairs(int(n_q), int(n_k), _ptr(m, _u8p), m.shape[0], m.shape[1], int(b),
+                                              int(h), int(block_q), int(block_k), int(window_left),
+                                              int(window_right)))

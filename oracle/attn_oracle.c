@@ -573,3 +573,136 @@ int oracle_num_threads(void) { return omp_get_max_threads(); }
 #else
 int oracle_num_threads(void) { return 1; }
 #endif
+
+/*
+ * Block-sparse attention (the synthesis page, section 5 item 4: the causal
+ * block skip extended to sliding windows and dilated patterns, as one
+ * sparse-block-skip mechanism).  A byte mask M selects (query block, key
+ * block) pairs: query rows are grouped in blocks of bq, keys in blocks of bk,
+ * and M has shape [Mb][Mh][ceil(N_q/bq)][ceil(N_k/bk)] with Mb in {1, B} and
+ * Mh in {1, H} (a size-1 dimension is shared by every batch or head).  Key j
+ * is visible to query i of (b, h) iff
+ *   j < N_k,
+ *   M[b mod Mb][h mod Mh][i / bq][j / bk] != 0, and
+ *   the band (wl, wr) admits it: (wl < 0 or j >= i - wl) and (wr < 0 or j <= i + wr).
+ * The softmax runs over the visible keys only (two passes: maximum, then the
+ * exponentials); a row that sees no key gets O = 0 and LSE = -inf.
+ */
+static int blockmask_visible(const uint8_t* mrow, int64_t i, int64_t j, int bk, int wl, int wr) {
+  if (wl >= 0 && j < i - wl) return 0;
+  if (wr >= 0 && j > i + wr) return 0;
+  return mrow[j / bk] != 0;
+}
+
+static void attend_masked_row(const double* q, const double* K, const double* V, int64_t n_k, int d,
+                              double scale, const uint8_t* mrow, int bk, int64_t i, int wl, int wr, double* s,
+                              double* o, double* lse) {
+  for (int c = 0; c < d; ++c) o[c] = 0.0;
+  double m = -INFINITY;
+  for (int64_t j = 0; j < n_k; ++j) {
+    if (!blockmask_visible(mrow, i, j, bk, wl, wr)) continue;
+    const double* kj = K + j * d;
+    double dot = 0.0;
+    for (int c = 0; c < d; ++c) dot += q[c] * kj[c];
+    s[j] = scale * dot;
+    if (s[j] > m) m = s[j];
+  }
+  if (m == -INFINITY) {
+    *lse = -INFINITY; /* no visible key: O stays zero */
+    return;
+  }
+  double l = 0.0;
+  for (int64_t j = 0; j < n_k; ++j) {
+    if (!blockmask_visible(mrow, i, j, bk, wl, wr)) continue;
+    const double p = exp(s[j] - m);
+    l += p;
+    const double* vj = V + j * d;
+    for (int c = 0; c < d; ++c) o[c] += p * vj[c];
+  }
+  for (int c = 0; c < d; ++c) o[c] /= l;
+  *lse = m + log(l);
+}
+
+static int check_blockmask(int B, int H, int Mb, int Mh, int bq, int bk) {
+  if (bq < 1 || bk < 1) return -1;
+  if (!(Mb == 1 || Mb == B) || !(Mh == 1 || Mh == H)) return -1;
+  return 0;
+}
+
+/* The mask row of query i of (b, h): M[b mod Mb][h mod Mh][i / bq][.] */
+static const uint8_t* blockmask_row(const uint8_t* M, int64_t b, int64_t h, int64_t i, int Mb, int Mh, int bq,
+                                    int64_t n_qb, int64_t n_kb) {
+  return M + (((b % Mb) * Mh + (h % Mh)) * n_qb + i / bq) * n_kb;
+}
+
+int oracle_attention_blockmask_f64(const double* Q, const double* K, const double* V, double* O, double* LSE,
+                                   int B, int H, int n_q, int n_k, int d, const uint8_t* M, int Mb, int Mh, int bq,
+                                   int bk, int wl, int wr, double scale) {
+  if (check_shape(B, H, n_q, n_k, d) || check_blockmask(B, H, Mb, Mh, bq, bk)) return -1;
+  const int64_t n_rows = (int64_t)B * H * n_q;
+  const int64_t n_qb = (n_q + bq - 1) / bq, n_kb = (n_k + bk - 1) / bk;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)n_k);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t row = 0; row < n_rows; ++row) {
+      const int64_t bh = row / n_q, i = row % n_q;
+      const uint8_t* mrow = blockmask_row(M, bh / H, bh % H, i, Mb, Mh, bq, n_qb, n_kb);
+      attend_masked_row(Q + row * d, K + bh * (int64_t)n_k * d, V + bh * (int64_t)n_k * d, n_k, d, scale, mrow,
+                        bk, i, wl, wr, s, O + row * d, LSE + row);
+    }
+    free(s);
+  }
+  return 0;
+}
+
+/* The block-sparse result for chosen rows of bf16 inputs (as oracle_attention_rows_bf16). */
+int oracle_attention_blockmask_rows_bf16(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                                         const int64_t* rows, int64_t n_rows, double* O_rows, double* LSE_rows,
+                                         int B, int H, int n_q, int n_k, int d, const uint8_t* M, int Mb, int Mh,
+                                         int bq, int bk, int wl, int wr, double scale) {
+  if (check_shape(B, H, n_q, n_k, d) || check_blockmask(B, H, Mb, Mh, bq, bk)) return -1;
+  for (int64_t r = 0; r < n_rows; ++r)
+    if (rows[r] < 0 || rows[r] >= (int64_t)B * H * n_q) return -1;
+  const int64_t n_qb = (n_q + bq - 1) / bq, n_kb = (n_k + bk - 1) / bk;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)n_k);
+    double* q = (double*)malloc(sizeof(double) * (size_t)d);
+    double* Kh = (double*)malloc(sizeof(double) * (size_t)n_k * d);
+    double* Vh = (double*)malloc(sizeof(double) * (size_t)n_k * d);
+    int64_t cached_bh = -1;
+    if (!s || !q || !Kh || !Vh) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      if (failed) continue;
+      const int64_t bh = rows[r] / n_q, i = rows[r] % n_q;
+      if (bh != cached_bh) {
+        oracle_bf16_to_f64(K + bh * (int64_t)n_k * d, Kh, (int64_t)n_k * d);
+        oracle_bf16_to_f64(V + bh * (int64_t)n_k * d, Vh, (int64_t)n_k * d);
+        cached_bh = bh;
+      }
+      oracle_bf16_to_f64(Q + rows[r] * d, q, d);
+      const uint8_t* mrow = blockmask_row(M, bh / H, bh % H, i, Mb, Mh, bq, n_qb, n_kb);
+      attend_masked_row(q, Kh, Vh, n_k, d, scale, mrow, bk, i, wl, wr, s, O_rows + r * d, LSE_rows + r);
+    }
+    free(s); free(q); free(Kh); free(Vh);
+  }
+  return failed ? -1 : 0;
+}
+
+/* Visible (query, key) pairs of one (b, h) under the block mask and band. */
+int64_t oracle_blockmask_pairs(int n_q, int n_k, const uint8_t* M, int Mb, int Mh, int b, int h, int bq, int bk,
+                               int wl, int wr) {
+  const int64_t n_qb = (n_q + bq - 1) / bq, n_kb = (n_k + bk - 1) / bk;
+  int64_t n = 0;
+  for (int64_t i = 0; i < n_q; ++i) {
+    const uint8_t* mrow = blockmask_row(M, b, h, i, Mb, Mh, bq, n_qb, n_kb);
+    for (int64_t j = 0; j < n_k; ++j) n += blockmask_visible(mrow, i, j, bk, wl, wr);
+  }
+  return n;
+}

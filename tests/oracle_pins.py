@@ -59,6 +59,19 @@ page, section 四 point ③, asks for scaling without giving a recipe):
       oracle on them; the row function equals the full composition for
       arbitrary descales; O scales with descale_v and the scores with
       descale_q * descale_k.
+
+Block-sparse pins (the synthesis page, section 5 item 4: one block-skip mechanism for windows
+and dilated patterns), for key j visible to query i of (b, h) iff M[b][h][i // bq][j // bk] != 0
+and the band admits it:
+
+  P22 brute force at 50 digits, without the max shift, over random masks (shared or per batch
+      and head), block sizes and bands; rows that see no key give O = 0, LSE = -inf;
+  P23 an all-ones mask is the pinned window oracle (and so plain and causal attention);
+  P24 torch's fp64 CPU scaled_dot_product_attention with the mask expanded to keys and
+      queries by repetition, and the visible-pair count against that expansion;
+  P25 with no band, the rows of a query block equal plain attention over the keys of its
+      visible key blocks only (the others deleted), and a mask shared over heads equals its
+      per-head copy.
 """
 import math
 
@@ -623,7 +636,121 @@ def pin_p21_fp8_attention(orc):
         assert np.max(np.abs(o3 - o8)) <= 1e-12 and np.max(np.abs(l3 - l8)) <= 1e-12
 
 
-ALL_PINS = [pin_p1_bruteforce, pin_p2_rows_sum_to_one, pin_p3_constant_v, pin_p4_causal_row0,
+def _expand_mask(mask4, B, H, n_q, n_k, bq, bk, wl, wr):
+    """Element mask [B, H, N_q, N_k] from a block mask by repeating each block entry over its
+    rows and keys (numpy broadcasting and repetition), with the band applied."""
+    m = np.broadcast_to(mask4, (B, H) + mask4.shape[2:]).astype(bool)
+    e = np.repeat(np.repeat(m, bq, axis=2), bk, axis=3)[:, :, :n_q, :n_k]
+    i = np.arange(n_q)[:, None]
+    j = np.arange(n_k)[None, :]
+    band = np.ones((n_q, n_k), dtype=bool)
+    if wl >= 0:
+        band &= j >= i - wl
+    if wr >= 0:
+        band &= j <= i + wr
+    return e & band
+
+
+def _random_blockmask(rng, B, H, n_q, n_k, bq, bk, density):
+    Mb = B if rng.random() < 0.5 else 1
+    Mh = H if rng.random() < 0.5 else 1
+    shape = (Mb, Mh, -(-n_q // bq), -(-n_k // bk))
+    return (rng.random(shape) < density).astype(np.uint8)
+
+
+def pin_p22_blockmask_bruteforce(orc):
+    mpmath.mp.dps = 50
+    rng = RNG(2222)
+    for trial in range(10):
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        n_q, n_k, d = int(rng.integers(1, 8)), int(rng.integers(1, 9)), int(rng.integers(1, 4))
+        bq, bk = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        wl, wr = [(-1, -1), (-1, 0), (2, 1), (0, 3)][trial % 4]
+        mask = _random_blockmask(rng, B, H, n_q, n_k, bq, bk, 0.6)
+        q, k, v = (rng.normal(size=(B, H, n, d)) for n in (n_q, n_k, n_k))
+        scale = 0.7
+        o, lse = orc.attention_blockmask(q, k, v, mask, bq, bk, scale, wl, wr)
+        for b in range(B):
+            for h in range(H):
+                for i in range(n_q):
+                    vis = [j for j in range(n_k) if mask[b % mask.shape[0], h % mask.shape[1], i // bq, j // bk]
+                           and (wl < 0 or j >= i - wl) and (wr < 0 or j <= i + wr)]
+                    if not vis:
+                        assert np.all(o[b, h, i] == 0) and np.isneginf(lse[b, h, i]), (trial, b, h, i)
+                        continue
+                    e = {j: mpmath.exp(scale * mpmath.fsum(mpmath.mpf(float(q[b, h, i, c])) * float(k[b, h, j, c])
+                                                           for c in range(d))) for j in vis}
+                    z = mpmath.fsum(e.values())
+                    for c in range(d):
+                        ref = mpmath.fsum(e[j] * float(v[b, h, j, c]) for j in vis) / z
+                        assert abs(float(ref) - o[b, h, i, c]) <= 1e-13 * (1 + abs(float(ref))), (trial, b, h, i)
+                    assert abs(float(mpmath.log(z)) - lse[b, h, i]) <= 1e-13 * (1 + abs(lse[b, h, i]))
+
+
+def pin_p23_blockmask_all_ones(orc):
+    rng = RNG(2323)
+    q, k, v = (rng.normal(size=(2, 2, n, 6)) for n in (21, 17, 17))
+    for bq, bk in ((1, 1), (4, 5), (32, 64)):
+        ones = np.ones((-(-21 // bq), -(-17 // bk)), dtype=np.uint8)
+        for wl, wr in ((-1, -1), (-1, 0), (3, 2), (0, 0)):
+            o, lse = orc.attention_blockmask(q, k, v, ones, bq, bk, 0.4, wl, wr)
+            o_w, lse_w = orc.attention_window(q, k, v, wl, wr, 0.4)
+            assert np.max(np.abs(o - o_w)) <= 1e-14
+            fin = np.isfinite(lse_w)
+            assert np.array_equal(fin, np.isfinite(lse)) and np.max(np.abs(lse[fin] - lse_w[fin])) <= 1e-14
+
+
+def pin_p24_blockmask_torch(orc):
+    rng = RNG(2424)
+    for (B, H, n_q, n_k, bq, bk, wl, wr) in [(2, 3, 40, 50, 8, 16, -1, -1), (1, 2, 33, 33, 4, 8, -1, 0),
+                                             (2, 2, 30, 45, 5, 3, 10, 4), (1, 4, 64, 64, 16, 16, 20, 0)]:
+        mask = _random_blockmask(rng, B, H, n_q, n_k, bq, bk, 0.5)
+        q, k, v = (rng.normal(size=(B, H, n, 8)) for n in (n_q, n_k, n_k))
+        o, lse = orc.attention_blockmask(q, k, v, mask, bq, bk, 0.3, wl, wr)
+        em = _expand_mask(mask, B, H, n_q, n_k, bq, bk, wl, wr)
+        rows = em.any(-1)
+        qt, kt, vt = (torch.from_numpy(x) for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(em), scale=0.3)
+        ref = ref.numpy()
+        assert np.max(np.abs(np.where(rows[..., None], o - ref, 0.0))) <= 1e-12
+        assert np.all(o[~rows] == 0) and np.all(np.isneginf(lse[~rows]))
+        scores = (qt @ kt.transpose(-1, -2)) * 0.3
+        lse_ref = torch.logsumexp(scores.masked_fill(~torch.from_numpy(em), float("-inf")), dim=-1).numpy()
+        assert np.max(np.abs(lse[rows] - lse_ref[rows])) <= 1e-12
+        for b in range(B):
+            for h in range(H):
+                assert orc.blockmask_pairs(n_q, n_k, mask, b, h, bq, bk, wl, wr) == int(em[b, h].sum())
+
+
+def pin_p25_blockmask_deletion(orc):
+    rng = RNG(2525)
+    B, H, n_q, n_k, d, bq, bk = 2, 3, 24, 40, 5, 8, 5
+    mask = _random_blockmask(rng, B, H, n_q, n_k, bq, bk, 0.5)
+    mask = np.broadcast_to(mask, (B, H) + mask.shape[2:]).copy()
+    mask[0, 0, 0] = 0  # a query block that sees nothing
+    q, k, v = (rng.normal(size=(B, H, n, d)) for n in (n_q, n_k, n_k))
+    o, lse = orc.attention_blockmask(q, k, v, mask, bq, bk, 0.6)
+    for b in range(B):
+        for h in range(H):
+            for qb in range(mask.shape[2]):
+                keep = np.repeat(mask[b, h, qb].astype(bool), bk)[:n_k]
+                rows = slice(qb * bq, min(n_q, (qb + 1) * bq))
+                if not keep.any():
+                    assert np.all(o[b, h, rows] == 0) and np.all(np.isneginf(lse[b, h, rows]))
+                    continue
+                o_r, lse_r = orc.attention(q[b:b + 1, h:h + 1, rows], k[b:b + 1, h:h + 1, keep],
+                                           v[b:b + 1, h:h + 1, keep], False, 0.6)
+                assert np.max(np.abs(o_r[0, 0] - o[b, h, rows])) <= 1e-13
+                assert np.max(np.abs(lse_r[0, 0] - lse[b, h, rows])) <= 1e-13
+    # a mask shared over heads and batches equals its explicit copy
+    shared = (rng.random((1, 1, 3, 8)) < 0.5).astype(np.uint8)
+    o1, l1 = orc.attention_blockmask(q, k, v, shared, bq, bk, 0.6, 5, 1)
+    o2, l2 = orc.attention_blockmask(q, k, v, np.broadcast_to(shared, (B, H, 3, 8)).copy(), bq, bk, 0.6, 5, 1)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+ALL_PINS = [pin_p22_blockmask_bruteforce, pin_p23_blockmask_all_ones, pin_p24_blockmask_torch,
+            pin_p25_blockmask_deletion, pin_p1_bruteforce, pin_p2_rows_sum_to_one, pin_p3_constant_v, pin_p4_causal_row0,
             pin_p5_uniform_scores, pin_p6_one_hot, pin_p7_lse_identity, pin_p8_torch_sdpa,
             pin_p9_invariants, pin_p10_recurrence, pin_p11_window_bruteforce, pin_p12_window_special,
             pin_p13_window_torch, pin_p14_window_recurrence, pin_p15_backward_finite_differences,

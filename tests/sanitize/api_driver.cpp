@@ -93,7 +93,7 @@ static void test_configs() {
   void *Q = dev(0), *K = dev(1), *V = dev(2), *O = dev(3);
   float* L = devf(4);
   const int n = fa2_fwd_num_configs();
-  CHECK(n == 8);
+  CHECK(n == 10);
   for (int c = 0; c < n; ++c) {
     CHECK(fa2_fwd_config_name(c) != nullptr);
     CHECK(fa2_fwd_config(Q, K, V, O, L, 2, 3, 300, 400, 128, -1, 0, 0.1f, c, nullptr) == FA2_OK);

@@ -30,6 +30,15 @@ int oracle_attention_window_rows_bf16(const uint16_t* Q, const uint16_t* K, cons
                                       int64_t n_rows, double* O_rows, double* LSE_rows, int B, int H, int n_q,
                                       int n_k, int d, int wl, int wr, double scale);
 int64_t oracle_window_pairs(int n_q, int n_k, int wl, int wr);
+int oracle_attention_blockmask_f64(const double* Q, const double* K, const double* V, double* O, double* LSE,
+                                   int B, int H, int n_q, int n_k, int d, const uint8_t* M, int Mb, int Mh, int bq,
+                                   int bk, int wl, int wr, double scale);
+int oracle_attention_blockmask_rows_bf16(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                                         const int64_t* rows, int64_t n_rows, double* O_rows, double* LSE_rows,
+                                         int B, int H, int n_q, int n_k, int d, const uint8_t* M, int Mb, int Mh,
+                                         int bq, int bk, int wl, int wr, double scale);
+int64_t oracle_blockmask_pairs(int n_q, int n_k, const uint8_t* M, int Mb, int Mh, int b, int h, int bq, int bk,
+                               int wl, int wr);
 int oracle_backward_f64(const double* Q, const double* K, const double* V, const double* dO, double* dQ, double* dK,
                         double* dV, int B, int H, int n_q, int n_k, int d, int causal, double scale);
 void oracle_bf16_to_f64(const uint16_t* src, double* dst, int64_t n);
@@ -146,6 +155,29 @@ static void run_shape(int B, int H, int nq, int nk, int d) {
     for (int64_t r = 0; r < R; ++r) CHECK((isinf(L[r]) && isinf(Lr[r])) || fabs(L[r] - Lr[r]) < 1e-12);
     CHECK(oracle_window_pairs(nq, nk, wl, wr) >= 0);
     free(rows), free(Or), free(Lr);
+  }
+  /* block masks of every broadcast shape and block size, exactly sized, whole and sampled */
+  const int blk[][2] = {{1, 1}, {2, 3}, {4, 2}, {64, 64}};
+  for (size_t t = 0; t < sizeof blk / sizeof blk[0]; ++t) {
+    const int bq = blk[t][0], bk = blk[t][1];
+    const int n_qb = (nq + bq - 1) / bq, n_kb = (nk + bk - 1) / bk;
+    for (int Mb = 1; Mb <= B; Mb += (B > 1 ? B - 1 : 1))
+      for (int Mh = 1; Mh <= H; Mh += (H > 1 ? H - 1 : 1)) {
+        uint8_t* M = alloc((size_t)Mb * Mh * n_qb * n_kb);
+        for (int64_t e = 0; e < (int64_t)Mb * Mh * n_qb * n_kb; ++e) M[e] = (uint8_t)((e * 7 + t) % 3 != 0);
+        CHECK(oracle_attention_blockmask_f64(Q, K, V, O, L, B, H, nq, nk, d, M, Mb, Mh, bq, bk, 3, 2, scale) == 0);
+        int64_t* rows = alloc(R * 8);
+        for (int64_t r = 0; r < R; ++r) rows[r] = r;
+        double *Or = alloc(nQ * 8), *Lr = alloc(R * 8);
+        CHECK(oracle_attention_blockmask_rows_bf16(Qb, Kb, Vb, rows, R, Or, Lr, B, H, nq, nk, d, M, Mb, Mh, bq, bk,
+                                                   3, 2, scale) == 0);
+        CHECK(maxdiff(O, Or, nQ) < 1e-12);
+        for (int64_t r = 0; r < R; ++r) CHECK((isinf(L[r]) && isinf(Lr[r])) || fabs(L[r] - Lr[r]) < 1e-12);
+        CHECK(oracle_blockmask_pairs(nq, nk, M, Mb, Mh, B - 1, H - 1, bq, bk, 3, 2) >= 0);
+        CHECK(oracle_attention_blockmask_f64(Q, K, V, O, L, B, H, nq, nk, d, M, 2 * B + 1, Mh, bq, bk, -1, -1,
+                                             scale) != 0);
+        free(M), free(rows), free(Or), free(Lr);
+      }
   }
   free(Qb), free(Kb), free(Vb), free(Q), free(K), free(V), free(dO), free(O), free(L), free(O2), free(L2);
 }

@@ -352,7 +352,7 @@ def cfg(q=Q, k=K, v=V, o=O, l=L, B=1, H=2, nq=256, nk=256, d=64, wl=-1, wr=0, sc
 
 def test_config_validation():
     n = fa2.num_configs()
-    assert n == 8 and len({fa2.config_name(c) for c in range(n)}) == n
+    assert n == 10 and len({fa2.config_name(c) for c in range(n)}) == n
     assert cfg(c=-1) == CONFIG and cfg(c=n) == CONFIG
     assert cfg(q=None) == NULLPTR and cfg(d=96) == HEAD_DIM and cfg(wl=-5) == WINDOW and cfg(o=Q) == ALIAS
     assert fa2.load_library().fa2_fwd_config_name(n) is None

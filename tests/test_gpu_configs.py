@@ -14,7 +14,7 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-CONFIGS = list(range(8))
+CONFIGS = list(range(fa2.num_configs()))
 
 # (B, H, N_q, N_k, d, window): ragged tails, both head dims, plain, causal and banded, and a
 # B*H that is not a multiple of the 8 XCDs

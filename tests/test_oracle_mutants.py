@@ -48,6 +48,14 @@ MUTANTS = [
     ("fp8_v_descale_from_k", "Vh[e] = table[vc[e]] * (double)descale_v[bh];", "Vh[e] = table[vc[e]] * (double)descale_k[bh];"),
     ("fp8_q_descale_head0", "q[c] = table[Qc[rows[r] * d + c]] * (double)descale_q[bh];",
      "q[c] = table[Qc[rows[r] * d + c]] * (double)descale_q[0];"),
+    ("blockmask_key_block_by_query", "return mrow[j / bk] != 0;", "return mrow[i / bk] != 0;"),
+    ("blockmask_head_from_batch", "return M + (((b % Mb) * Mh + (h % Mh)) * n_qb + i / bq) * n_kb;",
+     "return M + (((b % Mb) * Mh + (b % Mh)) * n_qb + i / bq) * n_kb;"),
+    ("blockmask_query_block_ignored", "return M + (((b % Mb) * Mh + (h % Mh)) * n_qb + i / bq) * n_kb;",
+     "return M + (((b % Mb) * Mh + (h % Mh)) * n_qb + 0) * n_kb;"),
+    ("blockmask_band_left_ignored", "  if (wl >= 0 && j < i - wl) return 0;\n  if (wr >= 0 && j > i + wr) return 0;",
+     "  if (wr >= 0 && j > i + wr) return 0;"),
+    ("blockmask_empty_lse_zero", "*lse = -INFINITY; /* no visible key: O stays zero */", "*lse = 0.0;"),
     ("first_key_skipped", "for (int64_t j = j0; j < j1; ++j) {\n    double p = exp", "for (int64_t j = j0 + 1; j < j1; ++j) {\n    double p = exp"),
 ]
 

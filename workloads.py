@@ -124,3 +124,36 @@ def make_fp8_descales(B: int, H: int, seed: int, lo: float = 0.008, hi: float = 
     """fp32 [B, H] descales drawn log-uniformly from [lo, hi]."""
     g = np.random.default_rng(seed)
     return np.exp(g.uniform(np.log(lo), np.log(hi), (B, H))).astype(np.float32)
+
+
+# ---- block masks (input structure of the block-sparse forward) ----
+BLOCK_Q, BLOCK_K = 128, 64  # rows and keys per mask entry
+
+
+def dilated_block_mask(n_q: int, n_k: int, dilation: int, window: int, causal: bool,
+                       block_q: int = BLOCK_Q, block_k: int = BLOCK_K) -> np.ndarray:
+    """uint8 [ceil(n_q/block_q), ceil(n_k/block_k)]: a dilated sliding window at block granularity.
+
+    Query block qb always sees the key blocks that hold its own positions, [k0, k1] with
+    k0 = qb*block_q // block_k and k1 = ((qb+1)*block_q - 1) // block_k, and beyond them every
+    dilation-th key block, `window` of them on each side it may look to: k0 - dilation*t (and,
+    unless causal, k1 + dilation*t) for t = 1 .. window.  Key blocks past n_k are dropped."""
+    assert dilation >= 1 and window >= 0
+    n_qb, n_kb = -(-n_q // block_q), -(-n_k // block_k)
+    m = np.zeros((n_qb, n_kb), dtype=np.uint8)
+    for qb in range(n_qb):
+        k0 = qb * block_q // block_k
+        k1 = ((qb + 1) * block_q - 1) // block_k
+        m[qb, k0:min(k1, n_kb - 1) + 1] = 1
+        for t in range(1, window + 1):
+            if 0 <= k0 - dilation * t < n_kb:
+                m[qb, k0 - dilation * t] = 1
+            if not causal and k1 + dilation * t < n_kb:
+                m[qb, k1 + dilation * t] = 1
+    return m
+
+
+def random_block_mask(shape, density: float, seed: int) -> np.ndarray:
+    """uint8 block mask of the given shape with entries 1 at probability `density` (seeded)."""
+    g = np.random.default_rng(seed)
+    return (g.random(shape) < density).astype(np.uint8)
