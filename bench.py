@@ -127,6 +127,17 @@ def cpu_baseline(w, causal: bool, q, k, v, o, lse):
     return baseline, parity
 
 
+def blockmask_causal_pairs(mask, n_q: int, n_k: int, block_q: int = 128, block_k: int = 64) -> int:
+    """Visible (query, key) pairs of one head under a block mask and the causal band (key j <= i)."""
+    i = np.arange(n_q)
+    total = 0
+    for qb, kb in zip(*np.nonzero(mask)):
+        rows = i[qb * block_q:(qb + 1) * block_q]
+        k0, k1 = kb * block_k, min(n_k, (kb + 1) * block_k)
+        total += int(np.clip(np.minimum(rows + 1, k1) - k0, 0, None).sum())
+    return total
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +265,25 @@ def main():
                           "visible_pairs_per_head": pairs})
             log(f"{wx.name} window ({wl},{wr}): {msx:.3f} ms, {tf:.1f} TFLOP/s")
             del qx, kx, vx, ox, lx
+        # block-sparse: a dilated causal window on the long-sequence shape (each query block sees the
+        # key blocks of its own positions and every 2nd of the 128 key blocks before them); FLOPs
+        # counted over the visible (query, key) pairs, 4*d per pair
+        wx = workloads.C4
+        qx, kx, vx = workloads.make_qkv(wx, dev)
+        ox = torch.empty_like(qx)
+        lx = torch.empty((wx.B, wx.H, wx.n_q), dtype=torch.float32, device=dev)
+        mask = workloads.dilated_block_mask(wx.n_q, wx.n_k, 2, 64, True)
+        mt = torch.from_numpy(mask).to(dev)
+        msx = time_launches(lambda: fa2.forward_blocksparse(qx, kx, vx, mt, -1, 0, scale=wx.scale, out=ox, lse=lx),
+                            steps_x, args.warmup)
+        pairs = blockmask_causal_pairs(mask, wx.n_q, wx.n_k)
+        fl = 4.0 * wx.d * wx.B * wx.H * pairs
+        tf = fl / (msx * 1e-3) / 1e12
+        extra.append({"workload": f"{wx.name}_dilated_r2_w64_causal", "mask_blocks": [int(mask.sum()), int(mask.size)],
+                      "ms": round(msx, 4), "TFLOP/s": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                      "visible_pairs_per_head": pairs})
+        log(f"{wx.name} block-sparse dilated r2 w64 causal: {msx:.3f} ms, {tf:.1f} TFLOP/s")
+        del qx, kx, vx, ox, lx, mt
         # backward (deterministic two-pass dQ): FLOPs 2.5x the forward's (five products instead of two)
         for wx, cx in ((workloads.C3, False), (workloads.C3, True), (workloads.C4, False)):
             qx, kx, vx = workloads.make_qkv(wx, dev)

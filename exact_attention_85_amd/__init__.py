@@ -15,6 +15,9 @@ from ._binding import (  # noqa: F401
     default_config,
     decode_fp8,
     forward,
+    forward_blocksparse,
+    MASK_BLOCK_K,
+    MASK_BLOCK_Q,
     forward_config,
     forward_fp8,
     forward_splitkv,

@@ -91,6 +91,8 @@ def open_library(path: str):
     lib.fa2_fwd_fp8.restype = i
     lib.fa2_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, vp]
     lib.fa2_decode_fp8.restype = i
+    lib.fa2_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, i, i, i, i, f, vp]
+    lib.fa2_fwd_blocksparse.restype = i
     lib.fa2_fwd_config.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
     lib.fa2_fwd_config.restype = i
     lib.fa2_fwd_num_configs.argtypes = []
@@ -191,6 +193,38 @@ def forward_window(q, k, v, window_left: int, window_right: int, scale=None, out
     rc = lib.fa2_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                             B, H, n_q, n_k, d, int(window_left), int(window_right), _scale(scale, d),
                             _stream_handle(q.device))
+    _check(rc)
+    return out, lse
+
+
+MASK_BLOCK_Q, MASK_BLOCK_K = 128, 64  # FA2_MASK_BLOCK_Q, FA2_MASK_BLOCK_K
+
+
+def forward_blocksparse(q, k, v, block_mask, window_left: int = -1, window_right: int = -1, scale=None, out=None,
+                        lse=None):
+    """Attention under a block mask via fa2_fwd_blocksparse.
+
+    block_mask: uint8 tensor on q's device, [n_qb, n_kb], [Mh, n_qb, n_kb] or [Mb, Mh, n_qb, n_kb]
+    with n_qb = ceil(N_q / 128), n_kb = ceil(N_k / 64), Mb in {1, B}, Mh in {1, H}; a non-zero
+    entry makes its (128-row query block, 64-key block) visible, further limited by the band
+    (window_left, window_right) as forward_window.  Returns (o, lse); rows that see no key get
+    O = 0 and LSE = -inf."""
+    lib = load_library()
+    B, H, n_q, n_k, d = _check_inputs(q, k, v)
+    if not isinstance(block_mask, torch.Tensor) or block_mask.dtype != torch.uint8:
+        raise TypeError("block_mask must be a uint8 torch tensor")
+    n_qb, n_kb = -(-n_q // MASK_BLOCK_Q), -(-n_k // MASK_BLOCK_K)
+    m = block_mask
+    while m.dim() < 4:
+        m = m.unsqueeze(0)
+    if (m.dim() != 4 or tuple(m.shape[2:]) != (n_qb, n_kb) or m.shape[0] not in (1, B) or m.shape[1] not in (1, H)
+            or not m.is_contiguous() or m.device != q.device):
+        raise ValueError(f"block_mask must be a contiguous uint8 [Mb, Mh, {n_qb}, {n_kb}] tensor on q's device "
+                         f"(Mb in {{1, {B}}}, Mh in {{1, {H}}}), got {tuple(block_mask.shape)} on {block_mask.device}")
+    out, lse = _outputs(out, lse, B, H, n_q, d, q.device)
+    rc = lib.fa2_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                 B, H, n_q, n_k, d, m.data_ptr(), int(m.shape[0]), int(m.shape[1]),
+                                 int(window_left), int(window_right), _scale(scale, d), _stream_handle(q.device))
     _check(rc)
     return out, lse
 

@@ -199,6 +199,38 @@ int fa2_fwd_config(const void* Q, const void* K, const void* V, void* O, float* 
   return FA2_OK;
 }
 
+int fa2_fwd_blocksparse(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q,
+                        int N_k, int d, const unsigned char* block_mask, int mask_batches, int mask_heads,
+                        int window_left, int window_right, float scale, void* stream) {
+  if (!block_mask) return FA2_ERR_NULLPTR;
+  int rc = check_common(Q, K, V, O, LSE, B, H, N_q, N_k, d, scale);
+  if (rc != FA2_OK) return rc;
+  if (window_left < -1 || window_right < -1 || window_left > kMaxWindow || window_right > kMaxWindow)
+    return FA2_ERR_WINDOW;
+  if (!(mask_batches == 1 || mask_batches == B) || !(mask_heads == 1 || mask_heads == H)) return FA2_ERR_BAD_SHAPE;
+  if (!fwd_fits(B, H, N_q)) return FA2_ERR_BAD_SHAPE;
+  rc = check_alias(Q, K, V, O, LSE, B, H, N_q, N_k, d, nullptr, 0);
+  if (rc != FA2_OK) return rc;
+  const long long n_qb = (N_q + fa2::kMaskBlockQ - 1) / fa2::kMaskBlockQ;
+  const long long n_kb = (N_k + fa2::kMaskBlockK - 1) / fa2::kMaskBlockK;
+  const long long mask_bytes = (long long)mask_batches * mask_heads * n_qb * n_kb;
+  const long long bh = (long long)B * H;
+  const Range m = range_of(block_mask, mask_bytes);
+  if (overlap(m, range_of(O, bh * N_q * d * 2)) || overlap(m, range_of(LSE, bh * N_q * 4))) return FA2_ERR_ALIAS;
+  fa2::FwdParams p = make_params(Q, K, V, O, LSE, B, H, N_q, N_k, d, 0, scale);
+  p.wl = window_left;
+  p.wr = window_right;
+  p.bmask = block_mask;
+  p.bm_n_kb = (int)n_kb;
+  p.bm_stride_h = mask_heads == 1 ? 0 : n_qb * n_kb;
+  p.bm_stride_b = mask_batches == 1 ? 0 : (long long)mask_heads * n_qb * n_kb;
+  // the workgroup order the tuned table picks for the shape (the masked kernel is the 4-wave one)
+  const bool banded = window_left >= 0 || window_right >= 0;
+  p.sched = fa2::kFwdConfigs[fa2::fwd_default_config(d, banded, N_q, bh)].sched;
+  if (fa2::launch_fwd_blockmask(p, static_cast<hipStream_t>(stream)) != hipSuccess) return FA2_ERR_HIP;
+  return FA2_OK;
+}
+
 int fa2_fwd_num_configs(void) { return fa2::kNumFwdConfigs; }
 
 const char* fa2_fwd_config_name(int config) {

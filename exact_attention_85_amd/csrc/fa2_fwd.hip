@@ -262,8 +262,11 @@ __device__ __forceinline__ void tile_step(WaveRows<D>& w, const LdsAddr<D>& la, 
 // reading one stage does not depend on the loads in flight into the other:
 // tile j+1 streams in while tile j computes, and one barrier per tile both
 // publishes tile j and retires the buffer of tile j-1.
-template <int D, int NW, bool SPLIT>
+//   MASK   stream only the key tiles that the block mask row of the workgroup's
+//          query block marks (p.bmask; 128-row workgroups, NW == 4, one mask row each)
+template <int D, int NW, bool SPLIT, bool MASK = false>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float sl2, unsigned qsign) {
+  static_assert(!MASK || (NW == 4 && !SPLIT), "block masks are read per 128-row workgroup");
   constexpr int BR = 32 * NW;
   constexpr int KT = D / 16;
   constexpr int NB = D / 32;
@@ -354,9 +357,49 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
           kk, row_lo, row_hi, sl2, lane);                                                            \
   } while (0)
 
+  if (MASK) {
+    // Block-sparse: tile t holds key block kfirst/kBC + t, streamed only when the mask row of
+    // this query block marks it.  The tile after the current one is found by a scan that every
+    // lane makes alike; the two-stage ring and its barriers are those of the dense loop below.
+    // The mask row is read through the constant address space, so the reads are scalar loads
+    // (scalar cache, lgkmcnt): a read never waits for the tile loads in flight (vmcnt).  The
+    // current dword of the row stays in a register; most steps need no load at all.
+    typedef __attribute__((address_space(4))) const unsigned cu32;
+    const unsigned long long mrow =
+        (unsigned long long)(uintptr_t)p.bmask + (unsigned long long)(bh / p.H) * p.bm_stride_b +
+        (unsigned long long)(bh % p.H) * p.bm_stride_h + (unsigned long long)qb * p.bm_n_kb + kfirst / kBC;
+    unsigned long long word_at = ~0ull;  // byte address of the dword held in `word`
+    unsigned word = 0;
+    auto next_active = [&](int t) {
+      for (; t < n_tiles; ++t) {
+        const unsigned long long a = mrow + (unsigned long long)t;
+        if ((a & ~3ull) != word_at) {
+          word_at = a & ~3ull;
+          word = *reinterpret_cast<cu32*>(word_at);
+        }
+        if ((word >> (8 * (a & 3))) & 0xffu) break;
+      }
+      return t;
+    };
+    int ta = next_active(0);
+    if (ta < n_tiles) issue_tile<D, NW>(krs, vrs, lds[0][0], lds[0][1], kfirst + ta * kBC, wave, lane);
+    while (ta < n_tiles) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      const int tb = next_active(ta + 1);
+      if (tb < n_tiles) issue_tile<D, NW>(krs, vrs, lds[1][0], lds[1][1], kfirst + tb * kBC, wave, lane);
+      FA2_STEP(0, kfirst + ta * kBC);
+      if (tb >= n_tiles) break;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      ta = next_active(tb + 1);
+      if (ta < n_tiles) issue_tile<D, NW>(krs, vrs, lds[0][0], lds[0][1], kfirst + ta * kBC, wave, lane);
+      FA2_STEP(1, kfirst + tb * kBC);
+    }
+  }
   // unrolled by two so that each stage's LDS offsets are compile-time constants
-  if (n_tiles > 0) issue_tile<D, NW>(krs, vrs, lds[0][0], lds[0][1], kfirst, wave, lane);
-  for (int j = 0; j < n_tiles; j += 2) {
+  if (!MASK && n_tiles > 0) issue_tile<D, NW>(krs, vrs, lds[0][0], lds[0][1], kfirst, wave, lane);
+  for (int j = 0; !MASK && j < n_tiles; j += 2) {
     const int k0 = kfirst + j * kBC;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -860,7 +903,7 @@ void fold_scale(float scale, float* sl2, unsigned* qsign) {
   *qsign = scale < 0.f ? 0x80008000u : 0u;
 }
 
-template <int D, int NW, bool SPLIT>
+template <int D, int NW, bool SPLIT, bool MASK = false>
 hipError_t launch_tile(const FwdParams& p, hipStream_t stream) {
   constexpr int BR = 32 * NW;
   const long long n_qb = (p.n_q + BR - 1) / BR;
@@ -868,7 +911,8 @@ hipError_t launch_tile(const FwdParams& p, hipStream_t stream) {
   float sl2;
   unsigned qsign;
   fold_scale(p.scale, &sl2, &qsign);
-  hipLaunchKernelGGL((fwd_kernel<D, NW, SPLIT>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, p, sl2, qsign);
+  hipLaunchKernelGGL((fwd_kernel<D, NW, SPLIT, MASK>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, p, sl2,
+                     qsign);
   return hipGetLastError();
 }
 
@@ -906,6 +950,10 @@ hipError_t launch_fwd(const FwdParams& p_in, int config, hipStream_t stream) {
   if (c.kernel == 1) return p.d == 128 ? launch_pp<128>(p, stream) : launch_pp<64>(p, stream);
   if (c.kernel == 2) return p.d == 128 ? launch_tile<128, 8, false>(p, stream) : launch_tile<64, 8, false>(p, stream);
   return p.d == 128 ? launch_tile<128, 4, false>(p, stream) : launch_tile<64, 4, false>(p, stream);
+}
+
+hipError_t launch_fwd_blockmask(const FwdParams& p, hipStream_t stream) {
+  return p.d == 128 ? launch_tile<128, 4, false, true>(p, stream) : launch_tile<64, 4, false, true>(p, stream);
 }
 
 hipError_t launch_splitkv_partial(const FwdParams& p, hipStream_t stream) {

@@ -35,8 +35,17 @@ struct FwdParams {
   float scale;
   int num_splits;    // 1 in forward mode
   int split_len;     // keys per chunk (N_k in forward mode)
-  int sched;         // workgroup order bits (fa2_device.h: kSchedRemap, kSchedQbMajor)
+  int sched;         // workgroup order bits (kSchedRemap, kSchedQbMajor)
+  // block-sparse forward: byte mask [Mb][Mh][ceil(N_q/128)][bm_n_kb], one entry per 128-row
+  // query block and 64-key tile; strides in entries, 0 for a shared (size-1) dimension
+  const uint8_t* bmask;
+  long long bm_stride_b, bm_stride_h;
+  int bm_n_kb;
 };
+
+// Rows and keys per block-mask entry (the 4-wave kernel's query block and key tile).
+constexpr int kMaskBlockQ = 128;
+constexpr int kMaskBlockK = 64;
 
 // Forward kernel configurations (fa2_fwd_config): the kernel and the workgroup order.
 //   kernel 0: 4 waves, 128 query rows per workgroup, two workgroups per compute unit
@@ -133,6 +142,9 @@ int splitkv_run(const void* Q, const void* K, const void* V, void* O, float* LSE
 // Forward: O, LSE, with configuration `config` (0 .. kNumFwdConfigs - 1; N_q == 1 always
 // takes the decode kernel).  Returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdParams& p, int config, hipStream_t stream);
+
+// Block-sparse forward (p.bmask set): the 4-wave kernel with the workgroup order in p.sched.
+hipError_t launch_fwd_blockmask(const FwdParams& p, hipStream_t stream);
 
 // Split-KV pass 1 (partials into the workspace) and pass 2 (merge into O, LSE).
 hipError_t launch_splitkv_partial(const FwdParams& p, hipStream_t stream);

@@ -110,6 +110,37 @@ int fa2_fwd_window(const void* Q, const void* K, const void* V, void* O, float* 
                    float scale, void* stream);
 
 /*
+ * fa2_fwd_blocksparse — attention forward under a block mask (the synthesis
+ * page, section 5 item 4: the causal block skip extended to sliding windows
+ * and dilated patterns as one sparse-block-skip mechanism).
+ *
+ * block_mask: device bytes [mask_batches][mask_heads][ceil(N_q/128)][ceil(N_k/64)],
+ * mask_batches in {1, B}, mask_heads in {1, H} (a size-1 dimension is shared by
+ * every batch or head).  One entry per (128-row query block, 64-key block):
+ * key j is visible to query i of (b, h) iff j < N_k, the entry
+ * [b mod mask_batches][h mod mask_heads][i / 128][j / 64] is non-zero, and the
+ * band admits it: (window_left < 0 or j >= i - window_left) and
+ * (window_right < 0 or j <= i + window_right), as fa2_fwd_window.  Each
+ * workgroup streams only the key tiles its mask row marks, and masks inside a
+ * tile only at the band's edges and the key tail.  A row that sees no key
+ * gets O = 0 and LSE = -inf.  A dilated pattern is a mask whose entries skip
+ * key blocks at a stride; the all-ones mask is fa2_fwd_window.
+ *
+ * The mask is read in aligned 4-byte words (never past the aligned word that
+ * holds its last byte).
+ *
+ * Other arguments, layouts and errors as fa2_fwd_window; FA2_ERR_NULLPTR for
+ * a NULL mask, FA2_ERR_BAD_SHAPE for mask dimensions other than 1 or B / H,
+ * FA2_ERR_ALIAS when O or LSE overlaps the mask.
+ */
+#define FA2_MASK_BLOCK_Q 128
+#define FA2_MASK_BLOCK_K 64
+int fa2_fwd_blocksparse(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                        int B, int H, int N_q, int N_k, int d, const unsigned char* block_mask,
+                        int mask_batches, int mask_heads, int window_left, int window_right,
+                        float scale, void* stream);
+
+/*
  * Forward configurations (the synthesis page, section 3 item 3: FA2 picks its
  * block sizes by hand from a few candidates; section 5 item 1: search block
  * sizes, warp counts and stages per shape instead).  A configuration is a

@@ -88,13 +88,16 @@ def balanced_order(n):
     return out
 
 
-def assert_all_rows(q, k, v, o, lse, causal, scale, what, heads_per_call=4, tol_o=TOL_O, tol_lse=TOL_LSE):
+def assert_all_rows(q, k, v, o, lse, causal, scale, what, heads_per_call=4, tol_o=TOL_O, tol_lse=TOL_LSE,
+                    rows_oracle=None):
     """Every row of a GPU result (o [B,H,N_q,d] bf16, lse [B,H,N_q] fp32) against the oracle.
 
     The oracle runs on the bf16 bits of q, k, v, a few heads per call, so host memory stays
     bounded; each call takes all rows of its heads.  Reports max|dO| and max|dLSE| with their
     (b, h, i, c) locations, the reference value there, the mean error and the count over the
-    tolerance, and asserts max|dO| <= tol_o, max|dLSE| <= tol_lse and no NaN."""
+    tolerance, and asserts max|dO| <= tol_o, max|dLSE| <= tol_lse and no NaN.  rows_oracle(qb, kb,
+    vb, rows, b) replaces the plain oracle (qb, kb, vb: bf16 bits of batch b, [1, H, N, d]); rows
+    whose reference LSE is -inf (no visible key) must have LSE = -inf and O = 0."""
     B, H, n_q, d = q.shape
     worst_o = (-1.0, None, 0.0)
     worst_l = (-1.0, None, 0.0)
@@ -109,9 +112,17 @@ def assert_all_rows(q, k, v, o, lse, causal, scale, what, heads_per_call=4, tol_
         for h0 in range(0, H, heads_per_call):
             h1 = min(H, h0 + heads_per_call)
             rows = (np.arange(h0, h1, dtype=np.int64)[:, None] * n_q + order[None, :]).reshape(-1)
-            o_ref, l_ref = oracle.attention_rows_bf16(qb, kb, vb, rows, causal, scale)
+            if rows_oracle is None:
+                o_ref, l_ref = oracle.attention_rows_bf16(qb, kb, vb, rows, causal, scale)
+            else:
+                o_ref, l_ref = rows_oracle(qb, kb, vb, rows, b)
             hh, ii = rows // n_q, rows % n_q
             o_g, l_g = og[hh, ii], lg[hh, ii]
+            empty = np.isneginf(l_ref)
+            if empty.any():
+                if not (np.all(np.isneginf(l_g[empty])) and np.all(o_g[empty] == 0)):
+                    raise AssertionError(f"{what}: a row with no visible key is not O = 0, LSE = -inf")
+                l_ref, l_g = np.where(empty, 0.0, l_ref), np.where(empty, 0.0, l_g)
             if not (np.all(np.isfinite(o_g)) and np.all(np.isfinite(l_g))):
                 raise AssertionError(f"{what}: non-finite output in batch {b}, heads {h0}..{h1 - 1}")
             do = np.abs(o_g - o_ref)

@@ -120,6 +120,28 @@ static void test_configs() {
       }
 }
 
+static void test_blocksparse() {
+  void *Q = dev(0), *K = dev(1), *V = dev(2), *O = dev(3);
+  float* L = devf(4);
+  const unsigned char* M = static_cast<const unsigned char*>(dev(10));
+  CHECK(fa2_fwd_blocksparse(Q, K, V, O, L, 2, 3, 300, 700, 64, nullptr, 1, 1, -1, -1, 0.1f, nullptr) ==
+        FA2_ERR_NULLPTR);
+  CHECK(fa2_fwd_blocksparse(Q, K, V, O, L, 2, 3, 300, 700, 64, M, 3, 1, -1, -1, 0.1f, nullptr) == FA2_ERR_BAD_SHAPE);
+  CHECK(fa2_fwd_blocksparse(Q, K, V, O, L, 2, 3, 300, 700, 64, M, 1, 2, -1, -1, 0.1f, nullptr) == FA2_ERR_BAD_SHAPE);
+  // per-(batch, head) mask: 3 query blocks x 11 key blocks each
+  CHECK(fa2_fwd_blocksparse(Q, K, V, O, L, 2, 3, 300, 700, 64, M, 2, 3, 50, 0, 0.1f, nullptr) == FA2_OK);
+  const fa2::FwdParams& p = stub::rec.fwd;
+  CHECK(p.bmask == M && p.bm_n_kb == 11 && p.bm_stride_h == 33 && p.bm_stride_b == 99 && p.wl == 50 && p.wr == 0);
+  CHECK(strcmp(stub::rec.kind, "fwd_blockmask") == 0);
+  // shared over batches and heads: zero strides
+  CHECK(fa2_fwd_blocksparse(Q, K, V, O, L, 2, 3, 300, 700, 64, M, 1, 1, -1, -1, 0.1f, nullptr) == FA2_OK);
+  CHECK(stub::rec.fwd.bm_stride_h == 0 && stub::rec.fwd.bm_stride_b == 0);
+  // the largest head: N_k * d just under 2^30
+  CHECK(fa2_fwd_blocksparse(Q, K, V, O, L, 1, 1, 1 << 10, (1 << 24) - 1, 64, M, 1, 1, -1, -1, 0.1f, nullptr) ==
+        FA2_OK);
+  CHECK(stub::rec.fwd.bm_n_kb == (1 << 18));
+}
+
 static void test_splitkv() {
   void *Q = dev(0), *K = dev(1), *V = dev(2), *O = dev(3), *W = dev(5);
   float* L = devf(4);
@@ -225,6 +247,7 @@ int main() {
   test_fwd();
   test_window();
   test_configs();
+  test_blocksparse();
   test_splitkv();
   test_num_splits();
   test_bwd();

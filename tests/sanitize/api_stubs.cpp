@@ -60,6 +60,13 @@ hipError_t launch_decode_fp8(const Fp8Params& p, hipStream_t) {
   return stub::rec.result;
 }
 
+hipError_t launch_fwd_blockmask(const FwdParams& p, hipStream_t) {
+  stub::rec.kind = "fwd_blockmask";
+  stub::rec.fwd = p;
+  ++stub::rec.calls;
+  return stub::rec.result;
+}
+
 hipError_t launch_xcc_probe(int*, int, hipStream_t) {
   stub::rec.kind = "xcc_probe";
   ++stub::rec.calls;

@@ -24,6 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_decode_fp8", "fa2_fp8_vt_stride", "fa2_fwd",
+                                    "fa2_fwd_blocksparse",
                                     "fa2_fwd_config", "fa2_fwd_config_name", "fa2_fwd_default_config",
                                     "fa2_fwd_fp8", "fa2_fwd_num_configs", "fa2_fwd_splitkv",
                                     "fa2_fwd_splitkv_noalloc", "fa2_fwd_window", "fa2_num_splits",
@@ -362,3 +363,20 @@ def test_config_validation():
         fa2.default_config(96, False, 100)
     assert fa2.load_library().fa2_probe_xcc(None, 10, None) == NULLPTR
     assert fa2.load_library().fa2_probe_xcc(Q, 0, None) == BAD_SHAPE
+
+
+MASK = 0x10000000000 + 9 * 64 * GB
+
+
+def bsp(q=Q, k=K, v=V, o=O, l=L, B=2, H=3, nq=300, nk=700, d=64, m=MASK, Mb=1, Mh=1, wl=-1, wr=-1, scale=0.125):
+    return fa2.load_library().fa2_fwd_blocksparse(q, k, v, o, l, B, H, nq, nk, d, m, Mb, Mh, wl, wr, scale, None)
+
+
+def test_blocksparse_validation():
+    assert bsp(m=None) == NULLPTR and bsp(q=None) == NULLPTR
+    assert bsp(Mb=3) == BAD_SHAPE and bsp(Mh=2) == BAD_SHAPE and bsp(Mb=0) == BAD_SHAPE
+    assert bsp(d=96) == HEAD_DIM and bsp(wl=-2) == WINDOW and bsp(scale=float("inf")) == BAD_SCALE
+    assert bsp(o=Q) == ALIAS
+    # O or LSE over the mask: [Mb][Mh][3][11] bytes at MASK
+    assert bsp(o=MASK + 16) == ALIAS and bsp(l=MASK + 2 * 3 * 3 * 11 - 1, Mb=2, Mh=3) == ALIAS
+    assert bsp(B=1 << 12, H=1 << 12, nq=128, nk=16) == BAD_SHAPE  # launch limits
