@@ -43,9 +43,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha(path: str = KERNEL_SRC) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+TUNE_TABLE = os.path.join(ROOT, "exact_attention_85_amd", "csrc", "fa2_tune_table.h")
+
+
+def kernel_source_sha(*paths) -> str:
+    """sha256[:16] of the concatenated sources (fa2_fwd.hip alone by default)."""
+    h = hashlib.sha256()
+    for path in paths or (KERNEL_SRC,):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def env_info() -> dict:
@@ -54,19 +61,21 @@ def env_info() -> dict:
     props = torch.cuda.get_device_properties(0)
     return {"gpu": props.name, "arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
             "hip": torch.version.hip, "torch": torch.__version__,
-            "kernel_sources": {os.path.basename(p): kernel_source_sha(p) for p in (KERNEL_SRC, BWD_SRC, FP8_SRC)}}
+            "kernel_sources": {os.path.basename(p): kernel_source_sha(p)
+                               for p in (KERNEL_SRC, TUNE_TABLE, BWD_SRC, FP8_SRC)}}
 
 
-def measured_traffic(key: str, src: str = KERNEL_SRC):
+def measured_traffic(key: str, src=(KERNEL_SRC,)):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None when
-    absent or taken on a different kernel source."""
+    absent or taken on different sources (the kernel file, and for the bf16
+    forward also the table that picks its configuration)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     e = t.get(key)
-    if not e or e.get("kernel_source_sha") != kernel_source_sha(src):
+    if not e or e.get("kernel_source_sha") != kernel_source_sha(*src):
         return None
     return e.get("hbm_bytes_per_launch")
 
@@ -212,10 +221,11 @@ def main():
 
     peak = PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
     if args.fp8:
-        kname, traffic = "fwd_fp8_kernel<128,4>", measured_traffic(f"fwd_fp8_kernel:{w.name}:noncausal", FP8_SRC)
+        kname, traffic = "fwd_fp8_kernel<128,4>", measured_traffic(f"fwd_fp8_kernel:{w.name}:noncausal", (FP8_SRC,))
         alg_bytes = w.B * w.H * (w.n_q * w.d + 2 * w.n_k * w.d + 2 * w.n_q * w.d + 4 * w.n_q)  # 1-byte Q, K, V codes
     else:
-        kname, traffic = "fwd_pp_kernel<128>", measured_traffic(f"fwd_pp_kernel:{w.name}:noncausal")
+        kname, traffic = "fwd_pp_kernel<128>", measured_traffic(f"fwd_pp_kernel:{w.name}:noncausal",
+                                                                (KERNEL_SRC, TUNE_TABLE))
         alg_bytes = w.io_bytes()
     result = {
         "metric": METRIC_FP8 if args.fp8 else METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,

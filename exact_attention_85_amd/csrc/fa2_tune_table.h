@@ -26,6 +26,7 @@ constexpr TuneRow kTuneTable[] = {
     {64, 1, 724, 9},  // tile256_noremap_qbmajor
     {128, 0, 1, 0},  // tile128_remap_headmajor
     {128, 0, 2896, 6},  // pingpong256_noremap_headmajor
+    {128, 0, 5793, 4},  // pingpong256_remap_headmajor
     {128, 1, 1, 3},  // tile128_noremap_qbmajor
     {128, 1, 724, 0},  // tile128_remap_headmajor
     {128, 1, 2896, 7},  // pingpong256_noremap_qbmajor

@@ -89,21 +89,29 @@ def time_configs(B, H, n, d, banded, reps, configs):
 NOISE = 0.02  # timings within 2 % of the fastest count as a tie
 
 
+def low_traffic(config: int) -> bool:
+    """The renumbered head-major order runs each head's blocks on one XCD, so each head's K/V is
+    fetched into one L2: HBM reads measured 1.0-1.7x the input bytes against 3.0-5.7x for the other
+    orders (with the renumbering and query-block-major order every XCD sees every head)."""
+    return fa2.config_name(config).endswith("_remap_headmajor")
+
+
 def table_rows(results, noise=NOISE):
     """(d, banded) -> rows (nq_min, config): per measured length the fastest configuration,
-    applying from the geometric midpoint to the previous measured length.  A configuration
-    within `noise` of the fastest counts as tied with it, and among tied ones the choice of the
-    previous length is kept, so that the table does not switch configurations on run-to-run
-    noise; equal neighbours are merged."""
+    applying from the geometric midpoint to the previous measured length.  Configurations within
+    `noise` of the fastest count as tied with it; among tied ones the lower-traffic (renumbered)
+    orders come first, then the previous length's choice (so that the table does not switch on
+    run-to-run noise), then the faster.  Equal neighbours are merged."""
     rows = {}
     for (d, banded), per_n in sorted(results.items()):
         lens = sorted(per_n)
         out = []
         for i, n in enumerate(lens):
             t = per_n[n]
-            best = min(t, key=t.get)
-            if out and t.get(out[-1][1], float("inf")) <= t[best] * (1 + noise):
-                best = out[-1][1]
+            fastest = min(t.values())
+            tied = [c for c in t if t[c] <= fastest * (1 + noise)]
+            prev = out[-1][1] if out else None
+            best = min(tied, key=lambda c: (not low_traffic(c), c != prev, t[c]))
             nq_min = 1 if i == 0 else int(round((lens[i - 1] * n) ** 0.5))
             if not out or out[-1][1] != best:
                 out.append((nq_min, best))
@@ -257,8 +265,9 @@ def main():
           f"Command: `python -m exact_attention_85_amd.tune --reps {reps}{' --quick' if quick else ''}`"
           f" ({source}).", f"{TOKENS} query tokens per launch (B*H = {TOKENS}/N), N_q = N_k = N, seeded N(0,1) bf16,"
           " scale 1/sqrt(d). TFLOP/s from the median of the launches of each configuration (timed in rotation);"
-          f" causal FLOPs halved. The table keeps the previous length's choice while it is within {100 * NOISE:.0f} %"
-          " of the fastest (column `table`).", "",
+          f" causal FLOPs halved. Configurations within {100 * NOISE:.0f} % of the fastest count as tied; ties go to the"
+          " XCD-renumbered head-major orders (fewest HBM bytes, `xcd_order_counters_c2_c3_c4.md`), then to the previous length's"
+          " choice (column `table`).", "",
           probe_text(probe) if "launches" in probe else
           f"Dispatch probe: {100 * probe['frac_on_xcd_id_mod_8']:.1f} % of {probe['workgroups']} workgroups ran on "
           f"XCD (id mod 8); per-XCD counts {probe['per_xcd']}.", "",

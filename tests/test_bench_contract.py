@@ -28,7 +28,8 @@ def _check_line(d, dtype, with_cpu):
     assert d["ms_per_step_min"] <= d["ms_per_step_median"]
     assert "workload" in d["config"]
     e = d["env"]
-    assert e["compute_units"] >= 1 and set(e["kernel_sources"]) == {"fa2_fwd.hip", "fa2_bwd.hip", "fa2_fp8.hip"}
+    assert e["compute_units"] >= 1 and set(e["kernel_sources"]) == {"fa2_fwd.hip", "fa2_tune_table.h", "fa2_bwd.hip",
+                                                                           "fa2_fp8.hip"}
     r = d["roofline"]
     for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert key in r, key

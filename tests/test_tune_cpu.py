@@ -14,6 +14,9 @@ def test_table_rows_pick_the_fastest_and_merge_neighbours():
     rows = tune.table_rows(results)
     assert rows[(128, 0)] == [(1, 0), (2048, 4)]      # 4096 and 16384 both pick 4: merged
     assert rows[(64, 1)] == [(1, 1), (2048, 3)]
+    # ties (within 2 %) go to the renumbered head-major order (configs 0, 4, 8), then to the previous choice
+    tied = {(128, 0): {1024: {0: 1.00, 2: 0.99}, 4096: {4: 1.00, 6: 0.985, 7: 0.90}, 8192: {4: 1.0, 6: 0.99}}}
+    assert tune.table_rows(tied)[(128, 0)] == [(1, 0), (2048, 7), (5793, 4)]
 
 
 def test_written_header_round_trips(tmp_path):
