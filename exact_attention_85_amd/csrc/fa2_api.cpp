@@ -291,8 +291,7 @@ int fa2_num_splits(int B, int H, int N_q, int N_k, int d, int num_cus) {
 size_t fa2_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d) {
   if (B < 1 || H < 1 || N_q < 1 || N_k < 1 || d < 1) return 0;
   const size_t R = (size_t)B * (size_t)H * (size_t)N_q;
-  const size_t n_slot = (size_t)fa2::bwd_num_slots(B, H, N_k);  // one dQ partial per group of key blocks
-  return (2 * R + n_slot * R * (size_t)d) * 4u;
+  return 2 * R * 4u;  // LSE * log2(e) and D per query row
 }
 
 int fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
@@ -302,11 +301,12 @@ int fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const vo
   // the forward's own checks on Q, K, V, O, LSE (LSE read-only here)
   int rc = check_common(Q, K, V, O, LSE, B, H, N_q, N_k, d, scale);
   if (rc != FA2_OK) return rc;
-  // the three launches: D and LSE*log2e (256 work-items per 256/(d/8) rows), the key-block
-  // groups (one workgroup of 256 per group), the dQ reduction (one work-item per 4 elements)
+  // the three launches: D and LSE*log2e (256 work-items per 256/(d/8) rows), the key blocks
+  // (one workgroup of 256 per 128 keys), the query blocks (one workgroup of 256 per 128 rows)
   const long long R_all = (long long)B * H * N_q;
   if (!launch_fits((R_all + 256 / (d / 8) - 1) / (256 / (d / 8)), 256) ||
-      !launch_fits(fa2::bwd_num_slots(B, H, N_k) * B * H, 256) || !launch_fits((R_all * (d / 4) + 255) / 256, 256))
+      !launch_fits((long long)((N_k + 127) / 128) * B * H, 256) ||
+      !launch_fits((long long)((N_q + 127) / 128) * B * H, 256))
     return FA2_ERR_BAD_SHAPE;
   const size_t need = fa2_bwd_workspace_bytes(B, H, N_q, N_k, d);
   if (!workspace || workspace_bytes < need) return FA2_ERR_WORKSPACE;
@@ -336,7 +336,6 @@ int fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const vo
   float* ws = static_cast<float*>(workspace);
   p.l2vec = ws;
   p.dvec = ws + R;
-  p.ws_dq = ws + 2 * R;
   p.B = B;
   p.H = H;
   p.n_q = N_q;

@@ -62,30 +62,9 @@ extern const FwdConfig kFwdConfigs[kNumFwdConfigs];
 // The configuration fa2_fwd takes for a shape (the measured table in fa2_tune_table.h).
 int fwd_default_config(int d, bool banded, int n_q, long long n_bh);
 
-// Backward: 128-key blocks that one workgroup takes one after the other,
-// sharing one dQ partial slot.  The largest of 8, 4 and 2 that still leaves at
-// least 256 workgroups (one per compute unit of an MI355X), else 1.  Each
-// doubling halves the dQ partials; fewer workgroups than compute units would
-// leave the chip idle.
-__host__ __device__ inline int bwd_blocks_per_group(long long B, long long H, long long n_k) {
-  const long long bh = B * H;  // B, H < 2^31: no overflow
-  if (bh >= 256) return 8;     // every group count leaves >= 256 workgroups
-  const long long n_kb = (n_k + 127) / 128;
-  for (int g = 8; g >= 2; g /= 2)
-    if (bh * ((n_kb + g - 1) / g) >= 256) return g;
-  return 1;
-}
-
-// dQ partial slots (= backward workgroups) per (batch, head).
-__host__ __device__ inline long long bwd_num_slots(long long B, long long H, long long n_k) {
-  const int g = bwd_blocks_per_group(B, H, n_k);
-  return ((n_k + 127) / 128 + g - 1) / g;
-}
-
 // Arguments of the backward launches.  dq, dk, dv are bf16 outputs; the
-// workspace holds l2vec [R] (LSE * log2 e), dvec [R] (rowsum dO * O) and the
-// dQ partials ws_dq [n_slot][R][d], R = B*H*N_q, one per group of
-// bwd_blocks_per_group() 128-key blocks (n_slot = bwd_num_slots()).
+// workspace holds l2vec [R] (LSE * log2 e) and dvec [R] (rowsum dO * O),
+// R = B*H*N_q.
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -98,7 +77,6 @@ struct BwdParams {
   uint16_t* dv;
   float* l2vec;
   float* dvec;
-  float* ws_dq;
   int B, H, n_q, n_k, d;
   int causal;
   float scale;
@@ -150,7 +128,8 @@ hipError_t launch_fwd_blockmask(const FwdParams& p, hipStream_t stream);
 hipError_t launch_splitkv_partial(const FwdParams& p, hipStream_t stream);
 hipError_t launch_splitkv_merge(const FwdParams& p, hipStream_t stream);
 
-// Backward: D and LSE*log2e, then dK, dV and the dQ partials, then the dQ reduction.
+// Backward: D and LSE*log2e, then dK and dV (one pass over the key blocks), then dQ (one
+// pass over the query blocks).
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 
 // Dispatch-order probe: out[2i] = XCD id, out[2i + 1] = hardware id word of workgroup i.

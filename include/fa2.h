@@ -227,9 +227,7 @@ int fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float*
 
 /*
  * fa2_bwd_workspace_bytes — bytes of caller-owned device workspace fa2_bwd
- * needs: (2*R + S * R * d) * 4 with R = B*H*N_q, one fp32 dQ partial for each
- * of the S = ceil(ceil(N_k/128)/G) groups of G 128-key blocks.  G is the
- * largest of 8, 4 and 2 with B*H*S >= 256 (the number of workgroups), else 1.
+ * needs: 2 * B * H * N_q * 4 (LSE * log2(e) and D for every query row).
  * Returns 0 when an argument is out of range.
  */
 size_t fa2_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d);
@@ -250,11 +248,12 @@ size_t fa2_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d);
  * P is rounded to bf16 for dV, dS to bf16 for dK and dQ; products accumulate
  * in fp32; dQ, dK, dV are written as bf16 (RNE).
  *
- * Passes: (1) D and LSE*log2(e) per row; (2) one workgroup per group of G
- * 128-key blocks (G as in fa2_bwd_workspace_bytes) computes dK and dV for the
- * keys of each block in turn, and writes the group's summed contribution to dQ
- * for every query row into the workspace; (3) dQ = scale * the sum of the group
- * contributions in group order.  No atomics: results are bit-reproducible.
+ * Passes: (1) D and LSE*log2(e) per row; (2) one workgroup per 128-key block
+ * streams the query blocks and accumulates dK and dV for its keys; (3) one
+ * workgroup per 128-row query block streams the key blocks and accumulates dQ
+ * for its rows.  Both passes recompute S and dP (seven products in all); every
+ * gradient element is accumulated by one wave in a fixed order, with no
+ * partial sums in memory and no atomics: results are bit-reproducible.
  *
  * Q, K, V, O, dO: bf16 [B][H][N][d] as in fa2_fwd; LSE: fp32 [B][H][N_q]
  * (natural log, as fa2_fwd writes it).  dQ [B][H][N_q][d], dK and dV

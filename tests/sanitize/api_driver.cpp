@@ -195,11 +195,10 @@ static void test_bwd() {
        *W = dev(5);
   float* L = devf(4);
   const long long R = 1 * 2 * 256;
-  // two heads: too few workgroups to group key blocks, so one dQ partial per 128-key block
-  CHECK(fa2_bwd_workspace_bytes(1, 2, 256, 200, 64) == (size_t)(2 * R + 2 * R * 64) * 4);
-  CHECK(fa2_bwd_workspace_bytes(1, 2, 256, 300, 64) == (size_t)(2 * R + 3 * R * 64) * 4);
-  // 32 heads x 128 blocks: groups of 8 blocks, 16 partials (and no overflow at the limits)
-  CHECK(fa2_bwd_workspace_bytes(1, 32, 16384, 16384, 128) == (size_t)(2 + 16 * 128) * 32 * 16384 * 4);
+  // LSE*log2e and D per query row, whatever N_k and d (and no overflow at the limits)
+  CHECK(fa2_bwd_workspace_bytes(1, 2, 256, 200, 64) == (size_t)(2 * R) * 4);
+  CHECK(fa2_bwd_workspace_bytes(1, 2, 256, 300, 128) == (size_t)(2 * R) * 4);
+  CHECK(fa2_bwd_workspace_bytes(1, 32, 16384, 16384, 128) == (size_t)2 * 32 * 16384 * 4);
   CHECK(fa2_bwd_workspace_bytes(INT32_MAX, INT32_MAX, 1, INT32_MAX, 128) > 0);
   CHECK(fa2_bwd_workspace_bytes(0, 2, 256, 200, 64) == 0);
   const size_t need = fa2_bwd_workspace_bytes(1, 2, 256, 200, 64);
@@ -213,9 +212,9 @@ static void test_bwd() {
   const fa2::BwdParams& p = stub::rec.bwd;
   float* ws = static_cast<float*>(W);
   CHECK(p.dout == dO && p.dq == dQ && p.dk == dK && p.dv == dV && p.lse == L && p.causal == 1);
-  // LSE*log2e [R], D [R], then the dQ partials [n_slot][R][d], ending at the workspace size
-  CHECK(p.l2vec == ws && p.dvec == ws + R && p.ws_dq == ws + 2 * R);
-  CHECK((size_t)((char*)(p.ws_dq + 2 * R * 64) - (char*)ws) == need);
+  // LSE*log2e [R], then D [R], ending at the workspace size
+  CHECK(p.l2vec == ws && p.dvec == ws + R);
+  CHECK((size_t)((char*)(p.dvec + R) - (char*)ws) == need);
 }
 
 static void test_fp8() {

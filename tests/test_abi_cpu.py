@@ -208,20 +208,10 @@ def bwd(q=Q, k=K, v=V, o=O, do=DO, l=L, dq=DQ, dk=DK, dv=DV, B=1, H=2, nq=256, n
 def test_bwd_validation():
     lib = fa2.load_library()
     R = 1 * 2 * 256
-    # one dQ partial per group of G 128-key blocks, G the largest of 8, 4, 2 that leaves at least
-    # 256 workgroups (B*H*ceil(n_kb/G)), else 1.  Two heads: too few workgroups to group any blocks
-    assert lib.fa2_bwd_workspace_bytes(1, 2, 256, 200, 64) == (2 * R + 2 * R * 64) * 4
-    assert lib.fa2_bwd_workspace_bytes(1, 2, 256, 300, 64) == (2 * R + 3 * R * 64) * 4
-    # 64 heads x 32 blocks (B4 H16 N4096): G = 8, 4 slots; 32 heads x 128 blocks: G = 8, 16 slots
-    R3, R4 = 4 * 16 * 4096, 32 * 16384
-    assert lib.fa2_bwd_workspace_bytes(4, 16, 4096, 4096, 128) == (2 * R3 + 4 * R3 * 128) * 4
-    assert lib.fa2_bwd_workspace_bytes(1, 32, 16384, 16384, 128) == (2 * R4 + 16 * R4 * 128) * 4
-    # 8 heads x 32 blocks: 8 * 16 = 128 < 256 even with G = 2, so G = 1 (32 slots)
-    R5 = 8 * 4096
-    assert lib.fa2_bwd_workspace_bytes(1, 8, 4096, 4096, 64) == (2 * R5 + 32 * R5 * 64) * 4
-    # 128 heads x 16 blocks: G = 8 gives 256 workgroups, 2 slots
-    R6 = 128 * 2048
-    assert lib.fa2_bwd_workspace_bytes(8, 16, 2048, 2048, 64) == (2 * R6 + 2 * R6 * 64) * 4
+    # LSE * log2(e) and D for every query row: 2 * B * H * N_q floats, whatever N_k and d
+    for (B, H, nq, nk, d) in ((1, 2, 256, 200, 64), (1, 2, 256, 300, 128), (4, 16, 4096, 4096, 128),
+                              (1, 32, 16384, 16384, 128), (8, 16, 2048, 2048, 64)):
+        assert lib.fa2_bwd_workspace_bytes(B, H, nq, nk, d) == 2 * B * H * nq * 4
     assert lib.fa2_bwd_workspace_bytes(0, 2, 256, 200, 64) == 0
     for name in ("q", "k", "v", "o", "do", "l", "dq", "dk", "dv"):
         assert bwd(**{name: None}) == NULLPTR, name
@@ -229,7 +219,7 @@ def test_bwd_validation():
     assert bwd(nk=0) == BAD_SHAPE
     assert bwd(scale=float("inf")) == BAD_SCALE
     assert bwd(ws=None) == WORKSPACE
-    assert bwd(ws_bytes=16) == WORKSPACE
+    assert bwd(ws_bytes=2 * 2 * 256 * 4 - 4) == WORKSPACE
     assert bwd(dq=Q) == ALIAS
     assert bwd(dk=DO + 10) == ALIAS
     assert bwd(dv=DQ) == ALIAS
@@ -320,10 +310,10 @@ def test_work_item_limits():
     assert window(B=1 << 12, H=1 << 12, nq=128, nk=16, d=64) == BAD_SHAPE
     assert fwd8(B=1 << 12, H=1 << 12, nq=128, nk=16, d=64) == BAD_SHAPE
     assert dec8(B=1 << 12, H=1 << 12, nk=16, d=64) == BAD_SHAPE
-    # the backward: its per-row pass takes 16 work-items per row at d = 128, its dQ reduction one
-    # per 4 elements (32 per row); R = 2^18 * 513 rows fit the first but not the second
-    assert bwd(B=1 << 9, H=1 << 9, nq=513, nk=16, d=128) == BAD_SHAPE
+    # the backward: its per-row pass takes 16 work-items per row at d = 128 (the largest of its
+    # launches), so 2^30 rows are refused
     assert bwd(B=1 << 11, H=1 << 11, nq=256, nk=16, d=128) == BAD_SHAPE
+    assert bwd(B=1 << 10, H=1 << 10, nq=255, nk=16, d=128) != BAD_SHAPE  # 16 * 2^20 * 255 < 2^32
 
 
 def noalloc(q=Q, k=K, v=V, o=O, l=L, B=1, H=2, nq=1, nk=256, d=64, causal=0, scale=0.125, s=4):
