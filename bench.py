@@ -37,6 +37,7 @@ KERNEL_SRC = os.path.join(ROOT, "exact_attention_85_amd", "csrc", "fa2_fwd.hip")
 FP8_SRC = os.path.join(ROOT, "exact_attention_85_amd", "csrc", "fa2_fp8.hip")
 BWD_SRC = os.path.join(ROOT, "exact_attention_85_amd", "csrc", "fa2_bwd.hip")
 METRIC_FP8 = "attention fwd TFLOP/s (fp8 e4m3 inputs, per-head scaling) and % of MI355X fp8 MFMA peak"
+METRIC_BWD = "attention bwd TFLOP/s (bf16, FLOPs counted as 2.5x the forward's) and % of MI355X MFMA peak"
 
 
 def log(*a):
@@ -157,6 +158,9 @@ def main():
     ap.add_argument("--fp8", action="store_true",
                     help="time the FP8 forward on the same workload instead (inputs quantised per head "
                          "before the timed region)")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward (fa2_bwd) of the same workload instead, FLOPs counted as 2.5x the "
+                         "forward's (for its profile)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB read + 1 GiB write elementwise kernel (counter calibration)")
     args = ap.parse_args()
@@ -187,7 +191,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    if args.fp8:
+    if args.bwd:
+        args.fp8 = False
+        dout = workloads.make_tensor(w.index, 3, w.B, w.H, w.n_q, w.d, dev)
+        fa2.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse)
+        wsb = torch.empty(fa2.bwd_workspace_bytes(w.B, w.H, w.n_q, w.n_k, w.d) // 4, dtype=torch.float32, device=dev)
+        gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+        def step():
+            fa2.backward(q, k, v, o, lse, dout, causal=causal, scale=w.scale, workspace=wsb, dq=gq, dk=gk, dv=gv)
+    elif args.fp8:
         qc, dq = fa2.quantize_fp8(q)
         kc, dk = fa2.quantize_fp8(k)
         vt, dv = fa2.quantize_fp8(v, transposed=True)
@@ -214,13 +227,19 @@ def main():
     ms = events[0].elapsed_time(events[-1]) / args.steps
     per_launch = sorted(events[i].elapsed_time(events[i + 1]) for i in range(args.steps))
     ms_median, ms_min = per_launch[len(per_launch) // 2], per_launch[0]
-    flop = w.flop(causal)
+    flop = w.flop(causal) * (2.5 if args.bwd else 1.0)
     tflops = flop / (ms * 1e-3) / 1e12
     assert torch.isfinite(lse).all().item(), "non-finite LSE"
-    log(f"{w.name} non-causal{' fp8' if args.fp8 else ''}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s, wall {t_wall:.2f} s")
+    mode = " fp8" if args.fp8 else (" backward" if args.bwd else "")
+    log(f"{w.name} non-causal{mode}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s, wall {t_wall:.2f} s")
 
     peak = PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
-    if args.fp8:
+    if args.bwd:
+        kname, traffic = "bwd_kv_kernel<128> + bwd_dq_kernel<128>", measured_traffic(f"bwd:{w.name}:noncausal",
+                                                                                      (BWD_SRC,))
+        # read Q, O, dO (N_q x d) and K, V (N_k x d) in bf16 and LSE in fp32; write dQ, dK, dV in bf16
+        alg_bytes = w.B * w.H * (2 * (3 * w.n_q + 2 * w.n_k) * w.d + 4 * w.n_q + 2 * (w.n_q + 2 * w.n_k) * w.d)
+    elif args.fp8:
         kname, traffic = "fwd_fp8_kernel<128,4>", measured_traffic(f"fwd_fp8_kernel:{w.name}:noncausal", (FP8_SRC,))
         alg_bytes = w.B * w.H * (w.n_q * w.d + 2 * w.n_k * w.d + 2 * w.n_q * w.d + 4 * w.n_q)  # 1-byte Q, K, V codes
     else:
@@ -228,7 +247,7 @@ def main():
                                                                 (KERNEL_SRC, TUNE_TABLE))
         alg_bytes = w.io_bytes()
     result = {
-        "metric": METRIC_FP8 if args.fp8 else METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC_FP8 if args.fp8 else (METRIC_BWD if args.bwd else METRIC), "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "ms_per_step_median": round(ms_median, 4), "ms_per_step_min": round(ms_min, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3" if args.fp8 else "bf16", "data": "synthetic",
@@ -385,7 +404,7 @@ def main():
         del qd, kd, vd, od, ld, ws, qc8, kc8, vc8
         result["workloads"] = extra
 
-    if not args.no_cpu and not args.fp8:  # the oracle baseline is the bf16 definition
+    if not args.no_cpu and not args.fp8 and not args.bwd:  # the oracle baseline is the bf16 forward
         result["cpu_baseline"], result["parity"] = cpu_baseline(w, causal, q, k, v, o, lse)
         log(f"oracle: {result['cpu_baseline']}")
         log(f"parity of the timed run: {result['parity']}")
