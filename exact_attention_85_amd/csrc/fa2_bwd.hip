@@ -180,104 +180,131 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
 
   if (qb0 < n_qb) issue_q(0, qb0);
 
-  // one query block; STG is the LDS stage (compile-time so that offsets are immediates)
-  auto step = [&](auto stg_c, int qi) {
+  // One query block of 64 rows; STG is the LDS stage (compile-time so that offsets are
+  // immediates), MASKED whether any (row, key) pair of the wave's tile is masked.  The
+  // 32 products of S and dP and the 32 of dV and dK form four phases of 16:
+  //   A  S, dP of rows 0-31
+  //   B  S, dP of rows 32-63   with the softmax of rows 0-31 (P, dS) between them
+  //   C  dV, dK over rows 0-31 with the softmax of rows 32-63 between them
+  //   D  dV, dK over rows 32-63
+  // so that the vector work of each half runs while the matrix core works on the other.
+  // The program order below is the issue order: after the two products of each pair
+  // come the LDS reads of a later pair, then a share of the softmax, and the scheduling
+  // groups at the end of each pair hold the compiler to that order.
+  auto step = [&](auto stg_c, auto mask_c, int qi) {
     constexpr int STG = decltype(stg_c)::value;
+    constexpr bool MASKED = decltype(mask_c)::value;
     constexpr unsigned QOFF = STG * 2 * TILE, DOFF = QOFF + TILE;
+    constexpr int NAB = 2 * KT;        // product pairs of phases A and B (k-steps of 16 over d)
+    constexpr int NC = 2 * NB;         // product pairs of phase C (and of D): (t, nb)
+    constexpr int NPAIR = NAB + 2 * NC;
+    constexpr int PA = 2;              // row-operand reads issued this many pairs ahead
+    constexpr int PT = 3;              // transposed-operand reads (two LDS reads each)
+    constexpr int EB = 16 / KT;        // softmax elements per pair of phase B
+    constexpr int EC = 16 / NC;        // ... of phase C
+    constexpr int VPE = MASKED ? 8 : 5;  // vector instructions per softmax element, conversion included
     const int i0 = qi * kBQ;
-    // masking: causal diagonal, query rows past n_q, keys past n_k
-    const bool need_mask = (p.causal && i0 < kw0 + 31) || (i0 + kBQ > p.n_q) || (kw0 + 32 > p.n_k);
+    // element (8g + e) of half qh is tile row 32qh + 8g + 4hf + e; it is visible to this
+    // lane's key when lo <= 32qh + 8g + e < hi (causal: key <= row; rows past n_q and
+    // keys past n_k hidden)
+    const int lo = (p.causal ? key - i0 : 0) - 4 * hf;
+    const int hi = (key < p.n_k ? p.n_q - i0 : 0) - 4 * hf;
 
-    // S = Q K^T and dP = dO V^T for two 32-row halves
-    f32x16 s[2], dp[2];
-    {
-      // operands read PF steps ahead of their products (LDS latency exceeds two products)
-      constexpr int PF = 2;
-      constexpr int NST = 2 * KT;  // steps (qh, t)
-      bf16x8 ra[PF][2];
-#pragma unroll
-      for (int st = 0; st < PF; ++st) {
-        ra[st][0] = lds_load<bf16x8>(la.ka[st % KT] + QOFF + (st / KT) * 32 * ROW);
-        ra[st][1] = lds_load<bf16x8>(la.ka[st % KT] + DOFF + (st / KT) * 32 * ROW);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
-#pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const int qh = st / KT, t = st % KT;
-        if (t == 0) {
-          s[qh] = f32x16{};
-          dp[qh] = f32x16{};
-        }
-        s[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[st % PF][0], kf[t], s[qh], 0, 0, 0);
-        dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[st % PF][1], vf[t], dp[qh], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        if (st + PF < NST) {
-          const int s2 = st + PF;
-          ra[st % PF][0] = lds_load<bf16x8>(la.ka[s2 % KT] + QOFF + (s2 / KT) * 32 * ROW);
-          ra[st % PF][1] = lds_load<bf16x8>(la.ka[s2 % KT] + DOFF + (s2 / KT) * 32 * ROW);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-      }
-    }
-    // P = exp2(s * scale*log2e - LSE*log2e), dS = P (dP - D); row of register r:
-    // 32qh + 8(r/4) + 4hf + r%4
-    bf16x8 pb[2][2], db[2][2];
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-      f32x16 pv, dsv;
+    f32x4 l2v[2][4], ddv[2][4];  // LSE*log2e and D of this lane's 16 rows of each half
+    auto ld_rows = [&](int qh) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int rl = 32 * qh + 8 * g + 4 * hf;  // first of this lane's 4 rows in the tile
-        const f32x4 l2 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+        const int rl = 32 * qh + 8 * g + 4 * hf;
+        l2v[qh][g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
             (uintptr_t)(const lds_void*)&rowv[STG][0][rl]);
-        const f32x4 dd = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+        ddv[qh][g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
             (uintptr_t)(const lds_void*)&rowv[STG][1][rl]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qh][r], sl2, -l2[e]));
-          if (need_mask) {
-            const int row = i0 + rl + e;
-            const bool ok = row < p.n_q && key < p.n_k && (!p.causal || key <= row);
-            pr = ok ? pr : 0.f;
-          }
-          pv[r] = pr;
-          dsv[r] = pr * (dp[qh][r] - dd[e]);
-        }
       }
-      pb[qh][0] = cvt_bf16x8(slice8(pv, 0));
-      pb[qh][1] = cvt_bf16x8(slice8(pv, 1));
-      db[qh][0] = cvt_bf16x8(slice8(dsv, 0));
-      db[qh][1] = cvt_bf16x8(slice8(dsv, 1));
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS over the 64 rows (4 k-steps of 16), steps
-    // (qh, t, nb) in that order; the transposed operands are read PF steps ahead of
-    // their products (one LDS read outlasts the two products it feeds)
-    {
-      constexpr int NST = 4 * NB;
-      constexpr int PF = 3;
-      bf16x8 rdo[PF], rq[PF];
-      auto load = [&](int st) {
-        const int qh = st / (2 * NB), t = (st / NB) % 2, nb = st % NB;
+    };
+    bf16x8 ra[PA][2];       // rows of Q and dO (A operands of S and dP)
+    bf16x8 rdo[PT], rq[PT]; // dO^T and Q^T (A operands of dV^T and dK^T)
+    auto load = [&](int m) {
+      if (m < NAB) {
+        const unsigned roff = (m / KT) * 32 * ROW;
+        ra[m % PA][0] = lds_load<bf16x8>(la.ka[m % KT] + QOFF + roff);
+        ra[m % PA][1] = lds_load<bf16x8>(la.ka[m % KT] + DOFF + roff);
+      } else {
+        const int st = m - NAB, qh = st / NC, t = (st / NB) % 2, nb = st % NB;
         const unsigned roff = (32 * qh + 16 * t) * ROW;
-        rdo[st % PF] = tr_pair(la.va[2 * nb] + DOFF + roff, la.va[2 * nb + 1] + DOFF + roff);
-        rq[st % PF] = tr_pair(la.va[2 * nb] + QOFF + roff, la.va[2 * nb + 1] + QOFF + roff);
-      };
-#pragma unroll
-      for (int st = 0; st < PF; ++st) load(st);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4 * PF, 0);
-#pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const int qh = st / (2 * NB), t = (st / NB) % 2, nb = st % NB;
-        dvt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rdo[st % PF], pb[qh][t], dvt[nb], 0, 0, 0);
-        dkt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq[st % PF], db[qh][t], dkt[nb], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        if (st + PF < NST) {
-          load(st + PF);
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        }
+        rdo[st % PT] = tr_pair(la.va[2 * nb] + DOFF + roff, la.va[2 * nb + 1] + DOFF + roff);
+        rq[st % PT] = tr_pair(la.va[2 * nb] + QOFF + roff, la.va[2 * nb + 1] + QOFF + roff);
       }
+    };
+    f32x16 s[2], dp[2], pv[2], dsv[2];
+    bf16x8 pb[2][2], db[2][2];
+    auto softmax = [&](int qh, int r) {
+      const int g = r >> 2, e = r & 3;
+      float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qh][r], sl2, -l2v[qh][g][e]));
+      if (MASKED) {
+        const int c = 32 * qh + 8 * g + e;
+        pr = (c >= lo && c < hi) ? pr : 0.f;
+      }
+      pv[qh][r] = pr;
+      dsv[qh][r] = pr * (dp[qh][r] - ddv[qh][g][e]);
+      if (r % 8 == 7) {
+        pb[qh][r / 8] = cvt_bf16x8(slice8(pv[qh], r / 8));
+        db[qh][r / 8] = cvt_bf16x8(slice8(dsv[qh], r / 8));
+      }
+    };
+
+    ld_rows(0);
+#pragma unroll
+    for (int m = 0; m < PA; ++m) load(m);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 2 * PA, 0);
+#pragma unroll
+    for (int m = 0; m < NPAIR; ++m) {
+      if (m < NAB) {  // phases A and B: S = Q K^T, dP = dO V^T
+        const int qh = m / KT, t = m % KT;
+        s[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[m % PA][0], kf[t], t ? s[qh] : f32x16{}, 0, 0, 0);
+        dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[m % PA][1], vf[t], t ? dp[qh] : f32x16{}, 0, 0, 0);
+      } else {        // phases C and D: dV^T += dO^T P, dK^T += Q^T dS
+        const int st = m - NAB, qh = st / NC, t = (st / NB) % 2, nb = st % NB;
+        dvt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rdo[st % PT], pb[qh][t], dvt[nb], 0, 0, 0);
+        dkt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq[st % PT], db[qh][t], dkt[nb], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      // the finished half's S and dP move to VGPRs, where the softmax reads them, and
+      // free their accumulator registers for the next half's products
+      if (m == KT) asm volatile("" : "+v"(s[0]), "+v"(dp[0]));
+      if (m == NAB) asm volatile("" : "+v"(s[1]), "+v"(dp[1]));
+      if (m + PA < NAB) {
+        load(m + PA);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      if (m + PT >= NAB && m + PT < NPAIR) {
+        load(m + PT);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
+      if (m == NAB - 2) {
+        ld_rows(1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      }
+      if (m >= KT && m < NAB) {  // phase B: softmax of rows 0-31
+#pragma unroll
+        for (int e = 0; e < EB; ++e) softmax(0, (m - KT) * EB + e);
+        __builtin_amdgcn_sched_group_barrier(0x002, EB * VPE, 0);
+      } else if (m >= NAB && m < NAB + NC) {  // phase C: softmax of rows 32-63
+#pragma unroll
+        for (int e = 0; e < EC; ++e) softmax(1, (m - NAB) * EC + e);
+        __builtin_amdgcn_sched_group_barrier(0x002, EC * VPE, 0);
+      }
+      // each pair is a scheduling region of its own: the issue order above is kept
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  auto run_step = [&](auto stg_c, int qi) {
+    const int i0 = qi * kBQ;
+    // masking: causal diagonal, query rows past n_q, keys past n_k (uniform per wave)
+    const bool need_mask = (p.causal && i0 < kw0 + 31) || (i0 + kBQ > p.n_q) || (kw0 + 32 > p.n_k);
+    if (need_mask)
+      step(stg_c, std::true_type{}, qi);
+    else
+      step(stg_c, std::false_type{}, qi);
   };
 
   // two LDS stages, unrolled by two so that every offset is an immediate
@@ -292,12 +319,12 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();  // stage 0 published; stage 1 free
     if (qi + 1 < n_qb) issue_q(1, qi + 1);
-    step(std::integral_constant<int, 0>{}, qi);
+    run_step(std::integral_constant<int, 0>{}, qi);
     if (qi + 1 < n_qb) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
       if (qi + 2 < n_qb) issue_q(0, qi + 2);
-      step(std::integral_constant<int, 1>{}, qi + 1);
+      run_step(std::integral_constant<int, 1>{}, qi + 1);
     }
   }
 
