@@ -661,44 +661,70 @@ __global__ void __launch_bounds__(256) splitkv_merge_kernel(FwdParams p) {
 //   vector phase:  P_j from S_j (online softmax)
 // and every phase ends at a workgroup barrier.  Group 0 runs the matrix phase
 // of tile j in global phase 2j and the vector phase in 2j+1; group 1 one phase
-// later.  K_j and V_{j-1} are read in phases 2j and 2j+1; K_{j+1} and V_j
-// stream into the other buffers meanwhile (issued at the start of 2j, waited
-// for at the end of 2j+1).  The raw scores stay in registers through the
-// vector phase, so the exact redo of a tile never reads K again.
-template <int D, int NW>
-__device__ __forceinline__ void issue_one(i32x4 rs, const char* dst, int k0, int wave, int lane) {
-  constexpr int CPR = D / 8;
-  constexpr int NLD = kBC * CPR / (64 * NW);
-  const unsigned toff = (unsigned)k0 * D * 2;
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int s = (i * NW + wave) * 64 + lane;
-    const int r = s / CPR;
-    const int c = (s % CPR) ^ (swz<D>(r, 0) - r * CPR);
-    const unsigned off = (unsigned)((r * D + c * 8) * 2) + toff;
-    lds_dma16(rs, dst + (i * NW + wave) * 64 * 16, off);
-  }
-}
+// later.  K and V each have a three-stage LDS ring (tile j in stage j % 3):
+// the matrix phase of tile j issues the loads of K_{j+2} and V_{j+1} among its
+// products, and the wait at the end of iteration j+1 retires them, so every
+// load has one to two phases to arrive.  The raw scores stay in registers
+// through the vector phase, so the exact redo of a tile never reads K again.
 
-template <int D, unsigned VOFF>
-__device__ __forceinline__ void pv_tile(WaveRows<D>& w, const LdsAddr<D>& la, const bf16x8 (&pb)[4]) {
+// O += P_{j-1} V_{j-1} followed by S_j = K_j Q^T as one stream of products whose A
+// operands (V^T read transposed, then K rows) come from one ring of PF registers, each
+// read issued PF products ahead: the score products start without an LDS round trip
+// at the hand-over.  The scheduling groups hold the compiler to that issue order.
+template <int D, unsigned VOFF, unsigned KOFF, int PF, int NDMA, typename Dma>
+__device__ __forceinline__ void pv_qk_tile(WaveRows<D>& w, const LdsAddr<D>& la, const bf16x8 (&pb)[4], f32x16& s0,
+                                           f32x16& s1, Dma&& dma) {
   constexpr int NB = D / 32;
+  constexpr int KT = D / 16;
+  constexpr int NPV = 4 * NB;        // products of P.V: (kb, t, nb)
+  constexpr int NM = NPV + 2 * KT;   // then the score products: (t, block)
   constexpr unsigned ROW = D * 2;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
+  bf16x8 a[PF];
+  auto load = [&](int m) {
+    if (m < NPV) {
+      const int kb = m / (2 * NB), t = (m / NB) % 2, nb = m % NB;
       const unsigned roff = VOFF + (kb * 32 + 16 * t) * ROW;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<lds_i16x4*>((uintptr_t)(la.va[2 * nb] + roff)));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<lds_i16x4*>((uintptr_t)(la.va[2 * nb + 1] + roff)));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        w.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[2 * kb + t], w.acc[nb], 0, 0, 0);
-      }
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<lds_i16x4*>((uintptr_t)(la.va[2 * nb] + roff)));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<lds_i16x4*>((uintptr_t)(la.va[2 * nb + 1] + roff)));
+      a[m % PF] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      const int i = m - NPV;
+      a[m % PF] = lds_load<bf16x8>(la.ka[i / 2] + KOFF + (i % 2) * 32 * ROW);
     }
+  };
+#pragma unroll
+  for (int m = 0; m < PF; ++m) load(m);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+  s0 = f32x16{};
+  s1 = f32x16{};
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    if (m < NPV) {
+      const int kb = m / (2 * NB), t = (m / NB) % 2, nb = m % NB;
+      w.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % PF], pb[2 * kb + t], w.acc[nb], 0, 0, 0);
+    } else {
+      const int i = m - NPV, t = i / 2;
+      if (i % 2 == 0)
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % PF], w.qf[t], s0, 0, 0, 0);
+      else
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % PF], w.qf[t], s1, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (m + PF < NPV) {
+      load(m + PF);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    } else if (m + PF < NM) {
+      load(m + PF);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    // the next tiles' buffer->LDS loads, spread over the stream (issued together they
+    // queue in the address unit and stall the issuing wave)
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i)
+      if (m == i * NM / NDMA + 1) dma(i);
+  }
 }
 
 // exp2(s * sl2 - m) of one 8-register slice, converted to bf16; adds to the sums
@@ -757,9 +783,12 @@ __global__ void __launch_bounds__(512, 1) fwd_pp_kernel(FwdParams p, float sl2, 
   constexpr int KT = D / 16;
   constexpr int NB = D / 32;
   constexpr int TILE_BYTES = kBC * D * 2;
-  constexpr unsigned STAGE = 2 * TILE_BYTES;
+  constexpr int CPR = D / 8;
+  constexpr int NLD = kBC * CPR / (64 * NW);  // buffer->LDS loads per tile and wave
 
-  __shared__ __attribute__((aligned(1024))) char lds[2][2][TILE_BYTES];  // [stage][K=0 / V=1]
+  // three-stage rings: tile j of K (V) in stage j % 3, loaded two (one) iterations ahead
+  __shared__ __attribute__((aligned(1024))) char ldsk[3][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char ldsv[3][TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -811,11 +840,48 @@ __global__ void __launch_bounds__(512, 1) fwd_pp_kernel(FwdParams p, float sl2, 
   w.l_run = 0.f;
   w.l16 = 0.f;
 
-  LdsAddr<D> la;
-  make_lds_addr<D>(la, (unsigned)(uintptr_t)(const lds_void*)&lds[0][0][0], lane);
+  LdsAddr<D> la;  // K-row addresses over the K ring, transposed-V addresses over the V ring
+  {
+    LdsAddr<D> lv;
+    make_lds_addr<D>(la, (unsigned)(uintptr_t)(const lds_void*)&ldsk[0][0], lane);
+    make_lds_addr<D>(lv, (unsigned)(uintptr_t)(const lds_void*)&ldsv[0][0], lane);
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) la.va[i] = lv.va[i];
+  }
+  // this lane's byte offset within a tile for each of its NLD loads (swizzled slots)
+  unsigned offp[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int sl = (i * NW + wave) * 64 + lane;
+    const int r = sl / CPR;
+    const int c = (sl % CPR) ^ (swz<D>(r, 0) - r * CPR);
+    offp[i] = (unsigned)((r * D + c * 8) * 2);
+  }
+  // load part i (0 .. 2 NLD - 1) of iteration j's prefetch: K_{j+2} into stage (KS + 2) % 3,
+  // then V_{j+1} into stage (KS + 1) % 3.  Tiles past the last one read past the buffer
+  // range and fill their stage with zeros, which no phase reads.
+  auto dma = [&](int j, auto kst, int i) {
+    constexpr unsigned KS = decltype(kst)::value;
+    if (i < NLD)
+      lds_dma16(krs, &ldsk[(KS + 2) % 3][(i * NW + wave) * 64 * 16],
+                offp[i] + (unsigned)(kfirst + (j + 2) * kBC) * D * 2);
+    else
+      lds_dma16(vrs, &ldsv[(KS + 1) % 3][((i - NLD) * NW + wave) * 64 * 16],
+                offp[i - NLD] + (unsigned)(kfirst + (j + 1) * kBC) * D * 2);
+  };
 
   f32x16 s0 = {}, s1 = {};
-  bf16x8 pb[4];
+  bf16x8 pb[4] = {};
+  // the first matrix phase multiplies P = 0 with V stage 2, which no load has written
+  // yet: zero it (published by the barrier before the loop)
+  {
+    constexpr int PER = TILE_BYTES / (64 * NW);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < PER / 16; ++i)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+          (uintptr_t)(const lds_void*)&ldsv[2][(tid * (PER / 16) + i) * 16]) = z;
+  }
 
   auto act = [&](int j) {
     const int kk = kfirst + j * kBC;
@@ -825,57 +891,81 @@ __global__ void __launch_bounds__(512, 1) fwd_pp_kernel(FwdParams p, float sl2, 
     const int kk = kfirst + j * kBC;
     return (kk + kBC > p.n_k) || (wr >= 0 && kk + kBC - 1 > q0w + wr) || (wl >= 0 && kk < q0w + 31 - wl);
   };
-  // matrix phase of tile j: O += P_{j-1} V_{j-1}, then S_j = K_j Q^T.  KST: stage of K_j.
+  // matrix phase of tile j: O += P_{j-1} V_{j-1}, then S_j = K_j Q^T, with the loads of
+  // K_{j+2} and V_{j+1} issued among the products.  KST = j % 3: stage of K_j.
   auto mat = [&](int j, auto kst) {
     constexpr unsigned KS = decltype(kst)::value;
+    // one straight-line stream whenever either half is live: an inactive previous tile
+    // left P = 0 (and V finite), an inactive current tile's scores are never used
     __builtin_amdgcn_s_setprio(1);
-    if (act(j - 1)) pv_tile<D, (1 - KS) * STAGE + TILE_BYTES>(w, la, pb);
-    __builtin_amdgcn_sched_barrier(0);
-    if (act(j)) qk_tile_pf<D, KS * STAGE, 2>(w, la, s0, s1);
+    if (act(j - 1) || act(j)) {
+      pv_qk_tile<D, ((KS + 2) % 3) * TILE_BYTES, KS * TILE_BYTES, 4, 2 * NLD>(w, la, pb, s0, s1,
+                                                                             [&](int i) { dma(j, kst, i); });
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2 * NLD; ++i) dma(j, kst, i);
+    }
     __builtin_amdgcn_s_setprio(0);
   };
   auto vec = [&](int j) {
-    if (act(j)) softmax_pp(w, s0, s1, pb, need_mask(j), kfirst + j * kBC, row_lo, row_hi, sl2, lane);
+    if (act(j))
+      softmax_pp(w, s0, s1, pb, need_mask(j), kfirst + j * kBC, row_lo, row_hi, sl2, lane);
+    else
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[i] = bf16x8{};
   };
-  // tile iteration j: phases 2j and 2j+1.  KST = j % 2.  Group 0 runs (matrix j, vector j),
+  // The loads a wave issues in iteration j are waited for at the end of iteration j + 1:
+  // the wait leaves this iteration's 2 NLD loads in flight (each wave's loads complete in
+  // order).  Both groups issue in their matrix phase.
+  auto wait_prev = [&]() {
+    if constexpr (NLD == 2)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  };
+  // tile iteration j: phases 2j and 2j+1.  KST = j % 3.  Group 0 runs (matrix j, vector j),
   // group 1 (vector j-1, matrix j); each group has its own loop so that its phases are
   // straight-line code.  Both execute the same barriers.
-  auto issue = [&](int j, auto kst) {
-    constexpr unsigned KS = decltype(kst)::value;
-    if (j + 1 < n_tiles) issue_one<D, NW>(krs, lds[1 - KS][0], kfirst + (j + 1) * kBC, wave, lane);
-    if (j < n_tiles) issue_one<D, NW>(vrs, lds[KS][1], kfirst + j * kBC, wave, lane);
-  };
   auto iter0 = [&](int j, auto kst) {
-    issue(j, kst);
     mat(j, kst);
     __syncthreads();
     vec(j);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_prev();
     __syncthreads();
   };
   auto iter1 = [&](int j, auto kst) {
-    issue(j, kst);
     vec(j - 1);
     __syncthreads();
     mat(j, kst);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_prev();
     __syncthreads();
   };
 
-  if (n_tiles > 0) issue_one<D, NW>(krs, lds[0][0], kfirst, wave, lane);
+  // K_0, K_1 and V_0 before the loop
+  {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      lds_dma16(krs, &ldsk[0][(i * NW + wave) * 64 * 16], offp[i] + (unsigned)kfirst * D * 2);
+      lds_dma16(krs, &ldsk[1][(i * NW + wave) * 64 * 16], offp[i] + (unsigned)(kfirst + kBC) * D * 2);
+      lds_dma16(vrs, &ldsv[0][(i * NW + wave) * 64 * 16], offp[i] + (unsigned)kfirst * D * 2);
+    }
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (grp == 0) {
-    for (int j = 0; j <= n_tiles; j += 2) {
+    for (int j = 0; j <= n_tiles; j += 3) {
       iter0(j, std::integral_constant<unsigned, 0>{});
       if (j + 1 <= n_tiles) iter0(j + 1, std::integral_constant<unsigned, 1>{});
+      if (j + 2 <= n_tiles) iter0(j + 2, std::integral_constant<unsigned, 2>{});
     }
   } else {
-    for (int j = 0; j <= n_tiles; j += 2) {
+    for (int j = 0; j <= n_tiles; j += 3) {
       iter1(j, std::integral_constant<unsigned, 0>{});
       if (j + 1 <= n_tiles) iter1(j + 1, std::integral_constant<unsigned, 1>{});
+      if (j + 2 <= n_tiles) iter1(j + 2, std::integral_constant<unsigned, 2>{});
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const float l_tot = w.l_run + __shfl_xor(w.l_run, 32);
   const float l16_tot = w.l16 + __shfl_xor(w.l16, 32);
