@@ -85,19 +85,22 @@ __device__ __forceinline__ bf16x8 tr_pair(unsigned a0, unsigned a1) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Loads of one 64-row tile (Q or dO) into LDS with the swizzled slot layout.
+// Load i of one 64-row tile (Q or dO) into LDS with the swizzled slot layout.
+template <int D>
+__device__ __forceinline__ void issue_rows_part(i32x4 rs, const char* dst, int r0, int wave, int lane, int i) {
+  constexpr int CPR = D / 8;
+  const unsigned toff = (unsigned)r0 * D * 2;
+  const int s = (i * 4 + wave) * 64 + lane;
+  const int r = s / CPR;
+  const int c = (s % CPR) ^ (swz<D>(r, 0) - r * CPR);
+  lds_dma16(rs, dst + (i * 4 + wave) * 64 * 16, (unsigned)((r * D + c * 8) * 2) + toff);
+}
+
 template <int D>
 __device__ __forceinline__ void issue_rows(i32x4 rs, const char* dst, int r0, int wave, int lane) {
-  constexpr int CPR = D / 8;
-  constexpr int NLD = kBQ * CPR / 256;
-  const unsigned toff = (unsigned)r0 * D * 2;
+  constexpr int NLD = kBQ * (D / 8) / 256;
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int s = (i * 4 + wave) * 64 + lane;
-    const int r = s / CPR;
-    const int c = (s % CPR) ^ (swz<D>(r, 0) - r * CPR);
-    lds_dma16(rs, dst + (i * 4 + wave) * 64 * 16, (unsigned)((r * D + c * 8) * 2) + toff);
-  }
+  for (int i = 0; i < NLD; ++i) issue_rows_part<D>(rs, dst, r0, wave, lane, i);
 }
 
 template <int D>
@@ -161,16 +164,39 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
     dkt[nb] = f32x16{};
   }
 
-  auto issue_q = [&](int stage, int qi) {
+  auto issue_rowv = [&](int stage, int qi) {
     const int r0 = qi * kBQ;
-    issue_rows<D>(qrs, qdo[stage][0], r0, wave, lane);
-    issue_rows<D>(dors, qdo[stage][1], r0, wave, lane);
     // lanes 0-15 of wave 0 bring the 64 L2 values, lanes 16-31 the 64 D values
     // (lane l writes 16 bytes at the LDS base + 16 l)
     if (wave == 0 && lane < 16)
       lds_dma16(l2rs, reinterpret_cast<const char*>(&rowv[stage][0][0]), (unsigned)(r0 * 4 + lane * 16));
     else if (wave == 0 && lane < 32)
       lds_dma16(dvrs, reinterpret_cast<const char*>(&rowv[stage][1][0]) - 256, (unsigned)(r0 * 4 + (lane - 16) * 16));
+  };
+  auto issue_q = [&](int stage, int qi) {
+    issue_rows<D>(qrs, qdo[stage][0], qi * kBQ, wave, lane);
+    issue_rows<D>(dors, qdo[stage][1], qi * kBQ, wave, lane);
+    issue_rowv(stage, qi);
+  };
+  // the Q and dO loads of query block qi into `stage`, issued one at a time among a
+  // step's products (issued together they queue in the address unit and stall the
+  // wave); a block past the last one reads past the buffers' range and fills the
+  // stage with zeros, which no step reads
+  constexpr int NLDQ = kBQ * (D / 8) / 256;
+  unsigned offq[NLDQ];  // this lane's byte offset within a tile for each of its loads
+#pragma unroll
+  for (int i = 0; i < NLDQ; ++i) {
+    const int sl = (i * 4 + wave) * 64 + lane;
+    const int r = sl / (D / 8);
+    const int c = (sl % (D / 8)) ^ (swz<D>(r, 0) - r * (D / 8));
+    offq[i] = (unsigned)((r * D + c * 8) * 2);
+  }
+  auto dma_part = [&](int stage, int qi, int i) {
+    const unsigned toff = (unsigned)(qi * kBQ) * D * 2;
+    if (i < NLDQ)
+      lds_dma16(qrs, qdo[stage][0] + (i * 4 + wave) * 64 * 16, offq[i] + toff);
+    else
+      lds_dma16(dors, qdo[stage][1] + ((i - NLDQ) * 4 + wave) * 64 * 16, offq[i - NLDQ] + toff);
   };
 
   // the key/value fragments have arrived (waited for here once, not inside the query loop)
@@ -284,6 +310,11 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
         ld_rows(1);
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
       }
+      // the next block's Q and dO loads, one per two pairs of phases A and B
+      static_assert(4 * NLDQ <= NAB, "loads spread over phases A and B");
+#pragma unroll
+      for (int i = 0; i < 2 * NLDQ; ++i)
+        if (m == 2 * i + 1) dma_part(1 - STG, qi + 1, i);
       if (m >= KT && m < NAB) {  // phase B: softmax of rows 0-31
 #pragma unroll
         for (int e = 0; e < EB; ++e) softmax(0, (m - KT) * EB + e);
@@ -318,15 +349,16 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
     // knows that no earlier load is outstanding inside the step
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();  // stage 0 published; stage 1 free
-    if (qi + 1 < n_qb) issue_q(1, qi + 1);
-    run_step(std::integral_constant<int, 0>{}, qi);
+    if (qi + 1 < n_qb) issue_rowv(1, qi + 1);
+    run_step(std::integral_constant<int, 0>{}, qi);  // also loads Q, dO of block qi + 1
     if (qi + 1 < n_qb) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
-      if (qi + 2 < n_qb) issue_q(0, qi + 2);
+      if (qi + 2 < n_qb) issue_rowv(0, qi + 2);
       run_step(std::integral_constant<int, 1>{}, qi + 1);
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last step's loads land before the workgroup ends
 
   // dK = scale * dK, dV, rows d 32nb + 8g + 4hf + 0..3 of this lane's key
   if (key < p.n_k) {
@@ -378,9 +410,9 @@ __device__ __forceinline__ void issue_kv(i32x4 krs, i32x4 vrs, const char* kdst,
 
 // acc[0..1] = A B over the tile's two 32-key blocks: A rows from the LDS tile at OFF,
 // B = this wave's fragments bf (row operand), k-steps of 16; operands read two ahead
-template <int D, unsigned OFF>
+template <int D, unsigned OFF, typename Dma>
 __device__ __forceinline__ void rows_product(const LdsAddr<D>& la, const bf16x8 (&bf)[D / 16], f32x16& a0,
-                                             f32x16& a1) {
+                                             f32x16& a1, Dma&& dma) {
   constexpr unsigned ROW = D * 2;
   constexpr int KT = D / 16;
   constexpr int PF = 2;
@@ -403,6 +435,7 @@ __device__ __forceinline__ void rows_product(const LdsAddr<D>& la, const bf16x8 
       a[t % PF][1] = lds_load<bf16x8>(la.ka[t + PF] + OFF + 32 * ROW);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
+    dma(t);
   }
 }
 
@@ -462,13 +495,36 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p, float sl2, 
 
   LdsAddr<D> la;
   make_lds_addr<D>(la, (unsigned)(uintptr_t)(const lds_void*)&lds[0][0][0], lane);
+  constexpr int NLDK = kBC * (D / 8) / 256;  // loads per tile and wave, for K and again for V
+  static_assert(2 * NLDK == KT, "one load per score product pair");
+  unsigned offk[NLDK];  // this lane's byte offset within a tile for each of its loads
+#pragma unroll
+  for (int i = 0; i < NLDK; ++i) {
+    const int sl = (i * 4 + wave) * 64 + lane;
+    const int r = sl / (D / 8);
+    const int c = (sl % (D / 8)) ^ (swz<D>(r, 0) - r * (D / 8));
+    offk[i] = (unsigned)((r * D + c * 8) * 2);
+  }
 
   auto step = [&](auto stg_c, int k0) {
     constexpr unsigned KOFF = decltype(stg_c)::value * STAGE, VOFF = KOFF + TILE;
-    if (k0 >= khi_w) return;  // no row of this wave sees the tile
+    // the next tile's K and V loads into the other stage, one per score product pair (a
+    // tile past the last one reads past the buffers' range: zeros that no step reads)
+    auto dma = [&](int t) {
+      constexpr unsigned NS = KOFF ? 0 : 1;
+      if (t < NLDK)
+        lds_dma16(krs, lds[NS][0] + (t * 4 + wave) * 64 * 16, offk[t] + (unsigned)(k0 + kBC) * D * 2);
+      else
+        lds_dma16(vrs, lds[NS][1] + ((t - NLDK) * 4 + wave) * 64 * 16, offk[t - NLDK] + (unsigned)(k0 + kBC) * D * 2);
+    };
+    if (k0 >= khi_w) {  // no row of this wave sees the tile
+#pragma unroll
+      for (int t = 0; t < KT; ++t) dma(t);
+      return;
+    }
     f32x16 s0, s1, d0, d1;
-    rows_product<D, KOFF>(la, qf, s0, s1);
-    rows_product<D, VOFF>(la, dof, d0, d1);
+    rows_product<D, KOFF>(la, qf, s0, s1, dma);
+    rows_product<D, VOFF>(la, dof, d0, d1, [](int) {});
     // register r of block kb holds key k0 + 32kb + 8(r/4) + 4hf + r%4 of this lane's row
     const bool need_mask = (k0 + kBC > p.n_k) || (p.causal && k0 + kBC - 1 > q0w);
     const int hi = min(p.n_k - 1, p.causal ? row : p.n_k - 1) - k0 - 4 * hf;  // last visible offset
@@ -508,15 +564,16 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p, float sl2, 
     const int k0 = j * kBC;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (j + 1 < n_tiles) issue_kv<D>(krs, vrs, lds[1][0], lds[1][1], k0 + kBC, wave, lane);
+    // (the step loads tile j + 1 into stage 1)
     step(std::integral_constant<unsigned, 0>{}, k0);
     if (j + 1 < n_tiles) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (j + 2 < n_tiles) issue_kv<D>(krs, vrs, lds[0][0], lds[0][1], k0 + 2 * kBC, wave, lane);
+      // (the step loads tile j + 2 into stage 0)
       step(std::integral_constant<unsigned, 1>{}, k0 + kBC);
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last step's loads land before the workgroup ends
 
   // dQ = scale * dQ^T^T: register 4g + i of block nb is d column 32nb + 8g + 4hf + i of `row`
   if (row >= p.n_q) return;
