@@ -60,6 +60,30 @@ def test_every_config_against_oracle(shape):
             by_kernel[kernel] = (o, lse)
 
 
+# key lengths of one to four 64-key tiles (and one past): the first and last tiles of a
+# kernel's load ring, for query blocks of one and of several waves' rows
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_short_key_ranges_every_config(d, causal):
+    scale = 1.0 / math.sqrt(d)
+    for nk in (1, 63, 64, 65, 128, 129, 192, 193, 256, 257):
+        nq = nk if causal else 300
+        q, k, v = workloads.make_qkv_shape(1, 3, nq, nk, d, 5 * nk + d + int(causal), DEV)
+        o_ref, lse_ref = gu.oracle_full(q, k, v, causal, scale)
+        by_kernel = {}
+        for c in CONFIGS:
+            print(f"case config {fa2.config_name(c)} d={d} causal={causal} nq={nq} nk={nk}", flush=True)
+            o, lse = fa2.forward_config(q, k, v, c, -1, 0 if causal else -1, scale=scale)
+            torch.cuda.synchronize()
+            gu.assert_close(o.float().cpu().double().numpy(), lse.cpu().double().numpy(), o_ref, lse_ref,
+                            what=f"config {fa2.config_name(c)} nk={nk}", out_grid=True)
+            kernel = fa2.config_name(c).split("_")[0]
+            if kernel in by_kernel:
+                assert torch.equal(o, by_kernel[kernel][0]) and torch.equal(lse, by_kernel[kernel][1])
+            else:
+                by_kernel[kernel] = (o, lse)
+
+
 def test_named_workload_every_config():
     # the C3 shape (B4 H16 N4096 d128), causal: every configuration on all rows of two heads
     w = workloads.C3
