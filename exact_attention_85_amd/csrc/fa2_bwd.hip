@@ -21,7 +21,9 @@
 //   bwd_dq_kernel      one workgroup per 128-row query block (one wave per 32
 //                      rows): streams 64-key K/V tiles through LDS as the
 //                      forward does and runs three products (S, dP, then
-//                      dQ += dS K); dQ stays in registers
+//                      dQ += dS K); dQ stays in registers.  From 2048 query
+//                      rows at d = 128, bwd_dq_pp_kernel does the same work
+//                      with 8 waves in the ping-pong schedule of the forward
 // This is the deterministic form of the synthesis page's section 5 item 2
 // without any partial sums in memory: every gradient element is accumulated
 // by exactly one wave, in a fixed order, and written once, so the result is
@@ -590,7 +592,275 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p, float sl2, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// dQ pass, ping-pong form: one workgroup of 8 waves per (batch, head, 256-row query
+// block), waves w and w + 4 on one SIMD, group 0 (waves 0-3) one phase ahead of group 1,
+// as in the ping-pong forward.  Per tile j and wave:
+//   matrix phase:  dQ^T += K_{j-1}^T dS_{j-1}^T;  S_j^T = K_j Q^T;  dP_j^T = V_j dO^T
+//   vector phase:  P_j = exp2(s * scale*log2e - LSE*log2e) (0 where masked), dS_j = P_j (dP_j - D)
+// so that on each SIMD one wave issues 48 products while its partner runs the vector
+// work of the previous tile.  K and V each have a four-stage LDS ring (tile j in stage
+// j % 4): the matrix phase reads K_{j-1}, K_j and V_j and issues the loads of K_{j+2}
+// and V_{j+2} among its products; the wait at the end of iteration j + 1 retires them.
+template <int D, unsigned KPREV, unsigned KCUR, unsigned VCUR, int PF, int NDMA, typename Dma>
+__device__ __forceinline__ void dq_mat_stream(const LdsAddr<D>& la, unsigned vdelta, const bf16x8 (&qf)[D / 16],
+                                              const bf16x8 (&dof)[D / 16], const bf16x8 (&db)[4], f32x16 (&dq)[D / 32],
+                                              f32x16& s0, f32x16& s1, f32x16& d0, f32x16& d1, Dma&& dma) {
+  constexpr int NB = D / 32;
+  constexpr int KT = D / 16;
+  constexpr unsigned ROW = D * 2;
+  constexpr int NQ = 4 * NB;         // dQ products (kb, t, nb)
+  constexpr int NS = 2 * KT;         // score products (t, block), then as many for dP
+  constexpr int NM = NQ + 2 * NS;
+  bf16x8 a[PF];
+  auto load = [&](int m) {
+    if (m < NQ) {
+      const int kb = m / (2 * NB), t = (m / NB) % 2, nb = m % NB;
+      const unsigned roff = KPREV + (kb * 32 + 16 * t) * ROW;
+      a[m % PF] = tr_pair(la.va[2 * nb] + roff, la.va[2 * nb + 1] + roff);
+    } else if (m < NQ + NS) {
+      const int i = m - NQ;
+      a[m % PF] = lds_load<bf16x8>(la.ka[i / 2] + KCUR + (i % 2) * 32 * ROW);
+    } else {
+      const int i = m - NQ - NS;
+      a[m % PF] = lds_load<bf16x8>(la.ka[i / 2] + vdelta + VCUR + (i % 2) * 32 * ROW);
+    }
+  };
+#pragma unroll
+  for (int m = 0; m < PF; ++m) load(m);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+  s0 = f32x16{};
+  s1 = f32x16{};
+  d0 = f32x16{};
+  d1 = f32x16{};
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    if (m < NQ) {
+      const int kb = m / (2 * NB), t = (m / NB) % 2, nb = m % NB;
+      dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % PF], db[2 * kb + t], dq[nb], 0, 0, 0);
+    } else if (m < NQ + NS) {
+      const int i = m - NQ, t = i / 2;
+      if (i % 2 == 0)
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % PF], qf[t], s0, 0, 0, 0);
+      else
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % PF], qf[t], s1, 0, 0, 0);
+    } else {
+      const int i = m - NQ - NS, t = i / 2;
+      if (i % 2 == 0)
+        d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % PF], dof[t], d0, 0, 0, 0);
+      else
+        d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % PF], dof[t], d1, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (m + PF < NQ) {
+      load(m + PF);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    } else if (m + PF < NM) {
+      load(m + PF);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i)
+      if (m == i * NM / NDMA + 1) dma(i);
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(512, 1) bwd_dq_pp_kernel(BwdParams p, float sl2, int sched) {
+  constexpr int NW = 8;
+  constexpr int BR = 32 * NW;
+  constexpr int KT = D / 16;
+  constexpr int NB = D / 32;
+  constexpr int TILE = kBC * D * 2;
+  constexpr int CPR = D / 8;
+  constexpr int NLD = kBC * CPR / (64 * NW);  // loads per tile and wave, for K and again for V
+
+  __shared__ __attribute__((aligned(1024))) char ldsk[4][TILE];
+  __shared__ __attribute__((aligned(1024))) char ldsv[4][TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int hf = lane >> 5;
+  const int col = lane & 31;
+
+  const int n_qb = (p.n_q + BR - 1) / BR;
+  int bh, qb;
+  wg_coords(wg_logical(sched), n_qb, p.B * p.H, sched, p.causal != 0, bh, qb);
+  const int q0 = qb * BR;
+  const int q0w = q0 + 32 * wave;
+  const int row = q0w + col;
+  // keys seen by some row of the workgroup [0, khi), of this wave [0, khi_w)
+  const int khi = p.causal ? min(p.n_k, q0 + BR) : p.n_k;
+  const int khi_w = p.causal ? min(p.n_k, q0w + 32) : p.n_k;
+  const int n_tiles = (khi + kBC - 1) / kBC;
+
+  const long long hq = (long long)bh * p.n_q, hk = (long long)bh * p.n_k;
+  const i32x4 krs = raw_rsrc(p.k + hk * D, (long long)khi * D * 2);
+  const i32x4 vrs = raw_rsrc(p.v + hk * D, (long long)khi * D * 2);
+
+  bf16x8 qf[KT], dof[KT];
+  float l2 = 0.f, dd = 0.f;
+  {
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(p.q + hq * D, (long long)p.n_q * D * 2);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(p.dout + hq * D, (long long)p.n_q * D * 2);
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      const unsigned off = ((unsigned)row * D + 16 * t + 8 * hf) * 2u;
+      qf[t] = as_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0)));
+      dof[t] = as_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(drs, off, 0, 0)));
+    }
+    if (row < p.n_q) {
+      l2 = p.l2vec[hq + row];
+      dd = p.dvec[hq + row];
+    }
+  }
+  f32x16 dq[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) dq[nb] = f32x16{};
+
+  LdsAddr<D> la;  // K rows and K^T over the K ring; V rows at the same places of the V ring
+  make_lds_addr<D>(la, (unsigned)(uintptr_t)(const lds_void*)&ldsk[0][0], lane);
+  const unsigned vdelta = (unsigned)(uintptr_t)(const lds_void*)&ldsv[0][0] -
+                          (unsigned)(uintptr_t)(const lds_void*)&ldsk[0][0];
+  unsigned offp[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int sl = (i * NW + wave) * 64 + lane;
+    const int r = sl / CPR;
+    const int c = (sl % CPR) ^ (swz<D>(r, 0) - r * CPR);
+    offp[i] = (unsigned)((r * D + c * 8) * 2);
+  }
+  // part i of iteration j's loads: K_{j+2} then V_{j+2}, into stage (j + 2) % 4
+  auto dma = [&](int j, auto ks, int i) {
+    constexpr unsigned S2 = (decltype(ks)::value + 2) % 4;
+    const unsigned toff = (unsigned)((j + 2) * kBC) * D * 2;
+    if (i < NLD)
+      lds_dma16(krs, &ldsk[S2][(i * NW + wave) * 64 * 16], offp[i] + toff);
+    else
+      lds_dma16(vrs, &ldsv[S2][((i - NLD) * NW + wave) * 64 * 16], offp[i - NLD] + toff);
+  };
+
+  f32x16 s0 = {}, s1 = {}, d0 = {}, d1 = {};
+  bf16x8 db[4] = {};
+  // the first matrix phase multiplies dS = 0 with K stage 3, which no load has written
+  // yet: zero it (published by the barrier before the loop)
+  {
+    constexpr int PER = TILE / (64 * NW);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < PER / 16; ++i)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+          (uintptr_t)(const lds_void*)&ldsk[3][(tid * (PER / 16) + i) * 16]) = z;
+  }
+
+  auto act = [&](int j) { return j >= 0 && j < n_tiles && j * kBC < khi_w; };
+  auto mat = [&](int j, auto ks) {
+    constexpr unsigned KS = decltype(ks)::value;
+    __builtin_amdgcn_s_setprio(1);
+    if (act(j - 1) || act(j)) {
+      dq_mat_stream<D, ((KS + 3) % 4) * TILE, KS * TILE, KS * TILE, 4, 2 * NLD>(
+          la, vdelta, qf, dof, db, dq, s0, s1, d0, d1, [&](int i) { dma(j, ks, i); });
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2 * NLD; ++i) dma(j, ks, i);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto vec = [&](int j) {
+    if (!act(j)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) db[i] = bf16x8{};
+      return;
+    }
+    const int k0 = j * kBC;
+    // register r of block kb holds key k0 + 32kb + 8(r/4) + 4hf + r%4 of this lane's row
+    const bool need_mask = (k0 + kBC > p.n_k) || (p.causal && k0 + kBC - 1 > q0w);
+    const int hi = min(p.n_k - 1, p.causal ? row : p.n_k - 1) - k0 - 4 * hf;  // last visible offset
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const f32x16& s = kb ? s1 : s0;
+      f32x16& dp = kb ? d1 : d0;  // dS replaces dP in place
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2));
+        if (need_mask && 32 * kb + 8 * (r >> 2) + (r & 3) > hi) pr = 0.f;
+        dp[r] = pr * (dp[r] - dd);
+      }
+      db[2 * kb] = cvt_bf16x8(slice8(dp, 0));
+      db[2 * kb + 1] = cvt_bf16x8(slice8(dp, 1));
+    }
+  };
+  auto wait_prev = [&]() {
+    if constexpr (NLD == 2)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  };
+  auto iter0 = [&](int j, auto ks) {
+    mat(j, ks);
+    __syncthreads();
+    vec(j);
+    wait_prev();
+    __syncthreads();
+  };
+  auto iter1 = [&](int j, auto ks) {
+    vec(j - 1);
+    __syncthreads();
+    mat(j, ks);
+    wait_prev();
+    __syncthreads();
+  };
+
+  // K_0, K_1, V_0, V_1 before the loop
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int sl = (i * NW + wave) * 64 * 16;
+    lds_dma16(krs, &ldsk[0][sl], offp[i]);
+    lds_dma16(krs, &ldsk[1][sl], offp[i] + (unsigned)kBC * D * 2);
+    lds_dma16(vrs, &ldsv[0][sl], offp[i]);
+    lds_dma16(vrs, &ldsv[1][sl], offp[i] + (unsigned)kBC * D * 2);
+  }
+  // vmcnt(0) through the builtin, which the compiler's own wait tracking sees: the Q and
+  // dO fragments have then arrived, and it adds no waits of its own inside the loop
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  if (grp == 0) {
+    for (int j = 0; j <= n_tiles; j += 4) {
+      iter0(j, std::integral_constant<unsigned, 0>{});
+      if (j + 1 <= n_tiles) iter0(j + 1, std::integral_constant<unsigned, 1>{});
+      if (j + 2 <= n_tiles) iter0(j + 2, std::integral_constant<unsigned, 2>{});
+      if (j + 3 <= n_tiles) iter0(j + 3, std::integral_constant<unsigned, 3>{});
+    }
+  } else {
+    for (int j = 0; j <= n_tiles; j += 4) {
+      iter1(j, std::integral_constant<unsigned, 0>{});
+      if (j + 1 <= n_tiles) iter1(j + 1, std::integral_constant<unsigned, 1>{});
+      if (j + 2 <= n_tiles) iter1(j + 2, std::integral_constant<unsigned, 2>{});
+      if (j + 3 <= n_tiles) iter1(j + 3, std::integral_constant<unsigned, 3>{});
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last loads land before the workgroup ends
+
+  if (row >= p.n_q) return;
+  uint16_t* dqr = p.dq + (hq + row) * D;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      const f32x4 v = {dq[nb][4 * g] * p.scale, dq[nb][4 * g + 1] * p.scale, dq[nb][4 * g + 2] * p.scale,
+                       dq[nb][4 * g + 3] * p.scale};
+      *reinterpret_cast<u32x2*>(dqr + 32 * nb + 8 * g + 4 * hf) =
+          __builtin_bit_cast(u32x2, __builtin_convertvector(v, bf16x4));
+    }
+}
+
 }  // namespace
+
+// the dQ pass takes the ping-pong kernel from this many query rows
+constexpr int kDqPingPongMinRows = 2048;
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   const long long R = (long long)p.B * p.H * p.n_q;
@@ -601,14 +871,22 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   // dQ pass: the forward's workgroup orders (query-block-major without the renumbering under the
   // causal mask, the heaviest blocks of every head first; renumbered head-major otherwise)
   const int sched = p.causal ? kSchedQbMajor : kSchedRemap;
+  const unsigned g3 = (unsigned)((long long)p.B * p.H * ((p.n_q + 255) / 256));
+  const bool pp = p.d == 128 && p.n_q >= kDqPingPongMinRows;
   if (p.d == 128) {
     hipLaunchKernelGGL(bwd_prep_kernel<128>, dim3(g0), dim3(256), 0, stream, p);
     hipLaunchKernelGGL(bwd_kv_kernel<128>, dim3(g1), dim3(256), 0, stream, p, sl2);
-    hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(g2), dim3(256), 0, stream, p, sl2, sched);
+    if (pp)
+      hipLaunchKernelGGL(bwd_dq_pp_kernel<128>, dim3(g3), dim3(512), 0, stream, p, sl2, sched);
+    else
+      hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(g2), dim3(256), 0, stream, p, sl2, sched);
   } else {
     hipLaunchKernelGGL(bwd_prep_kernel<64>, dim3(g0), dim3(256), 0, stream, p);
     hipLaunchKernelGGL(bwd_kv_kernel<64>, dim3(g1), dim3(256), 0, stream, p, sl2);
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(g2), dim3(256), 0, stream, p, sl2, sched);
+    if (pp)
+      hipLaunchKernelGGL(bwd_dq_pp_kernel<64>, dim3(g3), dim3(512), 0, stream, p, sl2, sched);
+    else
+      hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(g2), dim3(256), 0, stream, p, sl2, sched);
   }
   return hipGetLastError();
 }

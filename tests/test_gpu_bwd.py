@@ -64,6 +64,19 @@ def test_bwd_many_heads(B, H, nq, nk, d, causal):
                  f"many heads nq={nq} nk={nk} d={d} causal={causal}")
 
 
+# From 2048 query rows at d = 128 the dQ pass takes the 8-wave ping-pong kernel: ragged row
+# and key counts around its 256-row blocks and 64-key tiles, both masks
+@pytest.mark.parametrize("nq,nk,causal", [(2053, 2053, True), (2053, 2053, False), (2100, 1, False),
+                                          (2048, 100, True), (2300, 333, False), (2049, 4100, True)])
+def test_bwd_pingpong_dq(nq, nk, causal):
+    print(f"case bwd ping-pong dQ nq={nq} nk={nk} causal={causal}", flush=True)
+    d, scale = 128, 1.0 / math.sqrt(128)
+    q, k, v = workloads.make_qkv_shape(1, 2, nq, nk, d, 5 * nq + nk + int(causal), DEV)
+    do = workloads.make_qkv_shape(1, 2, nq, 1, d, 55 + nq, DEV)[0]
+    o, dq, dk, dv = _run(q, k, v, do, causal, scale)
+    _check_heads(q, k, v, do, o, dq, dk, dv, causal, scale, [(0, 0), (0, 1)], f"pp nq={nq} nk={nk} causal={causal}")
+
+
 def test_bwd_deterministic_and_stream():
     q, k, v = workloads.make_qkv_shape(2, 3, 700, 900, 128, 21, DEV)
     do = workloads.make_qkv_shape(2, 3, 700, 1, 128, 22, DEV)[0]

@@ -78,10 +78,11 @@ def test_splitkv_partials():
     same(a, b, "split-KV")
 
 
-# B*H = 2: one key block per workgroup; B*H = 256: groups of key blocks per workgroup, which
-# refill the same LDS buffers block after block
+# B*H = 2: few workgroups; B*H = 256: many workgroups per compute unit in turn, which refill
+# the same LDS buffers; from 2048 rows at d = 128 the dQ pass is the ping-pong kernel
 @pytest.mark.parametrize("B,H,nq,d,causal", [(1, 2, 700, 128, 0), (1, 2, 700, 128, 1), (1, 2, 450, 64, 0),
-                                             (16, 16, 600, 128, 1), (16, 16, 1000, 64, 0)])
+                                             (16, 16, 600, 128, 1), (16, 16, 1000, 64, 0), (2, 2, 2100, 128, 0),
+                                             (2, 2, 2100, 128, 1)])
 def test_backward(B, H, nq, d, causal):
     print(f"race check fa2_bwd B{B} H{H} N{nq} d{d} causal={causal}", flush=True)
     q, k, v = workloads.make_qkv_shape(B, H, nq, nq, d, 74, DEV)
