@@ -302,11 +302,13 @@ int fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const vo
   int rc = check_common(Q, K, V, O, LSE, B, H, N_q, N_k, d, scale);
   if (rc != FA2_OK) return rc;
   // the three launches: D and LSE*log2e (256 work-items per 256/(d/8) rows), the key blocks
-  // (one workgroup of 256 per 128 keys), the query blocks (one workgroup of 256 per 128 rows)
+  // (one workgroup of 256 per 128 keys), the query blocks (one workgroup of 256 per 128 rows,
+  // or of 512 per 256 rows in the ping-pong form)
   const long long R_all = (long long)B * H * N_q;
   if (!launch_fits((R_all + 256 / (d / 8) - 1) / (256 / (d / 8)), 256) ||
       !launch_fits((long long)((N_k + 127) / 128) * B * H, 256) ||
-      !launch_fits((long long)((N_q + 127) / 128) * B * H, 256))
+      !launch_fits((long long)((N_q + 127) / 128) * B * H, 256) ||
+      !launch_fits((long long)((N_q + 255) / 256) * B * H, 512))
     return FA2_ERR_BAD_SHAPE;
   const size_t need = fa2_bwd_workspace_bytes(B, H, N_q, N_k, d);
   if (!workspace || workspace_bytes < need) return FA2_ERR_WORKSPACE;
