@@ -14,10 +14,12 @@
 //
 // Three launches:
 //   bwd_prep_kernel    D_i and LSE_i * log2(e) for every query row
-//   bwd_kv_kernel      one workgroup per 128-key block (one wave per 32 keys):
-//                      streams 64-row query blocks through LDS and runs four
-//                      products on the matrix cores (S, dP, then dV and dK);
-//                      dK and dV stay in registers until the block is done
+//   bwd_kv8_kernel     one workgroup of 8 waves per 128-key block: two waves per
+//                      32 keys, each over half of every 64-row query block
+//                      streamed through LDS; four products on the matrix cores
+//                      (S, dP, then dV and dK); K and V of the block stay in
+//                      LDS, dK and dV in registers, and the two halves' sums
+//                      are added at the end
 //   bwd_dq_kernel      one workgroup per 128-row query block (one wave per 32
 //                      rows): streams 64-key K/V tiles through LDS as the
 //                      forward does and runs three products (S, dP, then
@@ -87,44 +89,37 @@ __device__ __forceinline__ bf16x8 tr_pair(unsigned a0, unsigned a1) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Load i of one 64-row tile (Q or dO) into LDS with the swizzled slot layout.
+// ---------------------------------------------------------------------------
+// Key pass with two waves per SIMD: one workgroup of 8 waves per (batch, head, 128-key
+// block).  Wave w owns keys 32 (w % 4) .. + 31 of the block and rows 32 (w / 4) .. + 31 of
+// every 64-row query block, so the two waves of a SIMD share their keys and split the
+// rows; each accumulates its own dV^T, dK^T (128 registers) and the pair is summed
+// through LDS at the end.  K and V of the block stay in LDS for the whole pass and serve
+// as the B operands of S and dP (instead of 64 registers per wave), which is what lets
+// two waves fit in a SIMD.  Per query block and wave: S, dP (16 products), P and dS in
+// the vector unit, dV^T and dK^T (16 products).
 template <int D>
-__device__ __forceinline__ void issue_rows_part(i32x4 rs, const char* dst, int r0, int wave, int lane, int i) {
-  constexpr int CPR = D / 8;
-  const unsigned toff = (unsigned)r0 * D * 2;
-  const int s = (i * 4 + wave) * 64 + lane;
-  const int r = s / CPR;
-  const int c = (s % CPR) ^ (swz<D>(r, 0) - r * CPR);
-  lds_dma16(rs, dst + (i * 4 + wave) * 64 * 16, (unsigned)((r * D + c * 8) * 2) + toff);
-}
-
-template <int D>
-__device__ __forceinline__ void issue_rows(i32x4 rs, const char* dst, int r0, int wave, int lane) {
-  constexpr int NLD = kBQ * (D / 8) / 256;
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) issue_rows_part<D>(rs, dst, r0, wave, lane, i);
-}
-
-template <int D>
-__global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) {
+__global__ void __launch_bounds__(512, 1) bwd_kv8_kernel(BwdParams p, float sl2) {
+  constexpr int NW = 8;
   constexpr int NB = D / 32;
   constexpr int KT = D / 16;
-  constexpr int ROW = D * 2;                    // bytes per tile row
-  constexpr int TILE = kBQ * D * 2;             // one 64-row Q or dO tile
+  constexpr int ROW = D * 2;         // bytes per row
+  constexpr int TILE = kBQ * D * 2;  // one 64-row Q or dO tile
+  constexpr int BLK = kBK * D * 2;   // the 128-key K or V block
+  constexpr int CPR = D / 8;
 
-  // [stage][Q=0 / dO=1] row tiles, then the row vectors
-  __shared__ __attribute__((aligned(1024))) char qdo[2][2][TILE];
-  __shared__ __attribute__((aligned(16))) float rowv[2][2][kBQ];  // [stage][L2=0 / D=1][row]
+  __shared__ __attribute__((aligned(1024))) char kvb[2][BLK];       // K = 0, V = 1
+  __shared__ __attribute__((aligned(1024))) char qdo[2][2][TILE];   // [stage][Q = 0 / dO = 1]
+  __shared__ __attribute__((aligned(16))) float rowv[2][2][kBQ];     // [stage][L2 = 0 / D = 1][row]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ks = wave & 3;   // key slice
+  const int rh = wave >> 2;  // row half
   const int hf = lane >> 5;
   const int col = lane & 31;
 
-  // One workgroup per (batch, head, 128-key block), key blocks of a head consecutive.  Under
-  // the causal mask the first key blocks see the most query rows, so the natural order
-  // dispatches the heaviest blocks first.
   const int n_kb = (p.n_k + kBK - 1) / kBK;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = L / n_kb;
@@ -136,249 +131,205 @@ __global__ void __launch_bounds__(256, 1) bwd_kv_kernel(BwdParams p, float sl2) 
   const i32x4 dors = raw_rsrc(p.dout + hq * D, (long long)p.n_q * D * 2);
   const i32x4 l2rs = raw_rsrc(p.l2vec + hq, (long long)p.n_q * 4);
   const i32x4 dvrs = raw_rsrc(p.dvec + hq, (long long)p.n_q * 4);
+  const i32x4 krs = raw_rsrc(p.k + hk * D, (long long)p.n_k * D * 2);
+  const i32x4 vrs = raw_rsrc(p.v + hk * D, (long long)p.n_k * D * 2);
 
-  LdsAddr<D> la;  // over qdo: ka = A operand of S / dP (rows x d), va = A operand of dV^T / dK^T
-  make_lds_addr<D>(la, (unsigned)(uintptr_t)(const lds_void*)&qdo[0][0][0], lane);
+  // la over qdo from this wave's first row (rows and transposed reads of Q, dO); lk over
+  // the K block from this wave's first key (the V block follows at +BLK)
+  LdsAddr<D> la, lk;
+  make_lds_addr<D>(la, (unsigned)(uintptr_t)(const lds_void*)&qdo[0][0][0] + (unsigned)(32 * rh) * ROW, lane);
+  make_lds_addr<D>(lk, (unsigned)(uintptr_t)(const lds_void*)&kvb[0][0] + (unsigned)(32 * ks) * ROW, lane);
 
   const int k0 = kb * kBK;
-  const int kw0 = k0 + 32 * wave;     // this wave's keys kw0 .. kw0 + 31
-  const int key = kw0 + col;          // this lane's key column
-  // causal: rows below the block's first key see none of its keys
+  const int kw0 = k0 + 32 * ks;  // this wave's keys kw0 .. kw0 + 31
+  const int key = kw0 + col;     // this lane's key column
   const int qb0 = p.causal ? min(k0 / kBQ, n_qb) : 0;
 
-  // this wave's keys and values as B operands (lane = key, k = d): zero past n_k
-  bf16x8 kf[KT], vf[KT];
-  {
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + hk * D, (long long)p.n_k * D * 2);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + hk * D, (long long)p.n_k * D * 2);
+  // slot offsets of this lane's loads: a 64-row tile takes NLDQ loads per wave, a 128-row
+  // block NLDB (the swizzle repeats every 16 rows, so block rows use the tile's pattern)
+  constexpr int NLDQ = kBQ * CPR / (64 * NW);
+  constexpr int NLDB = kBK * CPR / (64 * NW);
+  unsigned offb[NLDB];
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      const unsigned off = ((unsigned)key * D + 16 * t + 8 * hf) * 2u;
-      kf[t] = as_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0)));
-      vf[t] = as_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0)));
+  for (int i = 0; i < NLDB; ++i) {
+    const int sl = (i * NW + wave) * 64 + lane;
+    const int r = sl / CPR;
+    const int c = (sl % CPR) ^ (swz<D>(r, 0) - r * CPR);
+    offb[i] = (unsigned)((r * D + c * 8) * 2);
+  }
+  // K and V of the block (zero past n_k)
+#pragma unroll
+  for (int i = 0; i < NLDB; ++i) {
+    lds_dma16(krs, &kvb[0][(i * NW + wave) * 64 * 16], offb[i] + (unsigned)k0 * D * 2);
+    lds_dma16(vrs, &kvb[1][(i * NW + wave) * 64 * 16], offb[i] + (unsigned)k0 * D * 2);
+  }
+  auto issue_q = [&](int stage, int qi) {
+    const unsigned toff = (unsigned)(qi * kBQ) * D * 2;
+#pragma unroll
+    for (int i = 0; i < NLDQ; ++i) {  // the first NLDQ slot offsets of the block are the tile's
+      lds_dma16(qrs, &qdo[stage][0][(i * NW + wave) * 64 * 16], offb[i] + toff);
+      lds_dma16(dors, &qdo[stage][1][(i * NW + wave) * 64 * 16], offb[i] + toff);
     }
-  }
-
-  f32x16 dvt[NB], dkt[NB];  // dV^T, dK^T: rows d, columns this wave's keys
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    dvt[nb] = f32x16{};
-    dkt[nb] = f32x16{};
-  }
-
-  auto issue_rowv = [&](int stage, int qi) {
-    const int r0 = qi * kBQ;
     // lanes 0-15 of wave 0 bring the 64 L2 values, lanes 16-31 the 64 D values
-    // (lane l writes 16 bytes at the LDS base + 16 l)
+    const int r0 = qi * kBQ;
     if (wave == 0 && lane < 16)
       lds_dma16(l2rs, reinterpret_cast<const char*>(&rowv[stage][0][0]), (unsigned)(r0 * 4 + lane * 16));
     else if (wave == 0 && lane < 32)
       lds_dma16(dvrs, reinterpret_cast<const char*>(&rowv[stage][1][0]) - 256, (unsigned)(r0 * 4 + (lane - 16) * 16));
   };
-  auto issue_q = [&](int stage, int qi) {
-    issue_rows<D>(qrs, qdo[stage][0], qi * kBQ, wave, lane);
-    issue_rows<D>(dors, qdo[stage][1], qi * kBQ, wave, lane);
-    issue_rowv(stage, qi);
-  };
-  // the Q and dO loads of query block qi into `stage`, issued one at a time among a
-  // step's products (issued together they queue in the address unit and stall the
-  // wave); a block past the last one reads past the buffers' range and fills the
-  // stage with zeros, which no step reads
-  constexpr int NLDQ = kBQ * (D / 8) / 256;
-  unsigned offq[NLDQ];  // this lane's byte offset within a tile for each of its loads
+
+  f32x16 dvt[NB], dkt[NB];  // dV^T, dK^T over this wave's rows: rows d, columns its keys
 #pragma unroll
-  for (int i = 0; i < NLDQ; ++i) {
-    const int sl = (i * 4 + wave) * 64 + lane;
-    const int r = sl / (D / 8);
-    const int c = (sl % (D / 8)) ^ (swz<D>(r, 0) - r * (D / 8));
-    offq[i] = (unsigned)((r * D + c * 8) * 2);
+  for (int nb = 0; nb < NB; ++nb) {
+    dvt[nb] = f32x16{};
+    dkt[nb] = f32x16{};
   }
-  auto dma_part = [&](int stage, int qi, int i) {
-    const unsigned toff = (unsigned)(qi * kBQ) * D * 2;
-    if (i < NLDQ)
-      lds_dma16(qrs, qdo[stage][0] + (i * 4 + wave) * 64 * 16, offq[i] + toff);
-    else
-      lds_dma16(dors, qdo[stage][1] + ((i - NLDQ) * 4 + wave) * 64 * 16, offq[i - NLDQ] + toff);
-  };
-
-  // the key/value fragments have arrived (waited for here once, not inside the query loop)
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-  for (int t = 0; t < KT; ++t) asm volatile("" ::"v"(kf[t]), "v"(vf[t]));
-
   if (qb0 < n_qb) issue_q(0, qb0);
 
-  // One query block of 64 rows; STG is the LDS stage (compile-time so that offsets are
-  // immediates), MASKED whether any (row, key) pair of the wave's tile is masked.  The
-  // 32 products of S and dP and the 32 of dV and dK form four phases of 16:
-  //   A  S, dP of rows 0-31
-  //   B  S, dP of rows 32-63   with the softmax of rows 0-31 (P, dS) between them
-  //   C  dV, dK over rows 0-31 with the softmax of rows 32-63 between them
-  //   D  dV, dK over rows 32-63
-  // so that the vector work of each half runs while the matrix core works on the other.
-  // The program order below is the issue order: after the two products of each pair
-  // come the LDS reads of a later pair, then a share of the softmax, and the scheduling
-  // groups at the end of each pair hold the compiler to that order.
-  auto step = [&](auto stg_c, auto mask_c, int qi) {
+  // one query block: this wave's 32 rows against its 32 keys
+  auto step = [&](auto stg_c, int qi) {
     constexpr int STG = decltype(stg_c)::value;
-    constexpr bool MASKED = decltype(mask_c)::value;
     constexpr unsigned QOFF = STG * 2 * TILE, DOFF = QOFF + TILE;
-    constexpr int NAB = 2 * KT;        // product pairs of phases A and B (k-steps of 16 over d)
-    constexpr int NC = 2 * NB;         // product pairs of phase C (and of D): (t, nb)
-    constexpr int NPAIR = NAB + 2 * NC;
-    constexpr int PA = 2;              // row-operand reads issued this many pairs ahead
-    constexpr int PT = 3;              // transposed-operand reads (two LDS reads each)
-    constexpr int EB = 16 / KT;        // softmax elements per pair of phase B
-    constexpr int EC = 16 / NC;        // ... of phase C
-    constexpr int VPE = MASKED ? 8 : 5;  // vector instructions per softmax element, conversion included
-    const int i0 = qi * kBQ;
-    // element (8g + e) of half qh is tile row 32qh + 8g + 4hf + e; it is visible to this
-    // lane's key when lo <= 32qh + 8g + e < hi (causal: key <= row; rows past n_q and
-    // keys past n_k hidden)
+    constexpr int PF = D == 128 ? 1 : 2;  // operand k-steps read ahead of their products
+    const int i0 = qi * kBQ + 32 * rh;  // first row
+    // element (8g + e) is row i0 + 8g + 4hf + e: visible to this lane's key when
+    // lo <= 8g + e < hi
     const int lo = (p.causal ? key - i0 : 0) - 4 * hf;
     const int hi = (key < p.n_k ? p.n_q - i0 : 0) - 4 * hf;
 
-    f32x4 l2v[2][4], ddv[2][4];  // LSE*log2e and D of this lane's 16 rows of each half
-    auto ld_rows = [&](int qh) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int rl = 32 * qh + 8 * g + 4 * hf;
-        l2v[qh][g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-            (uintptr_t)(const lds_void*)&rowv[STG][0][rl]);
-        ddv[qh][g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-            (uintptr_t)(const lds_void*)&rowv[STG][1][rl]);
-      }
+    // S = Q K^T and dP = dO V^T (keys on the lanes), operands read PF k-steps ahead
+    f32x16 s, dp;
+    bf16x8 ra[PF][4];
+    auto ld = [&](int t) {
+      ra[t % PF][0] = lds_load<bf16x8>(la.ka[t] + QOFF);
+      ra[t % PF][1] = lds_load<bf16x8>(lk.ka[t]);
+      ra[t % PF][2] = lds_load<bf16x8>(la.ka[t] + DOFF);
+      ra[t % PF][3] = lds_load<bf16x8>(lk.ka[t] + BLK);
     };
-    bf16x8 ra[PA][2];       // rows of Q and dO (A operands of S and dP)
-    bf16x8 rdo[PT], rq[PT]; // dO^T and Q^T (A operands of dV^T and dK^T)
-    auto load = [&](int m) {
-      if (m < NAB) {
-        const unsigned roff = (m / KT) * 32 * ROW;
-        ra[m % PA][0] = lds_load<bf16x8>(la.ka[m % KT] + QOFF + roff);
-        ra[m % PA][1] = lds_load<bf16x8>(la.ka[m % KT] + DOFF + roff);
-      } else {
-        const int st = m - NAB, qh = st / NC, t = (st / NB) % 2, nb = st % NB;
-        const unsigned roff = (32 * qh + 16 * t) * ROW;
-        rdo[st % PT] = tr_pair(la.va[2 * nb] + DOFF + roff, la.va[2 * nb + 1] + DOFF + roff);
-        rq[st % PT] = tr_pair(la.va[2 * nb] + QOFF + roff, la.va[2 * nb + 1] + QOFF + roff);
-      }
-    };
-    f32x16 s[2], dp[2], pv[2], dsv[2];
-    bf16x8 pb[2][2], db[2][2];
-    auto softmax = [&](int qh, int r) {
-      const int g = r >> 2, e = r & 3;
-      float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qh][r], sl2, -l2v[qh][g][e]));
-      if (MASKED) {
-        const int c = 32 * qh + 8 * g + e;
-        pr = (c >= lo && c < hi) ? pr : 0.f;
-      }
-      pv[qh][r] = pr;
-      dsv[qh][r] = pr * (dp[qh][r] - ddv[qh][g][e]);
-      if (r % 8 == 7) {
-        pb[qh][r / 8] = cvt_bf16x8(slice8(pv[qh], r / 8));
-        db[qh][r / 8] = cvt_bf16x8(slice8(dsv[qh], r / 8));
-      }
-    };
-
-    ld_rows(0);
 #pragma unroll
-    for (int m = 0; m < PA; ++m) load(m);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 2 * PA, 0);
+    for (int t = 0; t < PF; ++t) ld(t);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * PF, 0);
 #pragma unroll
-    for (int m = 0; m < NPAIR; ++m) {
-      if (m < NAB) {  // phases A and B: S = Q K^T, dP = dO V^T
-        const int qh = m / KT, t = m % KT;
-        s[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[m % PA][0], kf[t], t ? s[qh] : f32x16{}, 0, 0, 0);
-        dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[m % PA][1], vf[t], t ? dp[qh] : f32x16{}, 0, 0, 0);
-      } else {        // phases C and D: dV^T += dO^T P, dK^T += Q^T dS
-        const int st = m - NAB, qh = st / NC, t = (st / NB) % 2, nb = st % NB;
-        dvt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rdo[st % PT], pb[qh][t], dvt[nb], 0, 0, 0);
-        dkt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq[st % PT], db[qh][t], dkt[nb], 0, 0, 0);
-      }
+    for (int t = 0; t < KT; ++t) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[t % PF][0], ra[t % PF][1], t ? s : f32x16{}, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[t % PF][2], ra[t % PF][3], t ? dp : f32x16{}, 0, 0, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      // the finished half's S and dP move to VGPRs, where the softmax reads them, and
-      // free their accumulator registers for the next half's products
-      if (m == KT) asm volatile("" : "+v"(s[0]), "+v"(dp[0]));
-      if (m == NAB) asm volatile("" : "+v"(s[1]), "+v"(dp[1]));
-      if (m + PA < NAB) {
-        load(m + PA);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      if (m + PT >= NAB && m + PT < NPAIR) {
-        load(m + PT);
+      if (t + PF < KT) {
+        ld(t + PF);
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       }
-      if (m == NAB - 2) {
-        ld_rows(1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    }
+    // P = exp2(s * scale*log2e - L2), dS = P (dP - D), rows 8g + 4hf + e of this wave's half;
+    // only this part differs between blocks with and without masked pairs
+    bf16x8 pb[2], db[2];
+    auto softmax = [&](auto mask_c) {
+      constexpr bool MASKED = decltype(mask_c)::value;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int rl = 32 * rh + 8 * g + 4 * hf;
+        const f32x4 l2 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+            (uintptr_t)(const lds_void*)&rowv[STG][0][rl]);
+        const f32x4 dd = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+            (uintptr_t)(const lds_void*)&rowv[STG][1][rl]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2[e]));
+          if (MASKED) {
+            const int c = 8 * g + e;
+            pr = (c >= lo && c < hi) ? pr : 0.f;
+          }
+          dp[r] = pr * (dp[r] - dd[e]);  // dS over dP and P over S, in place
+          s[r] = pr;
+        }
       }
-      // the next block's Q and dO loads, one per two pairs of phases A and B
-      static_assert(4 * NLDQ <= NAB, "loads spread over phases A and B");
+      pb[0] = cvt_bf16x8(slice8(s, 0));
+      pb[1] = cvt_bf16x8(slice8(s, 1));
+      db[0] = cvt_bf16x8(slice8(dp, 0));
+      db[1] = cvt_bf16x8(slice8(dp, 1));
+    };
+    // masking: causal diagonal, query rows past n_q, keys past n_k (uniform per wave)
+    if ((p.causal && i0 < kw0 + 31) || (i0 + 32 > p.n_q) || (kw0 + 32 > p.n_k))
+      softmax(std::true_type{});
+    else
+      softmax(std::false_type{});
+    // dV^T += dO^T P, dK^T += Q^T dS over the wave's 32 rows (2 k-steps of 16), the
+    // transposed operands read PT products ahead
+    {
+      constexpr int NST = 2 * NB;
+      constexpr int PT = D == 128 ? 2 : 3;
+      bf16x8 rdo[PT], rq[PT];
+      auto ldt = [&](int st) {
+        const int t = st / NB, nb = st % NB;
+        const unsigned o = 16 * t * ROW;
+        rdo[st % PT] = tr_pair(la.va[2 * nb] + DOFF + o, la.va[2 * nb + 1] + DOFF + o);
+        rq[st % PT] = tr_pair(la.va[2 * nb] + QOFF + o, la.va[2 * nb + 1] + QOFF + o);
+      };
 #pragma unroll
-      for (int i = 0; i < 2 * NLDQ; ++i)
-        if (m == 2 * i + 1) dma_part(1 - STG, qi + 1, i);
-      if (m >= KT && m < NAB) {  // phase B: softmax of rows 0-31
+      for (int st = 0; st < PT; ++st) ldt(st);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * PT, 0);
 #pragma unroll
-        for (int e = 0; e < EB; ++e) softmax(0, (m - KT) * EB + e);
-        __builtin_amdgcn_sched_group_barrier(0x002, EB * VPE, 0);
-      } else if (m >= NAB && m < NAB + NC) {  // phase C: softmax of rows 32-63
-#pragma unroll
-        for (int e = 0; e < EC; ++e) softmax(1, (m - NAB) * EC + e);
-        __builtin_amdgcn_sched_group_barrier(0x002, EC * VPE, 0);
+      for (int st = 0; st < NST; ++st) {
+        const int t = st / NB, nb = st % NB;
+        dvt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rdo[st % PT], pb[t], dvt[nb], 0, 0, 0);
+        dkt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq[st % PT], db[t], dkt[nb], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (st + PT < NST) {
+          ldt(st + PT);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        }
       }
-      // each pair is a scheduling region of its own: the issue order above is kept
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto run_step = [&](auto stg_c, int qi) {
-    const int i0 = qi * kBQ;
-    // masking: causal diagonal, query rows past n_q, keys past n_k (uniform per wave)
-    const bool need_mask = (p.causal && i0 < kw0 + 31) || (i0 + kBQ > p.n_q) || (kw0 + 32 > p.n_k);
-    if (need_mask)
-      step(stg_c, std::true_type{}, qi);
-    else
-      step(stg_c, std::false_type{}, qi);
-  };
 
-  // two LDS stages, unrolled by two so that every offset is an immediate
   for (int qi = qb0; qi < n_qb; qi += 2) {
-    // keep the dV^T / dK^T accumulators in AGPRs across iterations: otherwise the
-    // loop-carried values are assigned VGPRs and each iteration copies all 128 of
-    // them out of and back into the AGPRs the products accumulate in
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(dvt[nb]), "+a"(dkt[nb]));
-    // vmcnt(0) through the builtin, which the compiler's own wait tracking sees: it then
-    // knows that no earlier load is outstanding inside the step
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();  // stage 0 published; stage 1 free
-    if (qi + 1 < n_qb) issue_rowv(1, qi + 1);
-    run_step(std::integral_constant<int, 0>{}, qi);  // also loads Q, dO of block qi + 1
+    __syncthreads();  // stage 0 (and the K/V block) published; stage 1 free
+    if (qi + 1 < n_qb) issue_q(1, qi + 1);
+    step(std::integral_constant<int, 0>{}, qi);
     if (qi + 1 < n_qb) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
-      if (qi + 2 < n_qb) issue_rowv(0, qi + 2);
-      run_step(std::integral_constant<int, 1>{}, qi + 1);
+      if (qi + 2 < n_qb) issue_q(0, qi + 2);
+      step(std::integral_constant<int, 1>{}, qi + 1);
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last step's loads land before the workgroup ends
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();  // every wave is done with the tiles: their space takes the partial sums
 
-  // dK = scale * dK, dV, rows d 32nb + 8g + 4hf + 0..3 of this lane's key
-  if (key < p.n_k) {
-    uint16_t* dkr = p.dk + (hk + key) * D;
-    uint16_t* dvr = p.dv + (hk + key) * D;
+  // the two waves of a key slice add their partial sums: waves 4-7 store dV^T, then dK^T,
+  // in the Q/dO tiles' space, waves 0-3 add them and write the result
+  float* part = reinterpret_cast<float*>(&qdo[0][0][0]);  // [slice][nb][16][64 lanes]
+  static_assert(4 * NB * 16 * 64 * 4 <= (int)sizeof(qdo), "partials fit in the tile space");
+  const bool write = key < p.n_k;
+  uint16_t* dkr = p.dk + (hk + key) * D;
+  uint16_t* dvr = p.dv + (hk + key) * D;
+  auto reduce = [&](f32x16(&acc)[NB], uint16_t* dst, float sc) {
+    if (rh == 1) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        const f32x4 k4 = {dkt[nb][4 * g] * p.scale, dkt[nb][4 * g + 1] * p.scale, dkt[nb][4 * g + 2] * p.scale,
-                          dkt[nb][4 * g + 3] * p.scale};
-        const f32x4 v4 = {dvt[nb][4 * g], dvt[nb][4 * g + 1], dvt[nb][4 * g + 2], dvt[nb][4 * g + 3]};
-        const int d0 = 32 * nb + 8 * g + 4 * hf;
-        *reinterpret_cast<u32x2*>(dkr + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(k4, bf16x4));
-        *reinterpret_cast<u32x2*>(dvr + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(v4, bf16x4));
-      }
-  }
+        for (int r = 0; r < 16; ++r) part[((ks * NB + nb) * 16 + r) * 64 + lane] = acc[nb][r];
+    }
+    __syncthreads();
+    if (rh == 0 && write) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v4[e] = (acc[nb][4 * g + e] + part[((ks * NB + nb) * 16 + 4 * g + e) * 64 + lane]) * sc;
+          *reinterpret_cast<u32x2*>(dst + 32 * nb + 8 * g + 4 * hf) =
+              __builtin_bit_cast(u32x2, __builtin_convertvector(v4, bf16x4));
+        }
+    }
+    __syncthreads();
+  };
+  reduce(dvt, dvr, 1.f);
+  reduce(dkt, dkr, p.scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -875,14 +826,14 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   const bool pp = p.d == 128 && p.n_q >= kDqPingPongMinRows;
   if (p.d == 128) {
     hipLaunchKernelGGL(bwd_prep_kernel<128>, dim3(g0), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(bwd_kv_kernel<128>, dim3(g1), dim3(256), 0, stream, p, sl2);
+    hipLaunchKernelGGL(bwd_kv8_kernel<128>, dim3(g1), dim3(512), 0, stream, p, sl2);
     if (pp)
       hipLaunchKernelGGL(bwd_dq_pp_kernel<128>, dim3(g3), dim3(512), 0, stream, p, sl2, sched);
     else
       hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(g2), dim3(256), 0, stream, p, sl2, sched);
   } else {
     hipLaunchKernelGGL(bwd_prep_kernel<64>, dim3(g0), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(bwd_kv_kernel<64>, dim3(g1), dim3(256), 0, stream, p, sl2);
+    hipLaunchKernelGGL(bwd_kv8_kernel<64>, dim3(g1), dim3(512), 0, stream, p, sl2);
     if (pp)
       hipLaunchKernelGGL(bwd_dq_pp_kernel<64>, dim3(g3), dim3(512), 0, stream, p, sl2, sched);
     else
