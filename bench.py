@@ -235,7 +235,7 @@ def main():
 
     peak = PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
     if args.bwd:
-        kname, traffic = "bwd_kv8_kernel<128> + bwd_dq_pp_kernel<128>", measured_traffic(f"bwd:{w.name}:noncausal",
+        kname, traffic = "bwd_kv_pp_kernel<128> + bwd_dq_pp_kernel<128>", measured_traffic(f"bwd:{w.name}:noncausal",
                                                                                       (BWD_SRC,))
         # read Q, O, dO (N_q x d) and K, V (N_k x d) in bf16 and LSE in fp32; write dQ, dK, dV in bf16
         alg_bytes = w.B * w.H * (2 * (3 * w.n_q + 2 * w.n_k) * w.d + 4 * w.n_q + 2 * (w.n_q + 2 * w.n_k) * w.d)

@@ -19,7 +19,9 @@
 //                      streamed through LDS; four products on the matrix cores
 //                      (S, dP, then dV and dK); K and V of the block stay in
 //                      LDS, dK and dV in registers, and the two halves' sums
-//                      are added at the end
+//                      are added at the end.  At d = 128, bwd_kv_pp_kernel
+//                      does the same work with the two waves of a SIMD one
+//                      phase apart (ping-pong schedule)
 //   bwd_dq_kernel      one workgroup per 128-row query block (one wave per 32
 //                      rows): streams 64-key K/V tiles through LDS as the
 //                      forward does and runs three products (S, dP, then
@@ -32,7 +34,7 @@
 // bit-reproducible.  S and dP are computed twice (once per pass): seven
 // products instead of five, against no dQ workspace and no reduction pass.
 //
-// In bwd_kv_kernel the scores are computed as S = Q K^T (query rows x 32
+// In the key pass the scores are computed as S = Q K^T (query rows x 32
 // keys), so every lane owns one key column: P and dS in accumulator layout
 // are then directly the B operands of dV^T += dO^T P and dK^T += Q^T dS.  In
 // bwd_dq_kernel they are computed transposed (S^T = K Q^T, as the forward),
@@ -48,7 +50,7 @@
 namespace fa2 {
 namespace {
 
-constexpr int kBK = 128;  // keys per workgroup of bwd_kv_kernel
+constexpr int kBK = 128;  // keys per workgroup of the key pass
 constexpr int kBQ = 64;   // query rows per step
 // s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt fields at their maxima)
 constexpr int kWaitVm0 = 0x0F70;
@@ -292,6 +294,296 @@ __global__ void __launch_bounds__(512, 1) bwd_kv8_kernel(BwdParams p, float sl2)
       __syncthreads();
       if (qi + 2 < n_qb) issue_q(0, qi + 2);
       step(std::integral_constant<int, 1>{}, qi + 1);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();  // every wave is done with the tiles: their space takes the partial sums
+
+  // the two waves of a key slice add their partial sums: waves 4-7 store dV^T, then dK^T,
+  // in the Q/dO tiles' space, waves 0-3 add them and write the result
+  float* part = reinterpret_cast<float*>(&qdo[0][0][0]);  // [slice][nb][16][64 lanes]
+  static_assert(4 * NB * 16 * 64 * 4 <= (int)sizeof(qdo), "partials fit in the tile space");
+  const bool write = key < p.n_k;
+  uint16_t* dkr = p.dk + (hk + key) * D;
+  uint16_t* dvr = p.dv + (hk + key) * D;
+  auto reduce = [&](f32x16(&acc)[NB], uint16_t* dst, float sc) {
+    if (rh == 1) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) part[((ks * NB + nb) * 16 + r) * 64 + lane] = acc[nb][r];
+    }
+    __syncthreads();
+    if (rh == 0 && write) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v4[e] = (acc[nb][4 * g + e] + part[((ks * NB + nb) * 16 + 4 * g + e) * 64 + lane]) * sc;
+          *reinterpret_cast<u32x2*>(dst + 32 * nb + 8 * g + 4 * hf) =
+              __builtin_bit_cast(u32x2, __builtin_convertvector(v4, bf16x4));
+        }
+    }
+    __syncthreads();
+  };
+  reduce(dvt, dvr, 1.f);
+  reduce(dkt, dkr, p.scale);
+}
+
+// ---------------------------------------------------------------------------
+// Key pass, ping-pong form: the workgroup, keys and row halves of bwd_kv8_kernel, with
+// the two waves of a SIMD one phase apart as in the ping-pong forward: group 0 (waves
+// 0-3, rows 0-31 of every 64-row query block) runs one phase ahead of group 1 (waves
+// 4-7, rows 32-63).  Per query block j and wave:
+//   matrix phase:  dV^T += dO_{j-1}^T P_{j-1};  dK^T += Q_{j-1}^T dS_{j-1};
+//                  S_j = Q_j K^T;  dP_j = dO_j V^T
+//   vector phase:  P_j = exp2(s * scale*log2e - L2) (0 where masked), dS_j = P_j (dP_j - D)
+// so that one wave of a SIMD issues 32 products while its partner does the vector work.
+// The Q/dO tiles have two stages, each filled half by half: a group loads its rows of
+// its next block at the start of its vector phase, into the place of the block its
+// matrix phase has just finished with, and retires the loads before the phase ends, so
+// that neither the issue of the loads nor the wait for them falls in a matrix phase.
+template <int D>
+__global__ void __launch_bounds__(512, 1) bwd_kv_pp_kernel(BwdParams p, float sl2) {
+  constexpr int NW = 8;
+  constexpr int NB = D / 32;
+  constexpr int KT = D / 16;
+  constexpr int ROW = D * 2;         // bytes per row
+  constexpr int TILE = kBQ * D * 2;  // one 64-row Q or dO tile
+  constexpr int HALF = TILE / 2;     // its 32 rows of one group
+  constexpr int BLK = kBK * D * 2;   // the 128-key K or V block
+  constexpr int CPR = D / 8;
+
+  __shared__ __attribute__((aligned(1024))) char kvb[2][BLK];       // K = 0, V = 1
+  __shared__ __attribute__((aligned(1024))) char qdo[2][2][TILE];   // [stage][Q = 0 / dO = 1]
+  __shared__ __attribute__((aligned(16))) float rowv[2][2][kBQ];     // [stage][L2 = 0 / D = 1][row]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ks = wave & 3;   // key slice
+  const int rh = wave >> 2;  // row half, and the group
+  const int hf = lane >> 5;
+  const int col = lane & 31;
+
+  const int n_kb = (p.n_k + kBK - 1) / kBK;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = L / n_kb;
+  const int kb = L % n_kb;
+  const int n_qb = (p.n_q + kBQ - 1) / kBQ;
+
+  const long long hq = (long long)bh * p.n_q, hk = (long long)bh * p.n_k;
+  const i32x4 qrs = raw_rsrc(p.q + hq * D, (long long)p.n_q * D * 2);
+  const i32x4 dors = raw_rsrc(p.dout + hq * D, (long long)p.n_q * D * 2);
+  const i32x4 l2rs = raw_rsrc(p.l2vec + hq, (long long)p.n_q * 4);
+  const i32x4 dvrs = raw_rsrc(p.dvec + hq, (long long)p.n_q * 4);
+  const i32x4 krs = raw_rsrc(p.k + hk * D, (long long)p.n_k * D * 2);
+  const i32x4 vrs = raw_rsrc(p.v + hk * D, (long long)p.n_k * D * 2);
+
+  LdsAddr<D> la, lk;  // la over qdo from this wave's first row, lk over K from its first key
+  make_lds_addr<D>(la, (unsigned)(uintptr_t)(const lds_void*)&qdo[0][0][0] + (unsigned)(32 * rh) * ROW, lane);
+  make_lds_addr<D>(lk, (unsigned)(uintptr_t)(const lds_void*)&kvb[0][0] + (unsigned)(32 * ks) * ROW, lane);
+
+  const int k0 = kb * kBK;
+  const int kw0 = k0 + 32 * ks;  // this wave's keys kw0 .. kw0 + 31
+  const int key = kw0 + col;     // this lane's key column
+  const int qb0 = p.causal ? min(k0 / kBQ, n_qb) : 0;
+  const int n_t = n_qb - qb0;    // query blocks this key block sees
+
+  // slot offsets: the K/V block takes NLDB loads per wave and array, a half tile NLDH per
+  // wave of the loading group (the swizzle repeats every 16 rows)
+  constexpr int NLDB = kBK * CPR / (64 * NW);
+  constexpr int NLDH = 32 * CPR / (64 * 4);
+  constexpr int NDMA = 2 * NLDH;  // Q parts, then dO parts
+  unsigned offh[NLDH];
+#pragma unroll
+  for (int i = 0; i < NLDH; ++i) {
+    const int sl = (i * 4 + ks) * 64 + lane;
+    const int r = sl / CPR;
+    const int c = (sl % CPR) ^ (swz<D>(r, 0) - r * CPR);
+    offh[i] = (unsigned)((r * D + c * 8) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < NLDB; ++i) {
+    const int sl = (i * NW + wave) * 64 + lane;
+    const int r = sl / CPR;
+    const int c = (sl % CPR) ^ (swz<D>(r, 0) - r * CPR);
+    const unsigned o = (unsigned)((r * D + c * 8) * 2) + (unsigned)k0 * D * 2;
+    lds_dma16(krs, &kvb[0][(i * NW + wave) * 64 * 16], o);
+    lds_dma16(vrs, &kvb[1][(i * NW + wave) * 64 * 16], o);
+  }
+  // part i of this wave's share of half h of query block qi, into stage st; part 0 of a
+  // key-slice-0 wave also brings the half's 32 L2 and 32 D values
+  auto dma_half = [&](int st, int h, int qi, int i) {
+    if (qi >= n_qb) return;
+    const unsigned goff = (unsigned)(qi * kBQ + 32 * h) * ROW;
+    const int a = i / NLDH, ii = i % NLDH;
+    lds_dma16(a ? dors : qrs, &qdo[st][a][h * HALF + (ii * 4 + ks) * 64 * 16], offh[ii] + goff);
+    if (i == 0 && ks == 0) {
+      const unsigned roff = (unsigned)(qi * kBQ + 32 * h) * 4;
+      if (lane < 8)
+        lds_dma16(l2rs, reinterpret_cast<const char*>(&rowv[st][0][32 * h]), roff + lane * 16);
+      else if (lane < 16)
+        lds_dma16(dvrs, reinterpret_cast<const char*>(&rowv[st][1][32 * h]) - 128, roff + (lane - 8) * 16);
+    }
+  };
+  if (rh == 0) {
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) dma_half(0, 0, qb0, i);
+  }
+  // the first matrix phase of each group multiplies P = dS = 0 with stage 1, which no
+  // load has written yet: zero it
+  {
+    constexpr int PER = 2 * TILE / (64 * NW);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < PER / 16; ++i)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+          (uintptr_t)(const lds_void*)&qdo[1][0][(tid * (PER / 16) + i) * 16]) = z;
+  }
+
+  f32x16 dvt[NB], dkt[NB];  // dV^T, dK^T over this wave's rows: rows d, columns its keys
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    dvt[nb] = f32x16{};
+    dkt[nb] = f32x16{};
+  }
+  f32x16 s = {}, dp = {};
+  bf16x8 pb[2] = {}, db[2] = {};
+
+  // matrix phase of block j, whose tiles sit in stage STG (block j - 1 in the other): one
+  // stream of 32 products, dV^T and dK^T of block j - 1 (16-row k-step t, d block nb)
+  // then S and dP of block j (k-step t), each product's operands read PD products ahead
+  auto mat = [&](int j, auto stg_c) {
+    constexpr int STG = decltype(stg_c)::value;
+    constexpr unsigned QC = STG * 2 * TILE, DC = QC + TILE;
+    constexpr unsigned QP = (1 - STG) * 2 * TILE, DP = QP + TILE;
+    constexpr int NG = 4 * NB;  // gradient products
+    constexpr int NM = NG + 2 * KT;
+    constexpr int PD = 4;
+    bf16x8 oa[PD], ob[PD];
+    auto load = [&](int m) {
+      if (m < NG) {
+        const int st = m / 2, t = st / NB, nb = st % NB;
+        const unsigned o = (m % 2 ? QP : DP) + 16 * t * ROW;
+        oa[m % PD] = tr_pair(la.va[2 * nb] + o, la.va[2 * nb + 1] + o);
+      } else {
+        const int i = m - NG, t = i / 2;
+        oa[m % PD] = lds_load<bf16x8>(la.ka[t] + (i % 2 ? DC : QC));
+        ob[m % PD] = lds_load<bf16x8>(lk.ka[t] + (i % 2 ? BLK : 0));
+      }
+    };
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int m = 0; m < PD; ++m) load(m);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PD, 0);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      if (m < NG) {
+        const int st = m / 2, t = st / NB, nb = st % NB;
+        if (m % 2 == 0)
+          dvt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[m % PD], pb[t], dvt[nb], 0, 0, 0);
+        else
+          dkt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[m % PD], db[t], dkt[nb], 0, 0, 0);
+      } else {
+        const int i = m - NG, t = i / 2;
+        if (i % 2 == 0)
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[m % PD], ob[m % PD], t ? s : f32x16{}, 0, 0, 0);
+        else
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[m % PD], ob[m % PD], t ? dp : f32x16{}, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (m + PD < NM) {
+        load(m + PD);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // vector phase of block j (stage STG): P and dS (bf16) for the next matrix phase; the
+  // group's loads (dma(i), i < NDMA) are issued first
+  auto vec = [&](int j, auto stg_c, auto&& dma) {
+    constexpr int STG = decltype(stg_c)::value;
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) dma(i);
+    if (j < 0 || j >= n_t) {
+      pb[0] = pb[1] = db[0] = db[1] = bf16x8{};
+      return;
+    }
+    const int i0 = (qb0 + j) * kBQ + 32 * rh;  // first row
+    // element (8g + e) is row i0 + 8g + 4hf + e: visible to this lane's key when
+    // lo <= 8g + e < hi
+    const int lo = (p.causal ? key - i0 : 0) - 4 * hf;
+    const int hi = (key < p.n_k ? p.n_q - i0 : 0) - 4 * hf;
+    auto softmax = [&](auto mask_c) {
+      constexpr bool MASKED = decltype(mask_c)::value;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int rl = 32 * rh + 8 * g + 4 * hf;
+        const f32x4 l2 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+            (uintptr_t)(const lds_void*)&rowv[STG][0][rl]);
+        const f32x4 dd = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+            (uintptr_t)(const lds_void*)&rowv[STG][1][rl]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2[e]));
+          if (MASKED) {
+            const int c = 8 * g + e;
+            pr = (c >= lo && c < hi) ? pr : 0.f;
+          }
+          dp[r] = pr * (dp[r] - dd[e]);  // dS over dP and P over S, in place
+          s[r] = pr;
+        }
+      }
+      pb[0] = cvt_bf16x8(slice8(s, 0));
+      pb[1] = cvt_bf16x8(slice8(s, 1));
+      db[0] = cvt_bf16x8(slice8(dp, 0));
+      db[1] = cvt_bf16x8(slice8(dp, 1));
+    };
+    // masking: causal diagonal, query rows past n_q, keys past n_k (uniform per wave)
+    if ((p.causal && i0 < kw0 + 31) || (i0 + 32 > p.n_q) || (kw0 + 32 > p.n_k))
+      softmax(std::true_type{});
+    else
+      softmax(std::false_type{});
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  // group 0 loads the first half of block j + 1 in its vector phase on block j, group 1
+  // the second half of block j in its vector phase on block j - 1: places last read by
+  // the group's matrix phase just before
+  auto iter0 = [&](int j, auto stg_c) {
+    constexpr int STG = decltype(stg_c)::value;
+    mat(j, stg_c);
+    __syncthreads();
+    vec(j, stg_c, [&](int i) { dma_half(1 - STG, 0, qb0 + j + 1, i); });
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+  };
+  auto iter1 = [&](int j, auto stg_c) {
+    constexpr int STG = decltype(stg_c)::value;
+    vec(j - 1, std::integral_constant<int, 1 - STG>{}, [&](int i) { dma_half(STG, 1, qb0 + j, i); });
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    mat(j, stg_c);
+    __syncthreads();
+  };
+
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();  // the K/V block, the first half tile and the zeroed stage published
+  if (rh == 0) {
+    for (int j = 0; j <= n_t; j += 2) {
+      iter0(j, S0{});
+      if (j + 1 <= n_t) iter0(j + 1, S1{});
+    }
+  } else {
+    for (int j = 0; j <= n_t; j += 2) {
+      iter1(j, S0{});
+      if (j + 1 <= n_t) iter1(j + 1, S1{});
     }
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -826,7 +1118,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   const bool pp = p.d == 128 && p.n_q >= kDqPingPongMinRows;
   if (p.d == 128) {
     hipLaunchKernelGGL(bwd_prep_kernel<128>, dim3(g0), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(bwd_kv8_kernel<128>, dim3(g1), dim3(512), 0, stream, p, sl2);
+    hipLaunchKernelGGL(bwd_kv_pp_kernel<128>, dim3(g1), dim3(512), 0, stream, p, sl2);
     if (pp)
       hipLaunchKernelGGL(bwd_dq_pp_kernel<128>, dim3(g3), dim3(512), 0, stream, p, sl2, sched);
     else
