@@ -264,6 +264,24 @@ __device__ __forceinline__ void tile_step(WaveRows<D>& w, const LdsAddr<D>& la, 
 // publishes tile j and retires the buffer of tile j-1.
 //   MASK   stream only the key tiles that the block mask row of the workgroup's
 //          query block marks (p.bmask; 128-row workgroups, NW == 4, one mask row each)
+// Tile t of a wave's key range (keys kfirst + kBC t ..): live when ja <= t < jb, and
+// masked when t >= jmh (it reaches past kend or past the band's upper edge) or t < jml
+// (it starts before the lower edge).  Taken once per wave, so that each tile costs two
+// comparisons; >> 6 is a floor division by kBC, negative values included.
+struct TileBounds {
+  int ja, jb, jmh, jml;
+};
+__device__ __forceinline__ TileBounds tile_bounds(int kfirst, int n_tiles, int klo_w, int khi_w, int kend, int q0w,
+                                                  int wl, int wr) {
+  static_assert(kBC == 64, "tile bounds divide by 64");
+  TileBounds b;
+  b.ja = (klo_w - kfirst) >> 6;
+  b.jb = min(n_tiles, (khi_w - kfirst + 63) >> 6);
+  b.jmh = wr >= 0 ? min((kend - kfirst) >> 6, ((q0w + wr - 63 - kfirst) >> 6) + 1) : (kend - kfirst) >> 6;
+  b.jml = wl >= 0 ? (q0w + 31 - wl - kfirst + 63) >> 6 : -(1 << 30);
+  return b;
+}
+
 template <int D, int NW, bool SPLIT, bool MASK = false>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float sl2, unsigned qsign) {
   static_assert(!MASK || (NW == 4 && !SPLIT), "block masks are read per 128-row workgroup");
@@ -347,14 +365,13 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
 
   // A tile is skipped when no row of this wave sees any of its keys, and
   // masked when it crosses either edge of the wave's band or the key tail.
-#define FA2_STEP(STG, k0_)                                                                             \
-  do {                                                                                               \
-    const int kk = (k0_);                                                                            \
-    if (kk < khi_w && kk + kBC > klo_w)                                                              \
-      tile_step<D, STG * STAGE, STG * STAGE + TILE_BYTES>(                                           \
-          w, la,                                                                                     \
-          (kk + kBC > kend) || (wr >= 0 && kk + kBC - 1 > q0w + wr) || (wl >= 0 && kk < q0w + 31 - wl), \
-          kk, row_lo, row_hi, sl2, lane);                                                            \
+  const TileBounds bnd = tile_bounds(kfirst, n_tiles, klo_w, khi_w, kend, q0w, wl, wr);
+#define FA2_STEP(STG, t_)                                                                  \
+  do {                                                                                     \
+    const int t = (t_);                                                                    \
+    if (t >= bnd.ja && t < bnd.jb)                                                         \
+      tile_step<D, STG * STAGE, STG * STAGE + TILE_BYTES>(w, la, t >= bnd.jmh || t < bnd.jml, \
+                                                          kfirst + t * kBC, row_lo, row_hi, sl2, lane); \
   } while (0)
 
   if (MASK) {
@@ -388,13 +405,13 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
       __syncthreads();
       const int tb = next_active(ta + 1);
       if (tb < n_tiles) issue_tile<D, NW>(krs, vrs, lds[1][0], lds[1][1], kfirst + tb * kBC, wave, lane);
-      FA2_STEP(0, kfirst + ta * kBC);
+      FA2_STEP(0, ta);
       if (tb >= n_tiles) break;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       ta = next_active(tb + 1);
       if (ta < n_tiles) issue_tile<D, NW>(krs, vrs, lds[0][0], lds[0][1], kfirst + ta * kBC, wave, lane);
-      FA2_STEP(1, kfirst + tb * kBC);
+      FA2_STEP(1, tb);
     }
   }
   // unrolled by two so that each stage's LDS offsets are compile-time constants
@@ -404,12 +421,12 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (j + 1 < n_tiles) issue_tile<D, NW>(krs, vrs, lds[1][0], lds[1][1], k0 + kBC, wave, lane);
-    FA2_STEP(0, k0);
+    FA2_STEP(0, j);
     if (j + 1 < n_tiles) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (j + 2 < n_tiles) issue_tile<D, NW>(krs, vrs, lds[0][0], lds[0][1], k0 + 2 * kBC, wave, lane);
-      FA2_STEP(1, k0 + kBC);
+      FA2_STEP(1, j + 1);
     }
   }
 #undef FA2_STEP
@@ -883,14 +900,9 @@ __global__ void __launch_bounds__(512, 1) fwd_pp_kernel(FwdParams p, float sl2, 
           (uintptr_t)(const lds_void*)&ldsv[2][(tid * (PER / 16) + i) * 16]) = z;
   }
 
-  auto act = [&](int j) {
-    const int kk = kfirst + j * kBC;
-    return j >= 0 && j < n_tiles && kk < khi_w && kk + kBC > klo_w;
-  };
-  auto need_mask = [&](int j) {
-    const int kk = kfirst + j * kBC;
-    return (kk + kBC > p.n_k) || (wr >= 0 && kk + kBC - 1 > q0w + wr) || (wl >= 0 && kk < q0w + 31 - wl);
-  };
+  const TileBounds bnd = tile_bounds(kfirst, n_tiles, klo_w, khi_w, p.n_k, q0w, wl, wr);
+  auto act = [&](int j) { return j >= bnd.ja && j < bnd.jb; };
+  auto need_mask = [&](int j) { return j >= bnd.jmh || j < bnd.jml; };
   // matrix phase of tile j: O += P_{j-1} V_{j-1}, then S_j = K_j Q^T, with the loads of
   // K_{j+2} and V_{j+1} issued among the products.  KST = j % 3: stage of K_j.
   auto mat = [&](int j, auto kst) {
