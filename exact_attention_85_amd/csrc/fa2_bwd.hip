@@ -770,23 +770,32 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p, float sl2, 
     f32x16 s0, s1, d0, d1;
     rows_product<D, KOFF>(la, qf, s0, s1, dma);
     rows_product<D, VOFF>(la, dof, d0, d1, [](int) {});
-    // register r of block kb holds key k0 + 32kb + 8(r/4) + 4hf + r%4 of this lane's row
-    const bool need_mask = (k0 + kBC > p.n_k) || (p.causal && k0 + kBC - 1 > q0w);
-    const int hi = min(p.n_k - 1, p.causal ? row : p.n_k - 1) - k0 - 4 * hf;  // last visible offset
-    bf16x8 db[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const f32x16& s = kb ? s1 : s0;
-      const f32x16& dp = kb ? d1 : d0;
-      f32x16 ds;
+      f32x16& dp = kb ? d1 : d0;  // dS replaces dP in place
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2)) * (dp[r] - dd);
+    }
+    // masked pairs (keys past n_k, or past the row under the causal mask) get dS = 0,
+    // selected over whatever the unmasked formula gave; only tiles that reach past n_k or
+    // the diagonal (uniform per wave) take this branch
+    if ((k0 + kBC > p.n_k) || (p.causal && k0 + kBC - 1 > q0w)) {
+      // register r of block kb holds key k0 + 32kb + 8(r/4) + 4hf + r%4 of this lane's row
+      const int hi = min(p.n_k - 1, p.causal ? row : p.n_k - 1) - k0 - 4 * hf;  // last visible offset
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2));
-        if (need_mask && 32 * kb + 8 * (r >> 2) + (r & 3) > hi) pr = 0.f;
-        ds[r] = pr * (dp[r] - dd);
+        const int c = 8 * (r >> 2) + (r & 3);
+        d0[r] = c > hi ? 0.f : d0[r];
+        d1[r] = c + 32 > hi ? 0.f : d1[r];
       }
-      db[2 * kb] = cvt_bf16x8(slice8(ds, 0));
-      db[2 * kb + 1] = cvt_bf16x8(slice8(ds, 1));
+    }
+    bf16x8 db[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const f32x16& dp = kb ? d1 : d0;
+      db[2 * kb] = cvt_bf16x8(slice8(dp, 0));
+      db[2 * kb + 1] = cvt_bf16x8(slice8(dp, 1));
     }
     // dQ^T += K^T dS^T: K^T read transposed from the K tile, keys in the order of db
 #pragma unroll
@@ -1018,19 +1027,29 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_pp_kernel(BwdParams p, float sl
       return;
     }
     const int k0 = j * kBC;
-    // register r of block kb holds key k0 + 32kb + 8(r/4) + 4hf + r%4 of this lane's row
-    const bool need_mask = (k0 + kBC > p.n_k) || (p.causal && k0 + kBC - 1 > q0w);
-    const int hi = min(p.n_k - 1, p.causal ? row : p.n_k - 1) - k0 - 4 * hf;  // last visible offset
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const f32x16& s = kb ? s1 : s0;
       f32x16& dp = kb ? d1 : d0;  // dS replaces dP in place
 #pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2)) * (dp[r] - dd);
+    }
+    // masked pairs (keys past n_k, or past the row under the causal mask) get dS = 0,
+    // selected over whatever the unmasked formula gave; only tiles that reach past n_k or
+    // the diagonal (uniform per wave) take this branch
+    if ((k0 + kBC > p.n_k) || (p.causal && k0 + kBC - 1 > q0w)) {
+      // register r of block kb holds key k0 + 32kb + 8(r/4) + 4hf + r%4 of this lane's row
+      const int hi = min(p.n_k - 1, p.causal ? row : p.n_k - 1) - k0 - 4 * hf;  // last visible offset
+#pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2));
-        if (need_mask && 32 * kb + 8 * (r >> 2) + (r & 3) > hi) pr = 0.f;
-        dp[r] = pr * (dp[r] - dd);
+        const int c = 8 * (r >> 2) + (r & 3);
+        d0[r] = c > hi ? 0.f : d0[r];
+        d1[r] = c + 32 > hi ? 0.f : d1[r];
       }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const f32x16& dp = kb ? d1 : d0;
       db[2 * kb] = cvt_bf16x8(slice8(dp, 0));
       db[2 * kb + 1] = cvt_bf16x8(slice8(dp, 1));
     }
