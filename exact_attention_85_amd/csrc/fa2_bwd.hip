@@ -13,7 +13,7 @@
 //   dQ_i  = scale sum_j dS_ij k_j
 //
 // Three launches:
-//   bwd_prep_kernel    D_i and LSE_i * log2(e) for every query row
+//   bwd_prep_kernel    -D_i and LSE_i * log2(e) for every query row
 //   bwd_kv8_kernel     one workgroup of 8 waves per 128-key block: two waves per
 //                      32 keys, each over half of every 64-row query block
 //                      streamed through LDS; four products on the matrix cores
@@ -78,7 +78,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
 #pragma unroll
   for (int x = LPR / 2; x >= 1; x >>= 1) acc += __shfl_xor(acc, x);
   if (sub == 0 && row < R) {
-    p.dvec[row] = acc;
+    p.dvec[row] = -acc;  // -D: the products that need dP - D start from it
     p.l2vec[row] = p.lse[row] * kLog2e;
   }
 }
@@ -241,7 +241,7 @@ __global__ void __launch_bounds__(512, 1) bwd_kv8_kernel(BwdParams p, float sl2)
             const int c = 8 * g + e;
             pr = (c >= lo && c < hi) ? pr : 0.f;
           }
-          dp[r] = pr * (dp[r] - dd[e]);  // dS over dP and P over S, in place
+          dp[r] = pr * (dp[r] + dd[e]);  // dS over dP (dd = -D) and P over S, in place
           s[r] = pr;
         }
       }
@@ -466,6 +466,7 @@ __global__ void __launch_bounds__(512, 1) bwd_kv_pp_kernel(BwdParams p, float sl
     constexpr int NM = NG + 2 * KT;
     constexpr int PD = 4;
     bf16x8 oa[PD], ob[PD];
+    f32x4 nd[4];  // -D of this lane's rows of block j: the start of the dP accumulator
     auto load = [&](int m) {
       if (m < NG) {
         const int st = m / 2, t = st / NB, nb = st % NB;
@@ -494,18 +495,31 @@ __global__ void __launch_bounds__(512, 1) bwd_kv_pp_kernel(BwdParams p, float sl
         if (i % 2 == 0)
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[m % PD], ob[m % PD], t ? s : f32x16{}, 0, 0, 0);
         else
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[m % PD], ob[m % PD], t ? dp : f32x16{}, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              oa[m % PD], ob[m % PD],
+              t ? dp
+                : __builtin_shufflevector(__builtin_shufflevector(nd[0], nd[1], 0, 1, 2, 3, 4, 5, 6, 7),
+                                          __builtin_shufflevector(nd[2], nd[3], 0, 1, 2, 3, 4, 5, 6, 7), 0, 1,
+                                          2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15),
+              0, 0, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (m + PD < NM) {
         load(m + PD);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
+      if (m == NG - 4) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          nd[g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+              (uintptr_t)(const lds_void*)&rowv[STG][1][32 * rh + 8 * g + 4 * hf]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
   };
   // vector phase of block j (stage STG): P and dS (bf16) for the next matrix phase; the
-  // group's loads (dma(i), i < NDMA) are issued first
+  // group's loads (dma(i), i < NDMA) are issued first.  dp holds dP - D already.
   auto vec = [&](int j, auto stg_c, auto&& dma) {
     constexpr int STG = decltype(stg_c)::value;
 #pragma unroll
@@ -526,8 +540,6 @@ __global__ void __launch_bounds__(512, 1) bwd_kv_pp_kernel(BwdParams p, float sl
         const int rl = 32 * rh + 8 * g + 4 * hf;
         const f32x4 l2 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
             (uintptr_t)(const lds_void*)&rowv[STG][0][rl]);
-        const f32x4 dd = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-            (uintptr_t)(const lds_void*)&rowv[STG][1][rl]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
@@ -536,7 +548,7 @@ __global__ void __launch_bounds__(512, 1) bwd_kv_pp_kernel(BwdParams p, float sl
             const int c = 8 * g + e;
             pr = (c >= lo && c < hi) ? pr : 0.f;
           }
-          dp[r] = pr * (dp[r] - dd[e]);  // dS over dP and P over S, in place
+          dp[r] = pr * dp[r];  // dS over dP - D (the products started from -D) and P over S
           s[r] = pr;
         }
       }
@@ -731,7 +743,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p, float sl2, 
     }
     if (row < p.n_q) {
       l2 = p.l2vec[hq + row];
-      dd = p.dvec[hq + row];
+      dd = p.dvec[hq + row];  // -D
     }
   }
   f32x16 dq[NB];
@@ -775,7 +787,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p, float sl2, 
       const f32x16& s = kb ? s1 : s0;
       f32x16& dp = kb ? d1 : d0;  // dS replaces dP in place
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2)) * (dp[r] - dd);
+      for (int r = 0; r < 16; ++r) dp[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2)) * (dp[r] + dd);
     }
     // masked pairs (keys past n_k, or past the row under the causal mask) get dS = 0,
     // selected over whatever the unmasked formula gave; only tiles that reach past n_k or
@@ -849,7 +861,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p, float sl2, 
 // block), waves w and w + 4 on one SIMD, group 0 (waves 0-3) one phase ahead of group 1,
 // as in the ping-pong forward.  Per tile j and wave:
 //   matrix phase:  dQ^T += K_{j-1}^T dS_{j-1}^T;  S_j^T = K_j Q^T;  dP_j^T = V_j dO^T
-//   vector phase:  P_j = exp2(s * scale*log2e - LSE*log2e) (0 where masked), dS_j = P_j (dP_j - D)
+//   vector phase:  P_j = exp2(s * scale*log2e - LSE*log2e) (0 where masked), dS_j = P_j (dP_j - D),
+//                  dP_j - D coming from products that start at -D
 // so that on each SIMD one wave issues 48 products while its partner runs the vector
 // work of the previous tile.  K and V each have a four-stage LDS ring (tile j in stage
 // j % 4): the matrix phase reads K_{j-1}, K_j and V_j and issues the loads of K_{j+2}
@@ -857,7 +870,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p, float sl2, 
 template <int D, unsigned KPREV, unsigned KCUR, unsigned VCUR, int PF, int NDMA, typename Dma>
 __device__ __forceinline__ void dq_mat_stream(const LdsAddr<D>& la, unsigned vdelta, const bf16x8 (&qf)[D / 16],
                                               const bf16x8 (&dof)[D / 16], const bf16x8 (&db)[4], f32x16 (&dq)[D / 32],
-                                              f32x16& s0, f32x16& s1, f32x16& d0, f32x16& d1, Dma&& dma) {
+                                              f32x16& s0, f32x16& s1, f32x16& d0, f32x16& d1, float nd, Dma&& dma) {
   constexpr int NB = D / 32;
   constexpr int KT = D / 16;
   constexpr unsigned ROW = D * 2;
@@ -883,8 +896,12 @@ __device__ __forceinline__ void dq_mat_stream(const LdsAddr<D>& la, unsigned vde
   __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
   s0 = f32x16{};
   s1 = f32x16{};
-  d0 = f32x16{};
-  d1 = f32x16{};
+  // dP^T accumulates on -D of this lane's row, so that the vector phase gets dP - D
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    d0[r] = nd;
+    d1[r] = nd;
+  }
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     if (m < NQ) {
@@ -965,7 +982,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_pp_kernel(BwdParams p, float sl
     }
     if (row < p.n_q) {
       l2 = p.l2vec[hq + row];
-      dd = p.dvec[hq + row];
+      dd = p.dvec[hq + row];  // -D
     }
   }
   f32x16 dq[NB];
@@ -1013,7 +1030,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_pp_kernel(BwdParams p, float sl
     __builtin_amdgcn_s_setprio(1);
     if (act(j - 1) || act(j)) {
       dq_mat_stream<D, ((KS + 3) % 4) * TILE, KS * TILE, KS * TILE, 4, 2 * NLD>(
-          la, vdelta, qf, dof, db, dq, s0, s1, d0, d1, [&](int i) { dma(j, ks, i); });
+          la, vdelta, qf, dof, db, dq, s0, s1, d0, d1, dd, [&](int i) { dma(j, ks, i); });
     } else {
 #pragma unroll
       for (int i = 0; i < 2 * NLD; ++i) dma(j, ks, i);
@@ -1032,7 +1049,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_pp_kernel(BwdParams p, float sl
       const f32x16& s = kb ? s1 : s0;
       f32x16& dp = kb ? d1 : d0;  // dS replaces dP in place
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2)) * (dp[r] - dd);
+      for (int r = 0; r < 16; ++r) dp[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2)) * dp[r];
     }
     // masked pairs (keys past n_k, or past the row under the causal mask) get dS = 0,
     // selected over whatever the unmasked formula gave; only tiles that reach past n_k or

@@ -63,7 +63,7 @@ extern const FwdConfig kFwdConfigs[kNumFwdConfigs];
 int fwd_default_config(int d, bool banded, int n_q, long long n_bh);
 
 // Arguments of the backward launches.  dq, dk, dv are bf16 outputs; the
-// workspace holds l2vec [R] (LSE * log2 e) and dvec [R] (rowsum dO * O),
+// workspace holds l2vec [R] (LSE * log2 e) and dvec [R] (minus rowsum dO * O),
 // R = B*H*N_q.
 struct BwdParams {
   const uint16_t* q;
