@@ -454,6 +454,7 @@ __global__ void __launch_bounds__(512, 1) bwd_kv_pp_kernel(BwdParams p, float sl
   }
   f32x16 s = {}, dp = {};
   bf16x8 pb[2] = {}, db[2] = {};
+  f32x4 l2r[4];  // LSE*log2e of this lane's rows of the block in S, read by the matrix phase
 
   // matrix phase of block j, whose tiles sit in stage STG (block j - 1 in the other): one
   // stream of 32 products, dV^T and dK^T of block j - 1 (16-row k-step t, d block nb)
@@ -515,6 +516,13 @@ __global__ void __launch_bounds__(512, 1) bwd_kv_pp_kernel(BwdParams p, float sl
               (uintptr_t)(const lds_void*)&rowv[STG][1][32 * rh + 8 * g + 4 * hf]);
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       }
+      if (m == NM - 4) {  // and LSE*log2e of the rows for the vector phase
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          l2r[g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+              (uintptr_t)(const lds_void*)&rowv[STG][0][32 * rh + 8 * g + 4 * hf]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -537,9 +545,7 @@ __global__ void __launch_bounds__(512, 1) bwd_kv_pp_kernel(BwdParams p, float sl
       constexpr bool MASKED = decltype(mask_c)::value;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int rl = 32 * rh + 8 * g + 4 * hf;
-        const f32x4 l2 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-            (uintptr_t)(const lds_void*)&rowv[STG][0][rl]);
+        const f32x4 l2 = l2r[g];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
