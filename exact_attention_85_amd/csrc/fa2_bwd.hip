@@ -14,13 +14,12 @@
 //
 // Three launches:
 //   bwd_prep_kernel    -D_i and LSE_i * log2(e) for every query row
-//   bwd_kv8_kernel     one workgroup of 8 waves per 128-key block: two waves per
+//   bwd_kv_pp_kernel   one workgroup of 8 waves per 128-key block: two waves per
 //                      32 keys, each over half of every 64-row query block
 //                      streamed through LDS; four products on the matrix cores
 //                      (S, dP, then dV and dK); K and V of the block stay in
 //                      LDS, dK and dV in registers, and the two halves' sums
-//                      are added at the end.  At d = 128, bwd_kv_pp_kernel
-//                      does the same work with the two waves of a SIMD one
+//                      are added at the end.  The two waves of a SIMD run one
 //                      phase apart (ping-pong schedule)
 //   bwd_dq_kernel      one workgroup per 128-row query block (one wave per 32
 //                      rows): streams 64-key K/V tiles through LDS as the
@@ -92,253 +91,13 @@ __device__ __forceinline__ bf16x8 tr_pair(unsigned a0, unsigned a1) {
 }
 
 // ---------------------------------------------------------------------------
-// Key pass with two waves per SIMD: one workgroup of 8 waves per (batch, head, 128-key
-// block).  Wave w owns keys 32 (w % 4) .. + 31 of the block and rows 32 (w / 4) .. + 31 of
-// every 64-row query block, so the two waves of a SIMD share their keys and split the
-// rows; each accumulates its own dV^T, dK^T (128 registers) and the pair is summed
-// through LDS at the end.  K and V of the block stay in LDS for the whole pass and serve
-// as the B operands of S and dP (instead of 64 registers per wave), which is what lets
-// two waves fit in a SIMD.  Per query block and wave: S, dP (16 products), P and dS in
-// the vector unit, dV^T and dK^T (16 products).
-template <int D>
-__global__ void __launch_bounds__(512, 1) bwd_kv8_kernel(BwdParams p, float sl2) {
-  constexpr int NW = 8;
-  constexpr int NB = D / 32;
-  constexpr int KT = D / 16;
-  constexpr int ROW = D * 2;         // bytes per row
-  constexpr int TILE = kBQ * D * 2;  // one 64-row Q or dO tile
-  constexpr int BLK = kBK * D * 2;   // the 128-key K or V block
-  constexpr int CPR = D / 8;
-
-  __shared__ __attribute__((aligned(1024))) char kvb[2][BLK];       // K = 0, V = 1
-  __shared__ __attribute__((aligned(1024))) char qdo[2][2][TILE];   // [stage][Q = 0 / dO = 1]
-  __shared__ __attribute__((aligned(16))) float rowv[2][2][kBQ];     // [stage][L2 = 0 / D = 1][row]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ks = wave & 3;   // key slice
-  const int rh = wave >> 2;  // row half
-  const int hf = lane >> 5;
-  const int col = lane & 31;
-
-  const int n_kb = (p.n_k + kBK - 1) / kBK;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = L / n_kb;
-  const int kb = L % n_kb;
-  const int n_qb = (p.n_q + kBQ - 1) / kBQ;
-
-  const long long hq = (long long)bh * p.n_q, hk = (long long)bh * p.n_k;
-  const i32x4 qrs = raw_rsrc(p.q + hq * D, (long long)p.n_q * D * 2);
-  const i32x4 dors = raw_rsrc(p.dout + hq * D, (long long)p.n_q * D * 2);
-  const i32x4 l2rs = raw_rsrc(p.l2vec + hq, (long long)p.n_q * 4);
-  const i32x4 dvrs = raw_rsrc(p.dvec + hq, (long long)p.n_q * 4);
-  const i32x4 krs = raw_rsrc(p.k + hk * D, (long long)p.n_k * D * 2);
-  const i32x4 vrs = raw_rsrc(p.v + hk * D, (long long)p.n_k * D * 2);
-
-  // la over qdo from this wave's first row (rows and transposed reads of Q, dO); lk over
-  // the K block from this wave's first key (the V block follows at +BLK)
-  LdsAddr<D> la, lk;
-  make_lds_addr<D>(la, (unsigned)(uintptr_t)(const lds_void*)&qdo[0][0][0] + (unsigned)(32 * rh) * ROW, lane);
-  make_lds_addr<D>(lk, (unsigned)(uintptr_t)(const lds_void*)&kvb[0][0] + (unsigned)(32 * ks) * ROW, lane);
-
-  const int k0 = kb * kBK;
-  const int kw0 = k0 + 32 * ks;  // this wave's keys kw0 .. kw0 + 31
-  const int key = kw0 + col;     // this lane's key column
-  const int qb0 = p.causal ? min(k0 / kBQ, n_qb) : 0;
-
-  // slot offsets of this lane's loads: a 64-row tile takes NLDQ loads per wave, a 128-row
-  // block NLDB (the swizzle repeats every 16 rows, so block rows use the tile's pattern)
-  constexpr int NLDQ = kBQ * CPR / (64 * NW);
-  constexpr int NLDB = kBK * CPR / (64 * NW);
-  unsigned offb[NLDB];
-#pragma unroll
-  for (int i = 0; i < NLDB; ++i) {
-    const int sl = (i * NW + wave) * 64 + lane;
-    const int r = sl / CPR;
-    const int c = (sl % CPR) ^ (swz<D>(r, 0) - r * CPR);
-    offb[i] = (unsigned)((r * D + c * 8) * 2);
-  }
-  // K and V of the block (zero past n_k)
-#pragma unroll
-  for (int i = 0; i < NLDB; ++i) {
-    lds_dma16(krs, &kvb[0][(i * NW + wave) * 64 * 16], offb[i] + (unsigned)k0 * D * 2);
-    lds_dma16(vrs, &kvb[1][(i * NW + wave) * 64 * 16], offb[i] + (unsigned)k0 * D * 2);
-  }
-  auto issue_q = [&](int stage, int qi) {
-    const unsigned toff = (unsigned)(qi * kBQ) * D * 2;
-#pragma unroll
-    for (int i = 0; i < NLDQ; ++i) {  // the first NLDQ slot offsets of the block are the tile's
-      lds_dma16(qrs, &qdo[stage][0][(i * NW + wave) * 64 * 16], offb[i] + toff);
-      lds_dma16(dors, &qdo[stage][1][(i * NW + wave) * 64 * 16], offb[i] + toff);
-    }
-    // lanes 0-15 of wave 0 bring the 64 L2 values, lanes 16-31 the 64 D values
-    const int r0 = qi * kBQ;
-    if (wave == 0 && lane < 16)
-      lds_dma16(l2rs, reinterpret_cast<const char*>(&rowv[stage][0][0]), (unsigned)(r0 * 4 + lane * 16));
-    else if (wave == 0 && lane < 32)
-      lds_dma16(dvrs, reinterpret_cast<const char*>(&rowv[stage][1][0]) - 256, (unsigned)(r0 * 4 + (lane - 16) * 16));
-  };
-
-  f32x16 dvt[NB], dkt[NB];  // dV^T, dK^T over this wave's rows: rows d, columns its keys
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    dvt[nb] = f32x16{};
-    dkt[nb] = f32x16{};
-  }
-  if (qb0 < n_qb) issue_q(0, qb0);
-
-  // one query block: this wave's 32 rows against its 32 keys
-  auto step = [&](auto stg_c, int qi) {
-    constexpr int STG = decltype(stg_c)::value;
-    constexpr unsigned QOFF = STG * 2 * TILE, DOFF = QOFF + TILE;
-    constexpr int PF = D == 128 ? 1 : 2;  // operand k-steps read ahead of their products
-    const int i0 = qi * kBQ + 32 * rh;  // first row
-    // element (8g + e) is row i0 + 8g + 4hf + e: visible to this lane's key when
-    // lo <= 8g + e < hi
-    const int lo = (p.causal ? key - i0 : 0) - 4 * hf;
-    const int hi = (key < p.n_k ? p.n_q - i0 : 0) - 4 * hf;
-
-    // S = Q K^T and dP = dO V^T (keys on the lanes), operands read PF k-steps ahead
-    f32x16 s, dp;
-    bf16x8 ra[PF][4];
-    auto ld = [&](int t) {
-      ra[t % PF][0] = lds_load<bf16x8>(la.ka[t] + QOFF);
-      ra[t % PF][1] = lds_load<bf16x8>(lk.ka[t]);
-      ra[t % PF][2] = lds_load<bf16x8>(la.ka[t] + DOFF);
-      ra[t % PF][3] = lds_load<bf16x8>(lk.ka[t] + BLK);
-    };
-#pragma unroll
-    for (int t = 0; t < PF; ++t) ld(t);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 * PF, 0);
-#pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[t % PF][0], ra[t % PF][1], t ? s : f32x16{}, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[t % PF][2], ra[t % PF][3], t ? dp : f32x16{}, 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      if (t + PF < KT) {
-        ld(t + PF);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      }
-    }
-    // P = exp2(s * scale*log2e - L2), dS = P (dP - D), rows 8g + 4hf + e of this wave's half;
-    // only this part differs between blocks with and without masked pairs
-    bf16x8 pb[2], db[2];
-    auto softmax = [&](auto mask_c) {
-      constexpr bool MASKED = decltype(mask_c)::value;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int rl = 32 * rh + 8 * g + 4 * hf;
-        const f32x4 l2 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-            (uintptr_t)(const lds_void*)&rowv[STG][0][rl]);
-        const f32x4 dd = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-            (uintptr_t)(const lds_void*)&rowv[STG][1][rl]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2[e]));
-          if (MASKED) {
-            const int c = 8 * g + e;
-            pr = (c >= lo && c < hi) ? pr : 0.f;
-          }
-          dp[r] = pr * (dp[r] + dd[e]);  // dS over dP (dd = -D) and P over S, in place
-          s[r] = pr;
-        }
-      }
-      pb[0] = cvt_bf16x8(slice8(s, 0));
-      pb[1] = cvt_bf16x8(slice8(s, 1));
-      db[0] = cvt_bf16x8(slice8(dp, 0));
-      db[1] = cvt_bf16x8(slice8(dp, 1));
-    };
-    // masking: causal diagonal, query rows past n_q, keys past n_k (uniform per wave)
-    if ((p.causal && i0 < kw0 + 31) || (i0 + 32 > p.n_q) || (kw0 + 32 > p.n_k))
-      softmax(std::true_type{});
-    else
-      softmax(std::false_type{});
-    // dV^T += dO^T P, dK^T += Q^T dS over the wave's 32 rows (2 k-steps of 16), the
-    // transposed operands read PT products ahead
-    {
-      constexpr int NST = 2 * NB;
-      constexpr int PT = D == 128 ? 2 : 3;
-      bf16x8 rdo[PT], rq[PT];
-      auto ldt = [&](int st) {
-        const int t = st / NB, nb = st % NB;
-        const unsigned o = 16 * t * ROW;
-        rdo[st % PT] = tr_pair(la.va[2 * nb] + DOFF + o, la.va[2 * nb + 1] + DOFF + o);
-        rq[st % PT] = tr_pair(la.va[2 * nb] + QOFF + o, la.va[2 * nb + 1] + QOFF + o);
-      };
-#pragma unroll
-      for (int st = 0; st < PT; ++st) ldt(st);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4 * PT, 0);
-#pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const int t = st / NB, nb = st % NB;
-        dvt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rdo[st % PT], pb[t], dvt[nb], 0, 0, 0);
-        dkt[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq[st % PT], db[t], dkt[nb], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        if (st + PT < NST) {
-          ldt(st + PT);
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        }
-      }
-    }
-  };
-
-  for (int qi = qb0; qi < n_qb; qi += 2) {
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();  // stage 0 (and the K/V block) published; stage 1 free
-    if (qi + 1 < n_qb) issue_q(1, qi + 1);
-    step(std::integral_constant<int, 0>{}, qi);
-    if (qi + 1 < n_qb) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      __syncthreads();
-      if (qi + 2 < n_qb) issue_q(0, qi + 2);
-      step(std::integral_constant<int, 1>{}, qi + 1);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();  // every wave is done with the tiles: their space takes the partial sums
-
-  // the two waves of a key slice add their partial sums: waves 4-7 store dV^T, then dK^T,
-  // in the Q/dO tiles' space, waves 0-3 add them and write the result
-  float* part = reinterpret_cast<float*>(&qdo[0][0][0]);  // [slice][nb][16][64 lanes]
-  static_assert(4 * NB * 16 * 64 * 4 <= (int)sizeof(qdo), "partials fit in the tile space");
-  const bool write = key < p.n_k;
-  uint16_t* dkr = p.dk + (hk + key) * D;
-  uint16_t* dvr = p.dv + (hk + key) * D;
-  auto reduce = [&](f32x16(&acc)[NB], uint16_t* dst, float sc) {
-    if (rh == 1) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) part[((ks * NB + nb) * 16 + r) * 64 + lane] = acc[nb][r];
-    }
-    __syncthreads();
-    if (rh == 0 && write) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          f32x4 v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v4[e] = (acc[nb][4 * g + e] + part[((ks * NB + nb) * 16 + 4 * g + e) * 64 + lane]) * sc;
-          *reinterpret_cast<u32x2*>(dst + 32 * nb + 8 * g + 4 * hf) =
-              __builtin_bit_cast(u32x2, __builtin_convertvector(v4, bf16x4));
-        }
-    }
-    __syncthreads();
-  };
-  reduce(dvt, dvr, 1.f);
-  reduce(dkt, dkr, p.scale);
-}
-
-// ---------------------------------------------------------------------------
-// Key pass, ping-pong form: the workgroup, keys and row halves of bwd_kv8_kernel, with
-// the two waves of a SIMD one phase apart as in the ping-pong forward: group 0 (waves
-// 0-3, rows 0-31 of every 64-row query block) runs one phase ahead of group 1 (waves
-// 4-7, rows 32-63).  Per query block j and wave:
+// Key pass: one workgroup of 8 waves per (batch, head, 128-key block).  Wave w owns keys
+// 32 (w % 4) .. + 31 of the block and rows 32 (w / 4) .. + 31 of every 64-row query
+// block, so the two waves of a SIMD share their keys and split the rows; each
+// accumulates its own dV^T, dK^T (registers) and the pair is summed through LDS at the
+// end.  K and V of the block stay in LDS for the whole pass and serve as the B operands
+// of S and dP.  The two waves of a SIMD run one phase apart as in the ping-pong forward:
+// group 0 (waves 0-3) one phase ahead of group 1 (waves 4-7).  Per query block j and wave:
 //   matrix phase:  dV^T += dO_{j-1}^T P_{j-1};  dK^T += Q_{j-1}^T dS_{j-1};
 //                  S_j = Q_j K^T;  dP_j = dO_j V^T
 //   vector phase:  P_j = exp2(s * scale*log2e - L2) (0 where masked), dS_j = P_j (dP_j - D)
@@ -1167,7 +926,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
       hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(g2), dim3(256), 0, stream, p, sl2, sched);
   } else {
     hipLaunchKernelGGL(bwd_prep_kernel<64>, dim3(g0), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(bwd_kv8_kernel<64>, dim3(g1), dim3(512), 0, stream, p, sl2);
+    hipLaunchKernelGGL(bwd_kv_pp_kernel<64>, dim3(g1), dim3(512), 0, stream, p, sl2);
     if (pp)
       hipLaunchKernelGGL(bwd_dq_pp_kernel<64>, dim3(g3), dim3(512), 0, stream, p, sl2, sched);
     else
