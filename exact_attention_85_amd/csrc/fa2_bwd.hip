@@ -434,7 +434,7 @@ __device__ __forceinline__ void issue_kv(i32x4 krs, i32x4 vrs, const char* kdst,
 // B = this wave's fragments bf (row operand), k-steps of 16; operands read two ahead
 template <int D, unsigned OFF, typename Dma>
 __device__ __forceinline__ void rows_product(const LdsAddr<D>& la, const bf16x8 (&bf)[D / 16], f32x16& a0,
-                                             f32x16& a1, Dma&& dma) {
+                                             f32x16& a1, float start, Dma&& dma) {
   constexpr unsigned ROW = D * 2;
   constexpr int KT = D / 16;
   constexpr int PF = 2;
@@ -445,8 +445,11 @@ __device__ __forceinline__ void rows_product(const LdsAddr<D>& la, const bf16x8 
     a[t][1] = lds_load<bf16x8>(la.ka[t] + OFF + 32 * ROW);
   }
   __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
-  a0 = f32x16{};
-  a1 = f32x16{};
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {  // every element of this lane's row starts at `start`
+    a0[r] = start;
+    a1[r] = start;
+  }
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
     a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t % PF][0], bf[t], a0, 0, 0, 0);
@@ -545,14 +548,14 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p, float sl2, 
       return;
     }
     f32x16 s0, s1, d0, d1;
-    rows_product<D, KOFF>(la, qf, s0, s1, dma);
-    rows_product<D, VOFF>(la, dof, d0, d1, [](int) {});
+    rows_product<D, KOFF>(la, qf, s0, s1, 0.f, dma);
+    rows_product<D, VOFF>(la, dof, d0, d1, dd, [](int) {});  // dP^T - D: the products start at -D
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const f32x16& s = kb ? s1 : s0;
       f32x16& dp = kb ? d1 : d0;  // dS replaces dP in place
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2)) * (dp[r] + dd);
+      for (int r = 0; r < 16; ++r) dp[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2)) * dp[r];
     }
     // masked pairs (keys past n_k, or past the row under the causal mask) get dS = 0,
     // selected over whatever the unmasked formula gave; only tiles that reach past n_k or
