@@ -107,7 +107,7 @@ __device__ __forceinline__ bf16x8 tr_pair(unsigned a0, unsigned a1) {
 // matrix phase has just finished with, and retires the loads before the phase ends, so
 // that neither the issue of the loads nor the wait for them falls in a matrix phase.
 template <int D>
-__global__ void __launch_bounds__(512, 1) bwd_kv_pp_kernel(BwdParams p, float sl2) {
+__global__ void __launch_bounds__(512, 1) bwd_kv_pp_kernel(BwdParams p, float sl2, int sched) {
   constexpr int NW = 8;
   constexpr int NB = D / 32;
   constexpr int KT = D / 16;
@@ -130,9 +130,8 @@ __global__ void __launch_bounds__(512, 1) bwd_kv_pp_kernel(BwdParams p, float sl
   const int col = lane & 31;
 
   const int n_kb = (p.n_k + kBK - 1) / kBK;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = L / n_kb;
-  const int kb = L % n_kb;
+  int bh, kb;  // under the causal mask key block 0 sees the most query blocks: it goes first
+  wg_coords(wg_logical(sched), n_kb, p.B * p.H, sched, false, bh, kb);
   const int n_qb = (p.n_q + kBQ - 1) / kBQ;
 
   const long long hq = (long long)bh * p.n_q, hk = (long long)bh * p.n_k;
@@ -915,21 +914,21 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   const unsigned g0 = (unsigned)((R + (256 / (p.d / 8)) - 1) / (256 / (p.d / 8)));
   const unsigned g1 = (unsigned)((long long)p.B * p.H * ((p.n_k + kBK - 1) / kBK));
   const unsigned g2 = (unsigned)((long long)p.B * p.H * ((p.n_q + 127) / 128));
-  // dQ pass: the forward's workgroup orders (query-block-major without the renumbering under the
-  // causal mask, the heaviest blocks of every head first; renumbered head-major otherwise)
+  // both passes take the forward's workgroup orders: block-major without the renumbering under
+  // the causal mask, the heaviest blocks of every head first; renumbered head-major otherwise
   const int sched = p.causal ? kSchedQbMajor : kSchedRemap;
   const unsigned g3 = (unsigned)((long long)p.B * p.H * ((p.n_q + 255) / 256));
   const bool pp = p.d == 128 && p.n_q >= kDqPingPongMinRows;
   if (p.d == 128) {
     hipLaunchKernelGGL(bwd_prep_kernel<128>, dim3(g0), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(bwd_kv_pp_kernel<128>, dim3(g1), dim3(512), 0, stream, p, sl2);
+    hipLaunchKernelGGL(bwd_kv_pp_kernel<128>, dim3(g1), dim3(512), 0, stream, p, sl2, sched);
     if (pp)
       hipLaunchKernelGGL(bwd_dq_pp_kernel<128>, dim3(g3), dim3(512), 0, stream, p, sl2, sched);
     else
       hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(g2), dim3(256), 0, stream, p, sl2, sched);
   } else {
     hipLaunchKernelGGL(bwd_prep_kernel<64>, dim3(g0), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(bwd_kv_pp_kernel<64>, dim3(g1), dim3(512), 0, stream, p, sl2);
+    hipLaunchKernelGGL(bwd_kv_pp_kernel<64>, dim3(g1), dim3(512), 0, stream, p, sl2, sched);
     if (pp)
       hipLaunchKernelGGL(bwd_dq_pp_kernel<64>, dim3(g3), dim3(512), 0, stream, p, sl2, sched);
     else
