@@ -365,39 +365,64 @@ __global__ void __launch_bounds__(512, 1) bwd_kv_pp_kernel(BwdParams p, float sl
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();  // every wave is done with the tiles: their space takes the partial sums
 
-  // the two waves of a key slice add their partial sums: waves 4-7 store dV^T, then dK^T,
-  // in the Q/dO tiles' space, waves 0-3 add them and write the result
-  float* part = reinterpret_cast<float*>(&qdo[0][0][0]);  // [slice][nb][16][64 lanes]
-  static_assert(4 * NB * 16 * 64 * 4 <= (int)sizeof(qdo), "partials fit in the tile space");
-  const bool write = key < p.n_k;
-  uint16_t* dkr = p.dk + (hk + key) * D;
-  uint16_t* dvr = p.dv + (hk + key) * D;
-  auto reduce = [&](f32x16(&acc)[NB], uint16_t* dst, float sc) {
-    if (rh == 1) {
+  // The two waves of a key slice hold partial dV^T and dK^T of the same keys.  The second row
+  // half hands over its dV^T (in the Q/dO tiles' space), the first half its dK^T (in the K/V
+  // block's space); after one barrier the first half finishes dV and the second dK.  A finishing
+  // wave stages its 32 bf16 rows in its own slice of that space (row-major, each row padded by
+  // 16 bytes) and writes them out as whole rows, 16 bytes per lane.
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+  typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  constexpr int SLICE = NB * 16 * 64 * 4;  // bytes of one wave's partial sums
+  constexpr int SROW = ROW + 16;           // pitch of a staged row
+  constexpr int LPR = ROW / 16;            // lanes per row in the write-out
+  constexpr int RPI = 64 / LPR;            // rows per write-out instruction
+  static_assert(4 * SLICE <= (int)sizeof(qdo) && 4 * SLICE <= (int)sizeof(kvb), "partials fit");
+  static_assert(32 * SROW <= SLICE, "the staged rows fit in the slice");
+  const unsigned xv = (unsigned)(uintptr_t)(const lds_void*)&qdo[0][0][0] + (unsigned)(ks * SLICE);
+  const unsigned xk = (unsigned)(uintptr_t)(const lds_void*)&kvb[0][0] + (unsigned)(ks * SLICE);
+  auto slot = [&](unsigned base, int nb, int q) { return base + (unsigned)(((nb * 4 + q) * 64 + lane) * 16); };
+  auto hand_over = [&](const f32x16(&acc)[NB], unsigned base) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) part[((ks * NB + nb) * 16 + r) * 64 + lane] = acc[nb][r];
-    }
-    __syncthreads();
-    if (rh == 0 && write) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          f32x4 v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v4[e] = (acc[nb][4 * g + e] + part[((ks * NB + nb) * 16 + 4 * g + e) * 64 + lane]) * sc;
-          *reinterpret_cast<u32x2*>(dst + 32 * nb + 8 * g + 4 * hf) =
-              __builtin_bit_cast(u32x2, __builtin_convertvector(v4, bf16x4));
-        }
-    }
-    __syncthreads();
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {acc[nb][4 * q], acc[nb][4 * q + 1], acc[nb][4 * q + 2], acc[nb][4 * q + 3]};
+        *reinterpret_cast<lds_f32x4*>((uintptr_t)slot(base, nb, q)) = v;
+      }
   };
-  reduce(dvt, dvr, 1.f);
-  reduce(dkt, dkr, p.scale);
+  auto finish = [&](const f32x16(&acc)[NB], unsigned base, uint16_t* grad, float sc) {
+    // element 4q + e of acc[nb] is d = 32 nb + 8 q + 4 hf + e of this lane's key
+    u32x2 out[NB][4];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 o = *reinterpret_cast<const lds_f32x4*>((uintptr_t)slot(base, nb, q));
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (acc[nb][4 * q + e] + o[e]) * sc;
+        out[nb][q] = __builtin_bit_cast(u32x2, __builtin_convertvector(v, bf16x4));
+      }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<lds_u32x2*>((uintptr_t)(base + (unsigned)(col * SROW + (32 * nb + 8 * q + 4 * hf) * 2))) =
+            out[nb][q];
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + lane / LPR, c = lane % LPR;
+      const u32x4 v = *reinterpret_cast<const lds_u32x4*>((uintptr_t)(base + (unsigned)(r * SROW + c * 16)));
+      if (kw0 + r < p.n_k) *reinterpret_cast<u32x4*>(grad + (hk + kw0 + r) * D + c * 8) = v;
+    }
+  };
+  if (rh) hand_over(dvt, xv);
+  else hand_over(dkt, xk);
+  __syncthreads();
+  if (rh) finish(dkt, xk, p.dk, p.scale);
+  else finish(dvt, xv, p.dv, 1.f);
 }
 
 // ---------------------------------------------------------------------------
