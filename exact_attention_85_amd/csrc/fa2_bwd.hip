@@ -54,53 +54,6 @@ constexpr int kBQ = 64;   // query rows per step
 // s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt fields at their maxima)
 constexpr int kWaitVm0 = 0x0F70;
 
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-// Pitch of a gradient row staged in LDS: the row and 16 bytes, so that the 32 rows of a wave
-// written one per lane column fall on different banks.
-template <int D>
-constexpr int kStageRow = D * 2 + 16;
-
-// Write a wave's 32 gradient rows to HBM as whole rows.  The rows run along the lane columns
-// (lane column c holds row c), and out[nb][q] holds elements 32 nb + 8 q + 4 hf .. + 3 of its
-// row as bf16.  They are staged row-major at LDS address `stage` (32 * kStageRow<D> bytes that
-// no other wave uses now) and read back so that each store writes whole rows, 16 bytes per
-// lane.  Row r goes to dst + r * D when r < n_valid.
-template <int D>
-__device__ __forceinline__ void write_rows(const u32x2 (&out)[D / 32][4], unsigned stage, uint16_t* dst, int n_valid,
-                                           int lane) {
-  typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
-  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-  constexpr int SROW = kStageRow<D>;
-  constexpr int LPR = D * 2 / 16;  // lanes per row
-  constexpr int RPI = 64 / LPR;    // rows per store
-  const int col = lane & 31, hf = lane >> 5;
-#pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<lds_u32x2*>((uintptr_t)(stage + (unsigned)(col * SROW + (32 * nb + 8 * q + 4 * hf) * 2))) =
-          out[nb][q];
-#pragma unroll
-  for (int i = 0; i < 32 / RPI; ++i) {
-    const int r = i * RPI + lane / LPR, c = lane % LPR;
-    const u32x4 v = *reinterpret_cast<const lds_u32x4*>((uintptr_t)(stage + (unsigned)(r * SROW + c * 16)));
-    if (r < n_valid) *reinterpret_cast<u32x4*>(dst + (long long)r * D + c * 8) = v;
-  }
-}
-
-// out = bf16(acc * sc) in the layout write_rows takes
-template <int D>
-__device__ __forceinline__ void scaled_rows(const f32x16 (&acc)[D / 32], float sc, u32x2 (&out)[D / 32][4]) {
-#pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 v = {acc[nb][4 * q] * sc, acc[nb][4 * q + 1] * sc, acc[nb][4 * q + 2] * sc, acc[nb][4 * q + 3] * sc};
-      out[nb][q] = __builtin_bit_cast(u32x2, __builtin_convertvector(v, bf16x4));
-    }
-}
-
 // ---------------------------------------------------------------------------
 // D_i = sum_c dO_ic O_ic and LSE_i * log2(e).  D/8 lanes per row.
 template <int D>
@@ -419,7 +372,7 @@ __global__ void __launch_bounds__(512, 1) bwd_kv_pp_kernel(BwdParams p, float sl
   typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
   constexpr int SLICE = NB * 16 * 64 * 4;  // bytes of one wave's partial sums
   static_assert(4 * SLICE <= (int)sizeof(qdo) && 4 * SLICE <= (int)sizeof(kvb), "partials fit");
-  static_assert(32 * kStageRow<D> <= SLICE, "the staged rows fit in the slice");
+  static_assert(kStagedRows<D> <= SLICE, "the staged rows fit in the slice");
   const unsigned xv = (unsigned)(uintptr_t)(const lds_void*)&qdo[0][0][0] + (unsigned)(ks * SLICE);
   const unsigned xk = (unsigned)(uintptr_t)(const lds_void*)&kvb[0][0] + (unsigned)(ks * SLICE);
   auto slot = [&](unsigned base, int nb, int q) { return base + (unsigned)(((nb * 4 + q) * 64 + lane) * 16); };
@@ -661,13 +614,12 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p, float sl2, 
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last step's loads land before the workgroup ends
 
-  // dQ = scale * dQ^T^T (register 4g + i of block nb is d column 32nb + 8g + 4hf + i of the
-  // lane's row), staged in the tiles' space once every wave is done with it
-  static_assert(4 * 32 * kStageRow<D> <= (int)sizeof(lds), "the staged rows fit");
+  // dQ = scale * dQ^T^T, staged in the tiles' space once every wave is done with it
+  static_assert(4 * kStagedRows<D> <= (int)sizeof(lds), "the staged rows fit");
   u32x2 out[NB][4];
   scaled_rows<D>(dq, p.scale, out);
   __syncthreads();
-  write_rows<D>(out, (unsigned)(uintptr_t)(const lds_void*)&lds[0][0][0] + (unsigned)(wave * 32 * kStageRow<D>),
+  write_rows<D>(out, (unsigned)(uintptr_t)(const lds_void*)&lds[0][0][0] + (unsigned)(wave * kStagedRows<D>),
                 p.dq + (hq + q0w) * D, p.n_q - q0w, lane);
 }
 
@@ -938,12 +890,12 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_pp_kernel(BwdParams p, float sl
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last loads land before the workgroup ends
 
   // dQ staged in the K rings (waves 0-3) and the V rings (waves 4-7) once every wave is done
-  static_assert(4 * 32 * kStageRow<D> <= (int)sizeof(ldsk), "the staged rows fit");
+  static_assert(4 * kStagedRows<D> <= (int)sizeof(ldsk), "the staged rows fit");
   u32x2 out[NB][4];
   scaled_rows<D>(dq, p.scale, out);
   __syncthreads();
   const unsigned stage = (unsigned)(uintptr_t)(const lds_void*)(wave < 4 ? &ldsk[0][0] : &ldsv[0][0]) +
-                         (unsigned)((wave & 3) * 32 * kStageRow<D>);
+                         (unsigned)((wave & 3) * kStagedRows<D>);
   write_rows<D>(out, stage, p.dq + (hq + q0w) * D, p.n_q - q0w, lane);
 }
 

@@ -169,5 +169,56 @@ __device__ __forceinline__ void make_lds_addr(LdsAddr<D>& a, unsigned base, int 
   for (int i = 0; i < D / 16; ++i) asm volatile("" : "+v"(a.ka[i]), "+v"(a.va[i]));
 }
 
+// ---------------------------------------------------------------------------
+// Output rows.  The kernels hold a wave's 32 output rows transposed: lane column c owns row c,
+// and register 4q + e of 32-column block nb is element 32 nb + 8 q + 4 hf + e of it (hf the
+// lane half).  Written straight out, every store would cover 16 bytes of 32 rows.  write_rows
+// stages the rows in LDS instead (row-major, 2D bytes per row, the 16-byte chunks of row r
+// placed at chunk index c ^ (r mod 16) so that the 32 rows written by one instruction spread
+// over the banks) and reads them back so that each store writes whole rows, 16 bytes per lane.
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+constexpr int kStagedRows = 32 * D * 2;  // LDS bytes write_rows takes per wave
+
+// out[nb][q] = bf16(acc[nb][4q .. 4q + 3] * sc), round to nearest even
+template <int D>
+__device__ __forceinline__ void scaled_rows(const f32x16 (&acc)[D / 32], float sc, u32x2 (&out)[D / 32][4]) {
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = {acc[nb][4 * q] * sc, acc[nb][4 * q + 1] * sc, acc[nb][4 * q + 2] * sc, acc[nb][4 * q + 3] * sc};
+      out[nb][q] = __builtin_bit_cast(u32x2, __builtin_convertvector(v, bf16x4));
+    }
+}
+
+// Row r (r < 32) goes to dst + r * D when r < n_valid.  `stage`: kStagedRows<D> bytes of LDS
+// that no other wave touches until this call returns.
+template <int D>
+__device__ __forceinline__ void write_rows(const u32x2 (&out)[D / 32][4], unsigned stage, uint16_t* dst, int n_valid,
+                                           int lane) {
+  typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  constexpr int ROW = D * 2;
+  constexpr int LPR = ROW / 16;  // 16-byte chunks per row = lanes per row in the write-out
+  constexpr int RPI = 64 / LPR;  // rows per store
+  const int col = lane & 31, hf = lane >> 5;
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = (4 * nb + q) ^ (col & 15 & (LPR - 1));
+      *reinterpret_cast<lds_u32x2*>((uintptr_t)(stage + (unsigned)(col * ROW + c * 16 + hf * 8))) = out[nb][q];
+    }
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / LPR, c = lane % LPR;
+    const u32x4 v =
+        *reinterpret_cast<const lds_u32x4*>((uintptr_t)(stage + (unsigned)(r * ROW + (c ^ (r & 15 & (LPR - 1))) * 16)));
+    if (r < n_valid) *reinterpret_cast<u32x4*>(dst + (long long)r * D + c * 8) = v;
+  }
+}
+
 }  // namespace
 }  // namespace fa2

@@ -434,22 +434,19 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_kernel(FwdParams p, float
   // ---- epilogue ----
   const float l_tot = w.l_run + __shfl_xor(w.l_run, 32);
   const float l16_tot = w.l16 + __shfl_xor(w.l16, 32);
-  if (row >= p.n_q) return;
   if (!SPLIT) {
-    const float inv = l16_tot > 0.f ? 1.f / l16_tot : 0.f;  // a row with no visible key: O = 0
-    uint16_t* Orow = p.o + ((long long)bh * p.n_q + row) * D;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 o4 = {w.acc[nb][4 * g] * inv, w.acc[nb][4 * g + 1] * inv, w.acc[nb][4 * g + 2] * inv,
-                          w.acc[nb][4 * g + 3] * inv};
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        const bf16x4 b4 = __builtin_convertvector(o4, bf16x4);
-        *reinterpret_cast<u32x2*>(Orow + 32 * nb + 8 * g + 4 * hf) = __builtin_bit_cast(u32x2, b4);
-      }
-    if (hf == 0) p.lse[(long long)bh * p.n_q + row] = l_tot > 0.f ? (w.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    // O = acc / l16 (a row with no visible key: O = 0), staged in the tiles' space once every
+    // wave is done with it and written as whole rows
+    static_assert(NW * kStagedRows<D> <= (int)sizeof(lds), "the staged rows fit");
+    u32x2 out[NB][4];
+    scaled_rows<D>(w.acc, l16_tot > 0.f ? 1.f / l16_tot : 0.f, out);
+    __syncthreads();
+    write_rows<D>(out, (unsigned)(uintptr_t)(const lds_void*)&lds[0][0][0] + (unsigned)(wave * kStagedRows<D>),
+                  p.o + ((long long)bh * p.n_q + q0w) * D, p.n_q - q0w, lane);
+    if (hf == 0 && row < p.n_q)
+      p.lse[(long long)bh * p.n_q + row] = l_tot > 0.f ? (w.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
+    if (row >= p.n_q) return;
     // partial (acc, m, l) with l the fp32 sum: acc is rescaled by l / l16 so that acc / l is
     // the chunk's output exactly as normalised by its bf16 probabilities (0 for an empty chunk)
     const long long R = (long long)p.B * p.H * p.n_q;
@@ -981,20 +978,16 @@ __global__ void __launch_bounds__(512, 1) fwd_pp_kernel(FwdParams p, float sl2, 
 
   const float l_tot = w.l_run + __shfl_xor(w.l_run, 32);
   const float l16_tot = w.l16 + __shfl_xor(w.l16, 32);
-  if (row >= p.n_q) return;
-  const float inv = l16_tot > 0.f ? 1.f / l16_tot : 0.f;
-  uint16_t* Orow = p.o + ((long long)bh * p.n_q + row) * D;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 o4 = {w.acc[nb][4 * g] * inv, w.acc[nb][4 * g + 1] * inv, w.acc[nb][4 * g + 2] * inv,
-                        w.acc[nb][4 * g + 3] * inv};
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      const bf16x4 b4 = __builtin_convertvector(o4, bf16x4);
-      *reinterpret_cast<u32x2*>(Orow + 32 * nb + 8 * g + 4 * hf) = __builtin_bit_cast(u32x2, b4);
-    }
-  if (hf == 0) p.lse[(long long)bh * p.n_q + row] = l_tot > 0.f ? (w.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  // O staged in the K rings (group 0) and the V rings (group 1) once every wave is done with them
+  static_assert(4 * kStagedRows<D> <= (int)sizeof(ldsk), "the staged rows fit");
+  u32x2 out[NB][4];
+  scaled_rows<D>(w.acc, l16_tot > 0.f ? 1.f / l16_tot : 0.f, out);
+  __syncthreads();
+  const unsigned stage = (unsigned)(uintptr_t)(const lds_void*)(wave < 4 ? &ldsk[0][0] : &ldsv[0][0]) +
+                         (unsigned)((wave & 3) * kStagedRows<D>);
+  write_rows<D>(out, stage, p.o + ((long long)bh * p.n_q + q0w) * D, p.n_q - q0w, lane);
+  if (hf == 0 && row < p.n_q)
+    p.lse[(long long)bh * p.n_q + row] = l_tot > 0.f ? (w.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 // scale handling shared by all launches: fold |scale|*log2(e) into one positive
