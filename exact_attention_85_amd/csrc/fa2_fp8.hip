@@ -339,19 +339,15 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_fp8_kernel(Fp8Params p) {
   // ---- epilogue ----
   const float l_tot = w.l_run + __shfl_xor(w.l_run, 32);
   const float lq = w.lsum[0];
+  // O = dsv * acc / lq (a row with no visible key: O = 0), staged in the tiles' space once every
+  // wave is done with it and written as whole rows
+  static_assert(NW * kStagedRows<D> <= (int)sizeof(lds), "the staged rows fit");
+  u32x2 out[NB][4];
+  scaled_rows<D>(w.acc, lq > 0.f ? dsv / lq : 0.f, out);
+  __syncthreads();
+  write_rows<D>(out, (unsigned)(uintptr_t)(const lds_void*)&lds[0][0][0] + (unsigned)(wave * kStagedRows<D>),
+                p.o + ((long long)bh * p.n_q + q0w) * D, p.n_q - q0w, lane);
   if (row >= p.n_q) return;
-  const float inv = lq > 0.f ? dsv / lq : 0.f;  // a row with no visible key: O = 0
-  uint16_t* Orow = p.o + ((long long)bh * p.n_q + row) * D;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 o4 = {w.acc[nb][4 * g] * inv, w.acc[nb][4 * g + 1] * inv, w.acc[nb][4 * g + 2] * inv,
-                        w.acc[nb][4 * g + 3] * inv};
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      const bf16x4 b4 = __builtin_convertvector(o4, bf16x4);
-      *reinterpret_cast<u32x2*>(Orow + 32 * nb + 8 * g + 4 * hf) = __builtin_bit_cast(u32x2, b4);
-    }
   if (hf == 0)
     p.lse[(long long)bh * p.n_q + row] = l_tot > 0.f ? (w.m_run + __log2f(l_tot) - kPLog2) * kLn2 : -INFINITY;
 }
