@@ -301,12 +301,9 @@ int fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const vo
   // the forward's own checks on Q, K, V, O, LSE (LSE read-only here)
   int rc = check_common(Q, K, V, O, LSE, B, H, N_q, N_k, d, scale);
   if (rc != FA2_OK) return rc;
-  // the three launches: D and LSE*log2e (256 work-items per 256/(d/8) rows), the key blocks
-  // (one workgroup of 256 per 128 keys), the query blocks (one workgroup of 256 per 128 rows,
-  // or of 512 per 256 rows in the ping-pong form)
-  const long long R_all = (long long)B * H * N_q;
-  if (!launch_fits((R_all + 256 / (d / 8) - 1) / (256 / (d / 8)), 256) ||
-      !launch_fits((long long)((N_k + 127) / 128) * B * H, 256) ||
+  // the two launches: the query blocks (one workgroup of 256 per 128 rows, or of 512 per 256
+  // rows in the ping-pong form), then the key blocks (one workgroup of 512 per 128 keys)
+  if (!launch_fits((long long)((N_k + 127) / 128) * B * H, 512) ||
       !launch_fits((long long)((N_q + 127) / 128) * B * H, 256) ||
       !launch_fits((long long)((N_q + 255) / 256) * B * H, 512))
     return FA2_ERR_BAD_SHAPE;

@@ -12,8 +12,15 @@
 //   dK_j  = scale sum_i dS_ij q_i
 //   dQ_i  = scale sum_j dS_ij k_j
 //
-// Three launches:
-//   bwd_prep_kernel    -D_i and LSE_i * log2(e) for every query row
+// Two launches, the dQ pass first:
+//   bwd_dq_kernel      one workgroup per 128-row query block (one wave per 32
+//                      rows): forms -D_i and LSE_i * log2(e) of its rows (kept
+//                      in registers and stored for the key pass), streams
+//                      64-key K/V tiles through LDS as the forward does and
+//                      runs three products (S, dP, then dQ += dS K); dQ stays
+//                      in registers.  From 2048 query rows at d = 128,
+//                      bwd_dq_pp_kernel does the same work with 8 waves in the
+//                      ping-pong schedule of the forward
 //   bwd_kv_pp_kernel   one workgroup of 8 waves per 128-key block: two waves per
 //                      32 keys, each over half of every 64-row query block
 //                      streamed through LDS; four products on the matrix cores
@@ -21,12 +28,6 @@
 //                      LDS, dK and dV in registers, and the two halves' sums
 //                      are added at the end.  The two waves of a SIMD run one
 //                      phase apart (ping-pong schedule)
-//   bwd_dq_kernel      one workgroup per 128-row query block (one wave per 32
-//                      rows): streams 64-key K/V tiles through LDS as the
-//                      forward does and runs three products (S, dP, then
-//                      dQ += dS K); dQ stays in registers.  From 2048 query
-//                      rows at d = 128, bwd_dq_pp_kernel does the same work
-//                      with 8 waves in the ping-pong schedule of the forward
 // This is the deterministic form of the synthesis page's section 5 item 2
 // without any partial sums in memory: every gradient element is accumulated
 // by exactly one wave, in a fixed order, and written once, so the result is
@@ -53,34 +54,6 @@ constexpr int kBK = 128;  // keys per workgroup of the key pass
 constexpr int kBQ = 64;   // query rows per step
 // s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt fields at their maxima)
 constexpr int kWaitVm0 = 0x0F70;
-
-// ---------------------------------------------------------------------------
-// D_i = sum_c dO_ic O_ic and LSE_i * log2(e).  D/8 lanes per row.
-template <int D>
-__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
-  constexpr int LPR = D / 8;
-  const long long R = (long long)p.B * p.H * p.n_q;
-  const long long row = (long long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
-  const int sub = threadIdx.x % LPR;
-  float acc = 0.f;
-  if (row < R) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p.dout + row * D + sub * 8);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(p.o + row * D + sub * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const unsigned x = a[i], y = b[i];
-      acc = __builtin_fmaf(__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, y << 16), acc);
-      acc = __builtin_fmaf(__builtin_bit_cast(float, x & 0xffff0000u), __builtin_bit_cast(float, y & 0xffff0000u),
-                           acc);
-    }
-  }
-#pragma unroll
-  for (int x = LPR / 2; x >= 1; x >>= 1) acc += __shfl_xor(acc, x);
-  if (sub == 0 && row < R) {
-    p.dvec[row] = -acc;  // -D: the products that need dP - D start from it
-    p.l2vec[row] = p.lse[row] * kLog2e;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Two transposed 8-byte LDS reads forming one 16-byte MFMA operand.
@@ -514,9 +487,29 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p, float sl2, 
       qf[t] = as_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0)));
       dof[t] = as_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(drs, off, 0, 0)));
     }
+    // -D = -sum_c dO_c O_c of the row (its two halves in lanes c and c + 32) and LSE*log2e,
+    // kept in registers and stored for the key pass
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(p.o + hq * D, (long long)p.n_q * D * 2);
+    float dpart = 0.f;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      const unsigned off = ((unsigned)row * D + 16 * t + 8 * hf) * 2u;
+      const u32x4 ov = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ors, off, 0, 0));
+      const u32x4 dv = __builtin_bit_cast(u32x4, dof[t]);
+      const unsigned o0 = ov.x, o1 = ov.y, o2 = ov.z, o3 = ov.w, d0 = dv.x, d1 = dv.y, d2 = dv.z, d3 = dv.w;
+      dpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d0), __builtin_bit_cast(bf16x2, o0), dpart, false);
+      dpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d1), __builtin_bit_cast(bf16x2, o1), dpart, false);
+      dpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d2), __builtin_bit_cast(bf16x2, o2), dpart, false);
+      dpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d3), __builtin_bit_cast(bf16x2, o3), dpart, false);
+    }
+    const float dsum = dpart + __shfl_xor(dpart, 32);
     if (row < p.n_q) {
-      l2 = p.l2vec[hq + row];
-      dd = p.dvec[hq + row];  // -D
+      l2 = p.lse[hq + row] * kLog2e;
+      dd = -dsum;
+      if (hf == 0) {
+        p.dvec[hq + row] = dd;
+        p.l2vec[hq + row] = l2;
+      }
     }
   }
   f32x16 dq[NB];
@@ -747,9 +740,29 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_pp_kernel(BwdParams p, float sl
       qf[t] = as_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0)));
       dof[t] = as_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(drs, off, 0, 0)));
     }
+    // -D = -sum_c dO_c O_c of the row (its two halves in lanes c and c + 32) and LSE*log2e,
+    // kept in registers and stored for the key pass
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(p.o + hq * D, (long long)p.n_q * D * 2);
+    float dpart = 0.f;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      const unsigned off = ((unsigned)row * D + 16 * t + 8 * hf) * 2u;
+      const u32x4 ov = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ors, off, 0, 0));
+      const u32x4 dv = __builtin_bit_cast(u32x4, dof[t]);
+      const unsigned o0 = ov.x, o1 = ov.y, o2 = ov.z, o3 = ov.w, d0 = dv.x, d1 = dv.y, d2 = dv.z, d3 = dv.w;
+      dpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d0), __builtin_bit_cast(bf16x2, o0), dpart, false);
+      dpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d1), __builtin_bit_cast(bf16x2, o1), dpart, false);
+      dpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d2), __builtin_bit_cast(bf16x2, o2), dpart, false);
+      dpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d3), __builtin_bit_cast(bf16x2, o3), dpart, false);
+    }
+    const float dsum = dpart + __shfl_xor(dpart, 32);
     if (row < p.n_q) {
-      l2 = p.l2vec[hq + row];
-      dd = p.dvec[hq + row];  // -D
+      l2 = p.lse[hq + row] * kLog2e;
+      dd = -dsum;
+      if (hf == 0) {
+        p.dvec[hq + row] = dd;
+        p.l2vec[hq + row] = l2;
+      }
     }
   }
   f32x16 dq[NB];
@@ -905,9 +918,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_pp_kernel(BwdParams p, float sl
 constexpr int kDqPingPongMinRows = 2048;
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
-  const long long R = (long long)p.B * p.H * p.n_q;
   const float sl2 = p.scale * kLog2e;
-  const unsigned g0 = (unsigned)((R + (256 / (p.d / 8)) - 1) / (256 / (p.d / 8)));
   const unsigned g1 = (unsigned)((long long)p.B * p.H * ((p.n_k + kBK - 1) / kBK));
   const unsigned g2 = (unsigned)((long long)p.B * p.H * ((p.n_q + 127) / 128));
   // both passes take the forward's workgroup orders: block-major without the renumbering under
@@ -915,20 +926,19 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   const int sched = p.causal ? kSchedQbMajor : kSchedRemap;
   const unsigned g3 = (unsigned)((long long)p.B * p.H * ((p.n_q + 255) / 256));
   const bool pp = p.d == 128 && p.n_q >= kDqPingPongMinRows;
+  // the dQ pass first: it forms -D and LSE*log2e of its rows and stores them for the key pass
   if (p.d == 128) {
-    hipLaunchKernelGGL(bwd_prep_kernel<128>, dim3(g0), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(bwd_kv_pp_kernel<128>, dim3(g1), dim3(512), 0, stream, p, sl2, sched);
     if (pp)
       hipLaunchKernelGGL(bwd_dq_pp_kernel<128>, dim3(g3), dim3(512), 0, stream, p, sl2, sched);
     else
       hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(g2), dim3(256), 0, stream, p, sl2, sched);
+    hipLaunchKernelGGL(bwd_kv_pp_kernel<128>, dim3(g1), dim3(512), 0, stream, p, sl2, sched);
   } else {
-    hipLaunchKernelGGL(bwd_prep_kernel<64>, dim3(g0), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(bwd_kv_pp_kernel<64>, dim3(g1), dim3(512), 0, stream, p, sl2, sched);
     if (pp)
       hipLaunchKernelGGL(bwd_dq_pp_kernel<64>, dim3(g3), dim3(512), 0, stream, p, sl2, sched);
     else
       hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(g2), dim3(256), 0, stream, p, sl2, sched);
+    hipLaunchKernelGGL(bwd_kv_pp_kernel<64>, dim3(g1), dim3(512), 0, stream, p, sl2, sched);
   }
   return hipGetLastError();
 }

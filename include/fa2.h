@@ -248,10 +248,11 @@ size_t fa2_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d);
  * P is rounded to bf16 for dV, dS to bf16 for dK and dQ; products accumulate
  * in fp32; dQ, dK, dV are written as bf16 (RNE).
  *
- * Passes: (1) D and LSE*log2(e) per row; (2) one workgroup per 128-key block
- * streams the query blocks and accumulates dK and dV for its keys; (3) one
- * workgroup per 128-row query block streams the key blocks and accumulates dQ
- * for its rows.  Both passes recompute S and dP (seven products in all); every
+ * Passes: (1) one workgroup per 128-row query block forms D and LSE*log2(e)
+ * of its rows (stored in the workspace), streams the key blocks and
+ * accumulates dQ for its rows; (2) one workgroup per 128-key block streams
+ * the query blocks and accumulates dK and dV for its keys.  Both passes
+ * recompute S and dP (seven products in all); every
  * gradient element is accumulated by one wave in a fixed order, with no
  * partial sums in memory and no atomics: results are bit-reproducible.
  *

@@ -310,10 +310,11 @@ def test_work_item_limits():
     assert window(B=1 << 12, H=1 << 12, nq=128, nk=16, d=64) == BAD_SHAPE
     assert fwd8(B=1 << 12, H=1 << 12, nq=128, nk=16, d=64) == BAD_SHAPE
     assert dec8(B=1 << 12, H=1 << 12, nk=16, d=64) == BAD_SHAPE
-    # the backward: its per-row pass takes 16 work-items per row at d = 128 (the largest of its
-    # launches), so 2^30 rows are refused
-    assert bwd(B=1 << 11, H=1 << 11, nq=256, nk=16, d=128) == BAD_SHAPE
-    assert bwd(B=1 << 10, H=1 << 10, nq=255, nk=16, d=128) != BAD_SHAPE  # 16 * 2^20 * 255 < 2^32
+    # the backward: the key pass takes 512 work-items per 128-key block, the dQ pass 256 per
+    # 128-row block (or 512 per 256 rows); 2^22 heads reach 2^32 at 2 key blocks or 512 rows
+    assert bwd(B=1 << 11, H=1 << 11, nq=128, nk=256, d=128) == BAD_SHAPE
+    assert bwd(B=1 << 11, H=1 << 11, nq=512, nk=128, d=128) == BAD_SHAPE
+    assert bwd(B=1 << 11, H=1 << 11, nq=256, nk=128, d=128) != BAD_SHAPE  # 2^22 * 512 < 2^32
 
 
 def noalloc(q=Q, k=K, v=V, o=O, l=L, B=1, H=2, nq=1, nk=256, d=64, causal=0, scale=0.125, s=4):
