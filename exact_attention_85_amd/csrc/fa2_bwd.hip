@@ -338,6 +338,20 @@ __global__ void __launch_bounds__(512, 1) bwd_kv_pp_kernel(BwdParams p, float sl
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();  // every wave is done with the tiles: their space takes the partial sums
 
+  // The workgroup 256 ids later runs on this XCD next (ids go round the 8 XCDs, 32 units each):
+  // touch one dword of each 128-byte line of its K and V block, so that its prologue finds them
+  // in L2.  Waves 0-3 take K, 4-7 V, 64 lines each; the value is only kept until the end.
+  unsigned pref = 0;
+  if (blockIdx.x + 256 < gridDim.x) {
+    int nbh, nkb;
+    wg_coords((sched & kSchedRemap) ? xcd_remap(blockIdx.x + 256, gridDim.x) : (int)blockIdx.x + 256, n_kb,
+              p.B * p.H, sched, false, nbh, nkb);
+    const long long nhk = (long long)nbh * p.n_k;
+    const int nk0 = nkb * kBK;
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc((wave < 4 ? p.k : p.v) + (nhk + nk0) * D, (long long)(p.n_k - nk0) * D * 2);
+    pref = __builtin_amdgcn_raw_buffer_load_b32(prs, (unsigned)(((wave & 3) * 64 + lane) * 128) % (unsigned)BLK, 0, 0);
+  }
+
   // The two waves of a key slice hold partial dV^T and dK^T of the same keys.  The second row
   // half hands over its dV^T (in the Q/dO tiles' space), the first half its dK^T (in the K/V
   // block's space); after one barrier the first half finishes dV and the second dK, staging its
@@ -377,6 +391,7 @@ __global__ void __launch_bounds__(512, 1) bwd_kv_pp_kernel(BwdParams p, float sl
   __syncthreads();
   if (rh) finish(dkt, xk, p.dk, p.scale);
   else finish(dvt, xv, p.dv, 1.f);
+  asm volatile("" ::"v"(pref));
 }
 
 // ---------------------------------------------------------------------------
