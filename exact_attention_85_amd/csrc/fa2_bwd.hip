@@ -929,8 +929,10 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_pp_kernel(BwdParams p, float sl
 
 }  // namespace
 
-// the dQ pass takes the ping-pong kernel from this many query rows
+// the dQ pass takes the ping-pong kernel from this many query rows (d = 128); under the causal
+// mask its 256-row workgroups split the triangle too coarsely below 4096 rows
 constexpr int kDqPingPongMinRows = 2048;
+constexpr int kDqPingPongMinRowsCausal = 4096;
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   const float sl2 = p.scale * kLog2e;
@@ -940,7 +942,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   // the causal mask, the heaviest blocks of every head first; renumbered head-major otherwise
   const int sched = p.causal ? kSchedQbMajor : kSchedRemap;
   const unsigned g3 = (unsigned)((long long)p.B * p.H * ((p.n_q + 255) / 256));
-  const bool pp = p.d == 128 && p.n_q >= kDqPingPongMinRows;
+  const bool pp = p.d == 128 && p.n_q >= (p.causal ? kDqPingPongMinRowsCausal : kDqPingPongMinRows);
   // the dQ pass first: it forms -D and LSE*log2e of its rows and stores them for the key pass
   if (p.d == 128) {
     if (pp)

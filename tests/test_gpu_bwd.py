@@ -64,10 +64,12 @@ def test_bwd_many_heads(B, H, nq, nk, d, causal):
                  f"many heads nq={nq} nk={nk} d={d} causal={causal}")
 
 
-# From 2048 query rows at d = 128 the dQ pass takes the 8-wave ping-pong kernel: ragged row
-# and key counts around its 256-row blocks and 64-key tiles, both masks
-@pytest.mark.parametrize("nq,nk,causal", [(2053, 2053, True), (2053, 2053, False), (2100, 1, False),
-                                          (2048, 100, True), (2300, 333, False), (2049, 4100, True)])
+# From 2048 query rows at d = 128 (4096 under the causal mask) the dQ pass takes the 8-wave
+# ping-pong kernel: ragged row and key counts around its 256-row blocks and 64-key tiles, both
+# masks, and the causal 4-wave kernel just below its threshold
+@pytest.mark.parametrize("nq,nk,causal", [(4101, 4101, True), (2053, 2053, False), (2100, 1, False),
+                                          (4096, 100, True), (2300, 333, False), (4097, 4100, True),
+                                          (4095, 4095, True)])
 def test_bwd_pingpong_dq(nq, nk, causal):
     print(f"case bwd ping-pong dQ nq={nq} nk={nk} causal={causal}", flush=True)
     d, scale = 128, 1.0 / math.sqrt(128)
