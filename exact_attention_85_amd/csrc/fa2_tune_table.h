@@ -18,17 +18,14 @@ struct TuneRow {
   int config;
 };
 
-// source: tune.py on AMD Radeon Graphics (256 CUs), 2026-12-03 04:27 UTC, 20 reps
+// source: tune.py on AMD Radeon Graphics (256 CUs), 2026-12-03 07:33 UTC, 15 reps
 constexpr TuneRow kTuneTable[] = {
-    {64, 0, 1, 0},  // tile128_remap_headmajor
-    {64, 0, 724, 8},  // tile256_remap_headmajor
-    {64, 1, 1, 3},  // tile128_noremap_qbmajor
-    {64, 1, 1448, 9},  // tile256_noremap_qbmajor
+    {64, 0, 1, 8},  // tile256_remap_headmajor
+    {64, 1, 1, 9},  // tile256_noremap_qbmajor
     {128, 0, 1, 0},  // tile128_remap_headmajor
     {128, 0, 1448, 4},  // pingpong256_remap_headmajor
-    {128, 1, 1, 3},  // tile128_noremap_qbmajor
-    {128, 1, 1448, 9},  // tile256_noremap_qbmajor
-    {128, 1, 5793, 7},  // pingpong256_noremap_qbmajor
+    {128, 1, 1, 9},  // tile256_noremap_qbmajor
+    {128, 1, 2896, 7},  // pingpong256_noremap_qbmajor
 };
 
 }  // namespace fa2

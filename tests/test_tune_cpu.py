@@ -14,9 +14,12 @@ def test_table_rows_pick_the_fastest_and_merge_neighbours():
     rows = tune.table_rows(results)
     assert rows[(128, 0)] == [(1, 0), (2048, 4)]      # 4096 and 16384 both pick 4: merged
     assert rows[(64, 1)] == [(1, 1), (2048, 3)]
-    # ties (within 2 %) go to the renumbered head-major order (configs 0, 4, 8), then to the previous choice
+    # ties (within 2.5 %) go to the previous length's choice, then to the renumbered head-major
+    # order (configs 0, 4, 8), then to the faster
     tied = {(128, 0): {1024: {0: 1.00, 2: 0.99}, 4096: {4: 1.00, 6: 0.985, 7: 0.90}, 8192: {4: 1.0, 6: 0.99}}}
     assert tune.table_rows(tied)[(128, 0)] == [(1, 0), (2048, 7), (5793, 4)]
+    kept = {(128, 1): {1024: {2: 1.0, 0: 1.1}, 4096: {2: 1.01, 0: 1.0}, 16384: {2: 1.2, 0: 1.0}}}
+    assert tune.table_rows(kept)[(128, 1)] == [(1, 2), (8192, 0)]
 
 
 def test_written_header_round_trips(tmp_path):
